@@ -1,0 +1,15 @@
+"""CPU oracle for the LLM.int8() linear layer (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU baseline leg import
+this package. The product path (the HIP library and its binding) never does.
+"""
+from .oracle import (  # noqa: F401
+    half_to_float,
+    quantize_colwise,
+    find_outliers,
+    quantize_rowwise,
+    gemm_i8,
+    merge,
+    linear,
+    linear_rows,
+)

@@ -1,0 +1,210 @@
+/*
+ * CPU oracle for the LLM.int8() mixed-precision linear layer Y = X.W.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The GPU library never links it and
+ * shares no code, header or table with it.
+ *
+ * Plain, single-threaded, obviously-correct C. Every function follows one step
+ * of the method as the pages state it:
+ *
+ *   [P2] "8-bit quantization of giant language models: LLM.int8()" (2kiu.com)
+ *        section 2.1 (vector-wise scales: per-column for W, per-row for X),
+ *        section 2.3 (outlier columns of X by a threshold on the column's
+ *        absolute maximum, default 6.0; X_outlier.W_outlier in 16-bit, the rest
+ *        in int8 with row/column scales), section 4.2 (the whole column goes
+ *        the 16-bit way).
+ *   [P5] "LLM.int8() pitfalls: why your 8-bit model collapses" (codearts)
+ *        section 1 (scale_factor = 127 / max|x|, q = round(x * scale_factor)),
+ *        section 2 (worked example), section 3.3 (dequantize the 8-bit result
+ *        and ADD it to the 16-bit result).
+ *   [P3] "Large-model quantization in practice: from INT8 to QLoRA" (cnnetsun)
+ *        section 3.2 (round, then clamp, then cast; compute in float32) and
+ *        section 3.3 (symmetric: zero point 0, clamp to [-127, 127]).
+ *   [P1] "8-Bit LLM Quantization with Lightning Fabric" (aicoding) section 2.2
+ *        (int8 x int8 -> int32 matmul, then rescale by scale_x * scale_w).
+ *
+ * Readings taken where the pages are silent or disagree:
+ *   - outlier test is |x| >= threshold (inclusive); a column is an outlier when
+ *     any of its entries passes it;
+ *   - the row absmax of X excludes outlier columns; outlier columns of Xq are 0;
+ *   - the column absmax of W runs over all K rows (W is quantized once, at load);
+ *   - the scale is applied as x * fl32(127 / absmax): one IEEE fp32 division,
+ *     one fp32 multiply, round-half-to-even, clamp to [-127, 127], cast;
+ *   - an all-zero row/column has absmax 0 and quantizes to all zeros;
+ *   - merge is a sum; the 16-bit product and the merge are evaluated in fp64
+ *     here (the most exact reading of "fp32-accumulated"; the GPU's fp16 output
+ *     is compared against it with a tolerance).
+ *
+ * Build: gcc -O2 -ffp-contract=off -std=c11 -shared -fPIC (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE 754 binary16 -> binary32. Exact for every pattern (binary32 holds every
+ * binary16 value, including subnormals, as a normal or zero value). */
+static float ora_half(uint16_t h)
+{
+    unsigned sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    unsigned f = h & 0x3ffu;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);                   /* f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(f | 0x400u), e - 25);     /* (1024 + f) * 2^(e-25) */
+    return sign ? -v : v;
+}
+
+void ora_half_to_float(const uint16_t *h, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ora_half(h[i]);
+}
+
+/* The symmetric absmax quantizer of [P5] section 1 with the round/clamp/cast
+ * order of [P3] section 3.2: q = clamp(round_half_even(x * inv), -127, 127). */
+static int8_t ora_quant(float x, float inv)
+{
+    float v = x * inv;
+    float r = rintf(v);                 /* default mode: round half to even */
+    if (r > 127.0f)
+        r = 127.0f;
+    if (r < -127.0f)
+        r = -127.0f;
+    return (int8_t)r;
+}
+
+/* Weight side, run once per weight ([P2] section 2.1: one scale per column of
+ * W, i.e. per output channel; [P2] section 6: quantized at load and reused).
+ * W is [K x N] row-major (leading dimension ldw). Output Wq is [N x K]
+ * (row n holds output channel n, K-contiguous), s[n] = max_k |W[k, n]|. */
+void ora_quantize_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                          int8_t *Wq, float *s)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float m = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(ora_half(W[k * ldw + n]));
+            if (a > m)
+                m = a;
+        }
+        s[n] = m;
+        if (m == 0.0f) {
+            for (int64_t k = 0; k < K; ++k)
+                Wq[n * K + k] = 0;
+            continue;
+        }
+        float inv = 127.0f / m;
+        for (int64_t k = 0; k < K; ++k)
+            Wq[n * K + k] = ora_quant(ora_half(W[k * ldw + n]), inv);
+    }
+}
+
+/* Outlier columns of X ([P2] section 2.3 and 4.2): column k is an outlier when
+ * some row i has |X[i, k]| >= threshold. Writes the ascending list of such k
+ * into idx (capacity K) and returns how many there are. */
+int32_t ora_find_outliers(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                          float threshold, int32_t *idx)
+{
+    int32_t count = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        int hit = 0;
+        for (int64_t i = 0; i < M && !hit; ++i)
+            if (fabsf(ora_half(X[i * ldx + k])) >= threshold)
+                hit = 1;
+        if (hit)
+            idx[count++] = (int32_t)k;
+    }
+    return count;
+}
+
+/* Activation side ([P2] section 2.1 and 2.3: one scale per row of the
+ * non-outlier part X_normal). m[i] = max over non-outlier k of |X[i, k]|;
+ * Xq[i, k] = 0 on outlier columns, else the quantized value. Xq is [M x K],
+ * K-contiguous. */
+void ora_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                          const int32_t *idx, int32_t count, int8_t *Xq, float *m)
+{
+    unsigned char *is_out = calloc((size_t)(K > 0 ? K : 1), 1);
+    for (int32_t p = 0; p < count; ++p)
+        is_out[idx[p]] = 1;
+    for (int64_t i = 0; i < M; ++i) {
+        float mi = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (is_out[k])
+                continue;
+            float a = fabsf(ora_half(X[i * ldx + k]));
+            if (a > mi)
+                mi = a;
+        }
+        m[i] = mi;
+        float inv = mi > 0.0f ? 127.0f / mi : 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (is_out[k] || mi == 0.0f)
+                Xq[i * K + k] = 0;
+            else
+                Xq[i * K + k] = ora_quant(ora_half(X[i * ldx + k]), inv);
+        }
+    }
+    free(is_out);
+}
+
+/* The int8 matmul with int32 accumulation ([P1] section 2.2): C[i, n] =
+ * sum_k Xq[i, k] * Wq[n, k]. Accumulates in int64 and reports (returns 1)
+ * if a result would not fit in int32; it never does for K <= 133144. */
+int ora_gemm_i8(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t N, int64_t K,
+                int32_t *C)
+{
+    int overflow = 0;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)Xq[i * K + k] * (int64_t)Wq[n * K + k];
+            if (acc > INT32_MAX || acc < INT32_MIN)
+                overflow = 1;
+            C[i * N + n] = (int32_t)acc;
+        }
+    return overflow;
+}
+
+/* The 16-bit outlier product and the merge ([P2] section 2.3; [P5] section
+ * 3.3): Y[i, n] = C[i, n] * m[i] * s[n] / 127^2 + sum_{k in O} X[i, k] W[k, n].
+ * Evaluated in fp64, outlier terms summed in ascending k. */
+void ora_merge(const int32_t *C, const float *m, const float *s,
+               const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+               const int32_t *idx, int32_t count, int64_t M, int64_t N, double *Y)
+{
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t n = 0; n < N; ++n) {
+            double yo = 0.0;
+            for (int32_t p = 0; p < count; ++p) {
+                int64_t k = idx[p];
+                yo += (double)ora_half(X[i * ldx + k]) * (double)ora_half(W[k * ldw + n]);
+            }
+            Y[i * N + n] = (double)C[i * N + n] * (double)m[i] * (double)s[n] / 16129.0 + yo;
+        }
+}
+
+/* One whole layer call, step by step in the order the pages give: find the
+ * outlier columns, quantize X by rows, int8 matmul, 16-bit outlier product,
+ * dequantize and add. Wq/s come from ora_quantize_colwise (load time). The
+ * intermediates are returned through the caller's buffers. Returns the outlier
+ * count, or -1 if an int32 accumulator would overflow. */
+int32_t ora_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                   const uint16_t *W, int64_t ldw, int64_t N,
+                   const int8_t *Wq, const float *s, float threshold,
+                   int32_t *idx, int8_t *Xq, float *m, int32_t *C, double *Y)
+{
+    int32_t count = ora_find_outliers(X, M, K, ldx, threshold, idx);
+    ora_quantize_rowwise(X, M, K, ldx, idx, count, Xq, m);
+    if (ora_gemm_i8(Xq, Wq, M, N, K, C))
+        return -1;
+    ora_merge(C, m, s, X, ldx, W, ldw, idx, count, M, N, Y);
+    return count;
+}

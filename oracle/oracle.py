@@ -1,0 +1,150 @@
+"""ctypes wrapper around the plain-C oracle (test infrastructure only).
+
+Each function calls one step of llmint8_oracle.c on numpy arrays. fp16 inputs
+are passed as their IEEE binary16 bit patterns (numpy float16 or uint16).
+`linear` composes the steps in the order the pages give them: outlier columns,
+row-wise quantization of X, int8 matmul, 16-bit outlier product, merge.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        lib = C.CDLL(_build.LIB)
+        p = C.c_void_p
+        i64 = C.c_int64
+        lib.ora_half_to_float.argtypes = [p, i64, p]
+        lib.ora_half_to_float.restype = None
+        lib.ora_quantize_colwise.argtypes = [p, i64, i64, i64, p, p]
+        lib.ora_quantize_colwise.restype = None
+        lib.ora_find_outliers.argtypes = [p, i64, i64, i64, C.c_float, p]
+        lib.ora_find_outliers.restype = C.c_int32
+        lib.ora_quantize_rowwise.argtypes = [p, i64, i64, i64, p, C.c_int32, p, p]
+        lib.ora_quantize_rowwise.restype = None
+        lib.ora_gemm_i8.argtypes = [p, p, i64, i64, i64, p]
+        lib.ora_gemm_i8.restype = C.c_int
+        lib.ora_merge.argtypes = [p, p, p, p, i64, p, i64, p, C.c_int32, i64, i64, p]
+        lib.ora_merge.restype = None
+        _lib = lib
+    return _lib
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("fp16 input must be float16 or uint16 bit patterns")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def half_to_float(h: np.ndarray) -> np.ndarray:
+    h = _bits(h)
+    out = np.empty(h.shape, np.float32)
+    _load().ora_half_to_float(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def quantize_colwise(W: np.ndarray):
+    """W fp16 [K, N] -> (Wq int8 [N, K], s float32 [N])."""
+    W = _bits(W)
+    K, N = W.shape
+    Wq = np.empty((N, K), np.int8)
+    s = np.empty(N, np.float32)
+    _load().ora_quantize_colwise(_ptr(W), K, N, N, _ptr(Wq), _ptr(s))
+    return Wq, s
+
+
+def find_outliers(X: np.ndarray, threshold: float) -> np.ndarray:
+    """X fp16 [M, K] -> ascending int32 outlier column indices."""
+    X = _bits(X)
+    M, K = X.shape
+    idx = np.empty(max(K, 1), np.int32)
+    n = _load().ora_find_outliers(_ptr(X), M, K, K, float(threshold), _ptr(idx))
+    return idx[:n].copy()
+
+
+def quantize_rowwise(X: np.ndarray, idx: np.ndarray | None = None):
+    """X fp16 [M, K], outlier columns -> (Xq int8 [M, K], m float32 [M])."""
+    X = _bits(X)
+    M, K = X.shape
+    idx = np.ascontiguousarray(np.zeros(0, np.int32) if idx is None else idx, dtype=np.int32)
+    Xq = np.empty((M, K), np.int8)
+    m = np.empty(M, np.float32)
+    _load().ora_quantize_rowwise(_ptr(X), M, K, K, _ptr(idx), int(idx.size), _ptr(Xq), _ptr(m))
+    return Xq, m
+
+
+def gemm_i8(Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """Xq int8 [M, K], Wq int8 [N, K] -> C int32 [M, N] = Xq . Wq^T."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    Wq = np.ascontiguousarray(Wq, dtype=np.int8)
+    M, K = Xq.shape
+    N, K2 = Wq.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    Cm = np.empty((M, N), np.int32)
+    if _load().ora_gemm_i8(_ptr(Xq), _ptr(Wq), M, N, K, _ptr(Cm)):
+        raise OverflowError("int32 accumulator overflow")
+    return Cm
+
+
+def merge(Cm: np.ndarray, m: np.ndarray, s: np.ndarray, X: np.ndarray, W: np.ndarray,
+          idx: np.ndarray) -> np.ndarray:
+    """Dequantize C and add the fp16 outlier product -> Y float64 [M, N]."""
+    X = _bits(X)
+    W = _bits(W)
+    Cm = np.ascontiguousarray(Cm, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    M, N = Cm.shape
+    Y = np.empty((M, N), np.float64)
+    _load().ora_merge(_ptr(Cm), _ptr(m), _ptr(s), _ptr(X), X.shape[1], _ptr(W), W.shape[1],
+                      _ptr(idx), int(idx.size), M, N, _ptr(Y))
+    return Y
+
+
+def linear(X: np.ndarray, W: np.ndarray, threshold: float, Wq=None, s=None) -> dict:
+    """The whole layer. Returns every intermediate the GPU path also exposes."""
+    if Wq is None or s is None:
+        Wq, s = quantize_colwise(W)
+    idx = find_outliers(X, threshold)
+    Xq, m = quantize_rowwise(X, idx)
+    Cm = gemm_i8(Xq, Wq)
+    Y = merge(Cm, m, s, X, W, idx)
+    return dict(idx=idx, Xq=Xq, m=m, Wq=Wq, s=s, C=Cm, Y=Y)
+
+
+def linear_rows(X: np.ndarray, W: np.ndarray, threshold: float, rows, Wq=None, s=None) -> dict:
+    """The layer's results for selected rows of X only.
+
+    The outlier set is a property of the whole X, so it is found on all rows;
+    every later step is independent per row and runs on the selected rows.
+    """
+    if Wq is None or s is None:
+        Wq, s = quantize_colwise(W)
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = find_outliers(X, threshold)
+    Xs = np.ascontiguousarray(_bits(X)[rows])
+    Xq, m = quantize_rowwise(Xs, idx)
+    Cm = gemm_i8(Xq, Wq)
+    Y = merge(Cm, m, s, Xs, W, idx)
+    return dict(rows=rows, idx=idx, Xq=Xq, m=m, Wq=Wq, s=s, C=Cm, Y=Y)

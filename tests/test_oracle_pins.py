@@ -1,0 +1,285 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+None of these tests retypes the oracle's formulas: they check it against the
+pages' worked example and hand-derived fixtures (tests/golden/), library
+routines on special cases that reduce to them (numpy matmul, numpy's fp16
+decoding), brute-force searches on tiny inputs, closed forms and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from golden_io import floats, ints, load
+
+
+def f16(rows):
+    return np.array(rows, dtype=np.float16)
+
+
+# --- fp16 decoding -------------------------------------------------------------
+
+def test_half_decode_every_pattern():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.half_to_float(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    # bitwise, so signed zeros and subnormals are pinned too
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# --- the quantizer: page values and hand-derived values --------------------------
+
+def test_worked_example_codearts_section2():
+    g = load("p5_worked_example.txt")
+    X = f16([floats(g["x"])])
+    idx = oracle.find_outliers(X, float(g["threshold"][0]))
+    assert idx.size == 0
+    Xq, m = oracle.quantize_rowwise(X, idx)
+    assert Xq[0].tolist() == ints(g["q"])
+    assert round(127.0 / float(m[0]), 2) == float(g["scale_printed"][0])
+    deq = Xq[0].astype(np.float64) * float(m[0]) / 127.0
+    assert [round(float(v), 2) for v in deq] == floats(g["dequantized_printed"])
+
+
+def test_derived_row_with_outlier_column():
+    g = load("derived_tau6.txt")
+    X = f16([floats(g["x"])])
+    idx = oracle.find_outliers(X, float(g["threshold"][0]))
+    assert idx.tolist() == ints(g["outliers"])
+    Xq, m = oracle.quantize_rowwise(X, idx)
+    assert float(m[0]) == float(g["absmax"][0])
+    assert Xq[0].tolist() == ints(g["q"])
+
+
+def test_round_half_to_even_ties():
+    g = load("rne_ties.txt")
+    X = f16([floats(g["x"])])
+    Xq, _ = oracle.quantize_rowwise(X, oracle.find_outliers(X, math.inf))
+    assert Xq[0].tolist() == ints(g["q"])
+
+
+def test_resolution_loss_closed_form_walkthrough_section_2_2():
+    # A column max of 60 next to values of 3 leaves 3/60*127 ~ 6 levels for them
+    # (2kiu.com walkthrough, section 2.2); isolating the 60 restores all 127.
+    X = f16([[60.0, 3.0, -3.0, 1.5]])
+    Xq, m = oracle.quantize_rowwise(X, oracle.find_outliers(X, math.inf))
+    assert m[0] == 60.0 and Xq[0].tolist() == [127, 6, -6, 3]
+    assert abs(3.0 / 60.0 * 127.0 - 6.35) < 1e-12
+    idx = oracle.find_outliers(X, 6.0)
+    Xq, m = oracle.quantize_rowwise(X, idx)
+    assert idx.tolist() == [0] and m[0] == 3.0 and Xq[0].tolist() == [0, 127, -127, 64]
+
+
+def _nearest_even_search(v: float) -> int:
+    """The integer of [-127, 127] closest to v; ties go to the even one."""
+    best, best_d = None, None
+    for q in range(-127, 128):
+        d = abs(v - q)
+        if best is None or d < best_d or (d == best_d and q % 2 == 0):
+            best, best_d = q, d
+    return best
+
+
+def test_quantizer_brute_force_rounding_and_clamp():
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        K = int(rng.integers(1, 24))
+        x = (rng.standard_normal(K) * rng.choice([0.01, 1.0, 50.0])).astype(np.float16)
+        if trial % 5 == 0:
+            x[rng.integers(K)] = np.float16(0.5) * np.float16(rng.integers(-9, 9))
+        X = x[None, :]
+        Xq, m = oracle.quantize_rowwise(X, np.zeros(0, np.int32))
+        amax = np.float32(np.max(np.abs(x.astype(np.float32))))
+        assert m[0] == amax
+        if amax == 0:
+            assert not Xq.any()
+            continue
+        inv = np.float32(127.0) / amax
+        for k in range(K):
+            v = float(np.float32(x[k]) * inv)
+            assert Xq[0, k] == _nearest_even_search(v)
+
+
+def test_reconstruction_error_bound():
+    # |x - q*m/127| <= m/254 + m*2^-23 for every non-outlier entry (half a
+    # quantization step, plus the two fp32 roundings inside x * fl(127/m)).
+    X, _, planted = workloads.random_case(64, 512, 8, seed=5, n_out=6)
+    idx = oracle.find_outliers(X, 6.0)
+    Xq, m = oracle.quantize_rowwise(X, idx)
+    xf = X.astype(np.float64)
+    keep = np.ones(X.shape[1], bool)
+    keep[idx] = False
+    err = np.abs(xf - Xq.astype(np.float64) * m[:, None].astype(np.float64) / 127.0)[:, keep]
+    bound = (m.astype(np.float64) / 254.0 + m.astype(np.float64) * 2.0 ** -23)[:, None]
+    assert np.all(err <= bound)
+
+
+# --- outlier detection -------------------------------------------------------------
+
+def test_threshold_is_inclusive():
+    X = np.full((5, 16), 0.25, np.float16)
+    X[3, 7] = 6.0
+    assert oracle.find_outliers(X, 6.0).tolist() == [7]
+    just_above = float(np.nextafter(np.float32(6.0), np.float32(np.inf)))
+    assert oracle.find_outliers(X, just_above).size == 0
+
+
+def test_threshold_edges():
+    X, _, _ = workloads.random_case(9, 48, 4, seed=2, n_out=3)
+    assert oracle.find_outliers(X, math.inf).size == 0
+    assert oracle.find_outliers(X, 0.0).tolist() == list(range(48))
+    assert oracle.find_outliers(X, -1.0).tolist() == list(range(48))
+
+
+def test_outliers_match_brute_force_and_plants():
+    wl = workloads.WORKLOADS["tiny"]
+    X = workloads.make_x(wl)
+    idx = oracle.find_outliers(X, wl.threshold)
+    brute = [k for k in range(wl.K)
+             if any(abs(float(X[i, k])) >= wl.threshold for i in range(wl.M))]
+    assert idx.tolist() == brute == list(wl.fixed_cols)
+
+
+def test_outlier_set_shrinks_as_threshold_grows():
+    X, _, _ = workloads.random_case(40, 256, 4, seed=3, n_out=5)
+    prev = None
+    for tau in [0.0, 1.0, 2.0, 3.0, 4.0, 6.0, 20.0, math.inf]:
+        cur = set(oracle.find_outliers(X, tau).tolist())
+        if prev is not None:
+            assert cur <= prev
+        prev = cur
+
+
+# --- special cases that reduce to a library matmul -------------------------------
+
+def _exact_integer_case(rng, M, K, N):
+    """Integer-valued X, W (|v| <= 127) with a +-127 in every row of X and every
+    column of W, so both scales are exactly 1 and quantization is exact."""
+    X = rng.integers(-127, 128, size=(M, K)).astype(np.float64)
+    X[np.arange(M), rng.integers(0, K, M)] = 127.0 * rng.choice([-1, 1], M)
+    W = rng.integers(-127, 128, size=(K, N)).astype(np.float64)
+    W[rng.integers(0, K, N), np.arange(N)] = 127.0 * rng.choice([-1, 1], N)
+    return X, W
+
+
+def test_threshold_inf_is_plain_vectorwise_int8():
+    # With threshold +inf nothing is an outlier and the layer is the pure
+    # vector-wise int8 product (Lightning Fabric page, section 2.2). On exact
+    # integer data with unit scales it must equal X @ W exactly.
+    rng = np.random.default_rng(7)
+    X, W = _exact_integer_case(rng, 13, 37, 11)
+    r = oracle.linear(X.astype(np.float16), W.astype(np.float16), math.inf)
+    assert r["idx"].size == 0
+    ref = X @ W
+    assert np.array_equal(r["C"].astype(np.float64), ref)
+    assert np.array_equal(r["Y"], ref)
+    # power-of-two scaling of rows of X and columns of W: the int8 operands do
+    # not change, the scales absorb the powers exactly, Y scales exactly.
+    rs = 2.0 ** rng.integers(-6, 3, size=(13, 1))
+    cs = 2.0 ** rng.integers(-6, 3, size=(1, 11))
+    r2 = oracle.linear((X * rs).astype(np.float16), (W * cs).astype(np.float16), math.inf)
+    assert np.array_equal(r2["Xq"], r["Xq"]) and np.array_equal(r2["Wq"], r["Wq"])
+    assert np.array_equal(r2["m"].astype(np.float64), 127.0 * rs[:, 0])
+    assert np.array_equal(r2["s"].astype(np.float64), 127.0 * cs[0])
+    assert np.array_equal(r2["Y"], ref * rs * cs)
+
+
+def test_all_outlier_columns_reduce_to_fp16_matmul():
+    # threshold 0: every column is an outlier, the int8 part is empty and the
+    # layer is the 16-bit matmul of X and W.
+    X, W, _ = workloads.random_case(21, 96, 17, seed=4, n_out=2)
+    r = oracle.linear(X, W, 0.0)
+    assert r["idx"].tolist() == list(range(96))
+    assert not r["Xq"].any() and not r["m"].any() and not r["C"].any()
+    ref = X.astype(np.float64) @ W.astype(np.float64)
+    np.testing.assert_allclose(r["Y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_int8_matmul_matches_numpy():
+    rng = np.random.default_rng(8)
+    for M, K, N in [(1, 1, 1), (3, 70, 5), (17, 300, 9), (40, 64, 33)]:
+        Xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        Wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+        ref = Xq.astype(np.int64) @ Wq.astype(np.int64).T
+        assert np.array_equal(oracle.gemm_i8(Xq, Wq), ref)
+    big = np.full((2, 133144), 127, np.int8)
+    assert oracle.gemm_i8(big, big)[0, 0] == 127 * 127 * 133144
+
+
+def test_hand_worked_layer_call():
+    g = load("hand_linear.txt")
+    X = f16([floats(g["X"])])
+    W = f16([floats(r) for r in g["W_rows"]])
+    r = oracle.linear(X, W, float(g["threshold"][0]))
+    assert r["idx"].tolist() == ints(g["outliers"])
+    assert r["m"].tolist() == floats(g["absmax_x"])
+    assert r["Xq"][0].tolist() == ints(g["Xq"])
+    assert r["s"].tolist() == floats(g["absmax_w"])
+    assert r["Wq"].tolist() == [ints(row) for row in g["Wq_rows"]]
+    assert r["C"][0].tolist() == ints(g["C"])
+    np.testing.assert_allclose(r["Y"][0], floats(g["Y"]), rtol=1e-15, atol=0)
+
+
+# --- invariants ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_layer_invariants(seed):
+    X, W, planted = workloads.random_case(33, 160, 24, seed=seed, n_out=4)
+    r = oracle.linear(X, W, 6.0)
+    idx, Xq, m, C = r["idx"], r["Xq"], r["m"], r["C"]
+    assert set(planted.tolist()) <= set(idx.tolist())
+    assert np.all(np.abs(Xq.astype(np.int32)) <= 127)
+    assert not Xq[:, idx].any()
+    rows = np.nonzero(m > 0)[0]
+    assert np.all(np.abs(Xq[rows].astype(np.int32)).max(axis=1) == 127)
+    assert np.all(np.abs(r["Wq"].astype(np.int32)).max(axis=1)[r["s"] > 0] == 127)
+    assert np.all(np.abs(C.astype(np.int64)) <= 127 * 127 * (160 - idx.size))
+    # sign flips negate the integer results exactly (round-half-even is odd-symmetric)
+    rn = oracle.linear(-X, W, 6.0)
+    assert np.array_equal(rn["idx"], idx) and np.array_equal(rn["m"], m)
+    assert np.array_equal(rn["Xq"], -Xq) and np.array_equal(rn["C"], -C)
+    rw = oracle.linear(X, -W, 6.0)
+    assert np.array_equal(rw["Wq"], -r["Wq"]) and np.array_equal(rw["C"], -C)
+    np.testing.assert_allclose(rw["Y"], -r["Y"], rtol=0, atol=0)
+
+
+def test_joint_permutation_of_inner_dimension():
+    X, W, _ = workloads.random_case(12, 128, 20, seed=9, n_out=5)
+    perm = np.random.default_rng(1).permutation(128)
+    r = oracle.linear(X, W, 6.0)
+    rp = oracle.linear(np.ascontiguousarray(X[:, perm]), np.ascontiguousarray(W[perm]), 6.0)
+    assert sorted(perm[rp["idx"]].tolist()) == r["idx"].tolist()
+    assert np.array_equal(rp["m"], r["m"])
+    assert np.array_equal(rp["C"], r["C"])
+    np.testing.assert_allclose(rp["Y"], r["Y"], rtol=1e-12, atol=1e-12)
+
+
+def test_rows_are_independent_given_the_outlier_set():
+    X, W, _ = workloads.random_case(30, 96, 16, seed=12, n_out=3)
+    full = oracle.linear(X, W, 6.0)
+    rows = [0, 7, 29]
+    part = oracle.linear_rows(X, W, 6.0, rows)
+    assert np.array_equal(part["idx"], full["idx"])
+    assert np.array_equal(part["Xq"], full["Xq"][rows])
+    assert np.array_equal(part["C"], full["C"][rows])
+    assert np.array_equal(part["Y"], full["Y"][rows])
+
+
+def test_outlier_isolation_beats_per_tensor_int8():
+    # Qualitative (2kiu.com walkthrough section 2.2; codearts page sections 2
+    # and 4): one scale for the whole tensor loses the small values next to an
+    # outlier; the decomposition keeps them. Compared against exact X @ W.
+    wl = workloads.WORKLOADS["tiny"]
+    X, W = workloads.make_x(wl), workloads.make_w(wl)
+    exact = X.astype(np.float64) @ W.astype(np.float64)
+    y = oracle.linear(X, W, 6.0)["Y"]
+    xf, wf = X.astype(np.float64), W.astype(np.float64)
+    sx, sw = np.abs(xf).max() / 127, np.abs(wf).max() / 127
+    per_tensor = np.rint(xf / sx) @ np.rint(wf / sw) * sx * sw
+    e_mixed = np.linalg.norm(y - exact)
+    e_tensor = np.linalg.norm(per_tensor - exact)
+    assert e_mixed * 5 < e_tensor
