@@ -1,0 +1,183 @@
+"""MI355X (gfx950) LLM.int8() mixed-precision linear layer.
+
+Thin ctypes binding over libllmint8.so (include/llmint8.h). The Python
+functions carry the C entry points' names and do argument marshalling only:
+they check dtypes/devices, allocate outputs as torch tensors (PyTorch supplies
+device memory and the current HIP stream) and call the library, which runs
+every step of the layer in its own HIP kernels. There is no CPU fallback: if
+the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libllmint8.so")
+
+LLMINT8_OK = 0
+LLMINT8_ERR_INVALID_ARG = 1
+LLMINT8_ERR_UNSUPPORTED = 2
+LLMINT8_ERR_OVERFLOW = 3
+LLMINT8_ERR_WORKSPACE = 4
+LLMINT8_ERR_HIP = 5
+LLMINT8_MAX_K = 133144
+
+_lib = None
+
+
+class Llmint8Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> C.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = C.CDLL(LIB_PATH)
+        p, i64, f32, sz = C.c_void_p, C.c_int64, C.c_float, C.c_size_t
+        L.llmint8_quantize_colwise.argtypes = [p, i64, i64, i64, p, p, p]
+        L.llmint8_find_outliers_workspace_size.argtypes = [i64, i64]
+        L.llmint8_find_outliers_workspace_size.restype = sz
+        L.llmint8_find_outliers.argtypes = [p, i64, i64, i64, f32, p, p, p, sz, p]
+        L.llmint8_quantize_rowwise.argtypes = [p, i64, i64, i64, p, p, p, p, p]
+        L.llmint8_workspace_size.argtypes = [i64, i64, i64]
+        L.llmint8_workspace_size.restype = sz
+        L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p,
+                                     sz, p]
+        L.llmint8_status_string.argtypes = [C.c_int]
+        L.llmint8_status_string.restype = C.c_char_p
+        for name in ("llmint8_quantize_colwise", "llmint8_find_outliers",
+                     "llmint8_quantize_rowwise", "llmint8_linear"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def llmint8_status_string(status: int) -> str:
+    return lib().llmint8_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != LLMINT8_OK:
+        raise Llmint8Error(status, llmint8_status_string(status))
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(None)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def _ld(t: torch.Tensor, name: str) -> int:
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    return t.stride(0)
+
+
+def llmint8_quantize_colwise(W: torch.Tensor):
+    """fp16 W [K, N] -> (Wq int8 [N, K], col_absmax fp32 [N])."""
+    _need(W, "W", torch.float16, 2)
+    K, N = W.shape
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    s = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib().llmint8_quantize_colwise(_ptr(W), K, N, _ld(W, "W"), _ptr(Wq), _ptr(s),
+                                          _stream(W)))
+    return Wq, s
+
+
+def llmint8_find_outliers_workspace_size(M: int, K: int) -> int:
+    return int(lib().llmint8_find_outliers_workspace_size(M, K))
+
+
+def llmint8_find_outliers(X: torch.Tensor, threshold: float = 6.0, workspace=None):
+    """fp16 X [M, K] -> (idx int32 [K] ascending in idx[:count], count int32 [1]) on device."""
+    _need(X, "X", torch.float16, 2)
+    M, K = X.shape
+    idx = torch.empty((K,), dtype=torch.int32, device=X.device)
+    count = torch.empty((1,), dtype=torch.int32, device=X.device)
+    need = llmint8_find_outliers_workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    _check(lib().llmint8_find_outliers(_ptr(X), M, K, _ld(X, "X"), float(threshold), _ptr(idx),
+                                       _ptr(count), _ptr(workspace), workspace.numel(),
+                                       _stream(X)))
+    return idx, count
+
+
+def llmint8_quantize_rowwise(X: torch.Tensor, idx: torch.Tensor | None = None,
+                             count: torch.Tensor | None = None):
+    """fp16 X [M, K] (+ outlier idx/count on device) -> (Xq int8 [M, K], row_absmax fp32 [M])."""
+    _need(X, "X", torch.float16, 2)
+    if (idx is None) != (count is None):
+        raise ValueError("idx and count go together")
+    if idx is not None:
+        _need(idx, "idx", torch.int32, 1)
+        _need(count, "count", torch.int32, 1)
+    M, K = X.shape
+    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    m = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().llmint8_quantize_rowwise(_ptr(X), M, K, _ld(X, "X"), _ptr(idx), _ptr(count),
+                                          _ptr(Xq), _ptr(m), _stream(X)))
+    return Xq, m
+
+
+def llmint8_workspace_size(M: int, K: int, N: int) -> int:
+    return int(lib().llmint8_workspace_size(M, K, N))
+
+
+def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
+                   W: torch.Tensor | None, threshold: float = 6.0, *, Y=None, workspace=None,
+                   outlier_count: torch.Tensor | None = None,
+                   C_debug: torch.Tensor | None = None) -> torch.Tensor:
+    """The whole LLM.int8() layer: fp16 X [M, K] with Wq [N, K], col_absmax [N] and the
+    fp16 weight W [K, N] (rows in the outlier set feed the 16-bit product) -> fp16 Y [M, N]."""
+    _need(X, "X", torch.float16, 2)
+    _need(Wq, "Wq", torch.int8, 2)
+    _need(col_absmax, "col_absmax", torch.float32, 1)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or not Wq.is_contiguous():
+        raise ValueError("Wq must be contiguous [N, K]")
+    if W is not None:
+        _need(W, "W", torch.float16, 2)
+        if tuple(W.shape) != (K, N):
+            raise ValueError("W must be [K, N]")
+    elif not (math.isinf(threshold) and threshold > 0):
+        raise ValueError("W may be omitted only with threshold=+inf")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    for name, t in (("outlier_count", outlier_count), ("C_debug", C_debug)):
+        if t is not None:
+            _need(t, name, torch.int32)
+    if workspace is None:
+        workspace = torch.empty((llmint8_workspace_size(M, K, N),), dtype=torch.uint8,
+                                device=X.device)
+    _check(lib().llmint8_linear(
+        _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
+        _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
+        _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X)))
+    return Y

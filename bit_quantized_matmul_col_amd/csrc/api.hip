@@ -1,0 +1,178 @@
+// C ABI of the LLM.int8() linear layer: argument checks, workspace layout and
+// the launch sequence. Every check runs before the first HIP call, so a
+// rejected call enqueues nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "internal.hpp"
+#include "llmint8.h"
+
+#define LLMINT8_EXPORT extern "C" __attribute__((visibility("default")))
+
+using namespace llmint8;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Offsets (bytes) of the regions a call carves out of its workspace.
+struct Layout {
+  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, total;
+};
+
+Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer) {
+  const DetectPlan p = detect_plan(M, K);
+  Layout L{};
+  size_t o = 0;
+  L.pmask = o;
+  o += up((size_t)p.row_chunks * (size_t)p.kw * 4);
+  L.omask = o;
+  o += up((size_t)p.kw * 4);
+  L.wprefix = o;
+  o += up((size_t)p.kw * 4);
+  L.nidx = o;
+  o += up((size_t)K * 4);
+  if (layer) {
+    L.idx = o;
+    o += up((size_t)K * 4);
+    L.count = o;
+    o += up(64);
+    L.xq = o;
+    o += up((size_t)M * (size_t)K);
+    L.m = o;
+    o += up((size_t)M * 4);
+    L.xo = o;
+    o += up((size_t)M * (size_t)K * 2);
+    L.wqc = o;
+    o += up((size_t)N * (size_t)K);
+  }
+  L.total = o;
+  return L;
+}
+
+// Shape rules shared by the calls that read an fp16 [rows x cols] matrix.
+int check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld) {
+  if (!p || rows <= 0 || cols <= 0 || ld < cols) return LLMINT8_ERR_INVALID_ARG;
+  if (rows >= kMaxDim || cols >= kMaxDim || ld >= kMaxDim) return LLMINT8_ERR_INVALID_ARG;
+  if (!aligned16(p) || ld % 8 != 0) return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+int check_k(int64_t K) {
+  if (K > LLMINT8_MAX_K) return LLMINT8_ERR_OVERFLOW;
+  if (K % 16 != 0) return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP; }
+
+}  // namespace
+
+LLMINT8_EXPORT const char *llmint8_status_string(int status) {
+  switch (status) {
+    case LLMINT8_OK: return "LLMINT8_OK";
+    case LLMINT8_ERR_INVALID_ARG: return "LLMINT8_ERR_INVALID_ARG: null pointer, bad size or NaN threshold";
+    case LLMINT8_ERR_UNSUPPORTED: return "LLMINT8_ERR_UNSUPPORTED: alignment or multiple-of rule broken";
+    case LLMINT8_ERR_OVERFLOW: return "LLMINT8_ERR_OVERFLOW: K too large for int32 accumulation";
+    case LLMINT8_ERR_WORKSPACE: return "LLMINT8_ERR_WORKSPACE: workspace missing or too small";
+    case LLMINT8_ERR_HIP: return "LLMINT8_ERR_HIP: HIP launch or runtime error";
+    default: return "LLMINT8: unknown status";
+  }
+}
+
+LLMINT8_EXPORT int llmint8_quantize_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                            int8_t *Wq, float *col_absmax, void *stream) {
+  int st = check_matrix(W, K, N, ldw);
+  if (st) return st;
+  if (!Wq || !col_absmax) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  return hip_status(launch_colwise(W, K, N, ldw, Wq, col_absmax, (hipStream_t)stream));
+}
+
+LLMINT8_EXPORT size_t llmint8_find_outliers_workspace_size(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || M >= kMaxDim || K > LLMINT8_MAX_K) return 0;
+  return make_layout(M, K, 0, false).total;
+}
+
+LLMINT8_EXPORT int llmint8_find_outliers(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                         float threshold, int32_t *idx, int32_t *count,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if (!idx || !count || std::isnan(threshold)) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (!aligned16(idx) || !aligned16(count)) return LLMINT8_ERR_UNSUPPORTED;
+  const Layout L = make_layout(M, K, 0, false);
+  if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
+  uint8_t *ws = (uint8_t *)workspace;
+  DetectOut d{(uint32_t *)(ws + L.pmask), (uint32_t *)(ws + L.omask), (int32_t *)(ws + L.wprefix),
+              idx, (int32_t *)(ws + L.nidx), count, nullptr};
+  return hip_status(launch_detect(X, M, K, ldx, threshold, detect_plan(M, K), d,
+                                  (hipStream_t)stream));
+}
+
+LLMINT8_EXPORT int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                            const int32_t *idx, const int32_t *count, int8_t *Xq,
+                                            float *row_absmax, void *stream) {
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if (!Xq || !row_absmax || (!idx) != (!count)) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (!aligned16(Xq) || !aligned16(row_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if (idx && (!aligned16(idx) || !aligned16(count))) return LLMINT8_ERR_UNSUPPORTED;
+  return hip_status(
+      launch_rowquant_idx(X, M, K, ldx, idx, count, Xq, row_absmax, (hipStream_t)stream));
+}
+
+LLMINT8_EXPORT size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
+  return make_layout(M, K, N, true).total;
+}
+
+LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                  const int8_t *Wq, const float *col_absmax, const uint16_t *W,
+                                  int64_t ldw, int64_t N, float threshold, uint16_t *Y,
+                                  int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if ((st = check_matrix(Y, M, N, ldy))) return st;
+  if (!Wq || !col_absmax || std::isnan(threshold)) return LLMINT8_ERR_INVALID_ARG;
+  if (!W && !(std::isinf(threshold) && threshold > 0)) return LLMINT8_ERR_INVALID_ARG;
+  if (W && (st = check_matrix(W, K, N, ldw))) return st;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if ((outlier_count_out && !aligned16(outlier_count_out)) || (C_debug && !aligned16(C_debug)))
+    return LLMINT8_ERR_UNSUPPORTED;
+  const Layout L = make_layout(M, K, N, true);
+  if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  const DetectPlan plan = detect_plan(M, K);
+  uint32_t *omask = (uint32_t *)(ws + L.omask);
+  int32_t *wprefix = (int32_t *)(ws + L.wprefix);
+  int32_t *idx = (int32_t *)(ws + L.idx);
+  int32_t *count = (int32_t *)(ws + L.count);
+  int8_t *xq = (int8_t *)(ws + L.xq);
+  float *m = (float *)(ws + L.m);
+  uint16_t *xo = (uint16_t *)(ws + L.xo);
+  int8_t *wqc = (int8_t *)(ws + L.wqc);
+
+  DetectOut d{(uint32_t *)(ws + L.pmask), omask, wprefix, idx, (int32_t *)(ws + L.nidx), count,
+              outlier_count_out};
+  hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
+  if (e == hipSuccess) e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, m, xo, K, s);
+  if (e == hipSuccess) e = launch_compact_wq(Wq, K, N, omask, wprefix, count, wqc, s);
+  if (e == hipSuccess) {
+    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, W, idx, count, Y, C_debug, M, N, K, K, ldw, ldy};
+    e = launch_gemm(g, s);
+  }
+  return hip_status(e);
+}

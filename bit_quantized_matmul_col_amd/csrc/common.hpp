@@ -1,0 +1,72 @@
+// Device helpers shared by the gfx950 kernels of the LLM.int8() linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llmint8 {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Workspace regions are carved at this alignment.
+constexpr size_t kAlign = 256;
+
+// Outlier share above which the int8 GEMM runs on compacted operands (the K - |O|
+// kept columns only): |O| * 100 >= K * kCompactPct. Compaction also needs the
+// compacted row to fit in LDS (K <= kCompactMaxK).
+constexpr int kCompactPct = 5;
+constexpr int kCompactMaxK = 32768;
+
+__host__ __device__ inline bool use_compaction(int count, int64_t K) {
+  return count > 0 && K <= kCompactMaxK && (int64_t)count * 100 >= K * kCompactPct;
+}
+
+__device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// fl32(127 / a) correctly rounded: the fp64 quotient of two fp32 values rounded
+// once more to fp32 equals the correctly rounded fp32 quotient (53 >= 2*24 + 2).
+__device__ inline float inv_scale(float a) { return (float)(127.0 / (double)a); }
+
+// Symmetric int8 code of x for the scale inv = fl32(127 / absmax): one fp32
+// multiply, round half to even, clamp to [-127, 127].
+__device__ inline int quant_i8(float x, float inv) {
+  float r = __builtin_rintf(x * inv);
+  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// Absolute values of the 8 fp16 in a 16-byte chunk, folded into a running max.
+__device__ inline void absmax8(const u32x4 &v, float *mx) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t w = v[e];
+    mx[2 * e] = __builtin_fmaxf(mx[2 * e], __builtin_fabsf(h2f((uint16_t)(w & 0xffffu))));
+    mx[2 * e + 1] = __builtin_fmaxf(mx[2 * e + 1], __builtin_fabsf(h2f((uint16_t)(w >> 16))));
+  }
+}
+
+__device__ inline float fp16_lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
+__device__ inline float fp16_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace llmint8

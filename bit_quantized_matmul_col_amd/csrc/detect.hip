@@ -1,0 +1,153 @@
+// Outlier-column detection for gfx950.
+//
+// A column k of X [M x K] is an outlier when some row has |X[i, k]| >= threshold
+// ("8-bit quantization of giant language models: LLM.int8()" walkthrough,
+// sections 2.3 and 4.2). HBM-bound: X is read once, 2MK bytes.
+//
+// Pass 1 (k_detect_partial): a block owns 512 columns (64 lanes x one 16-byte
+// chunk of 8 fp16) of one row chunk; its 4 waves stride over the chunk's rows,
+// so every wave load is a fully coalesced 1 KB row segment. The running column
+// maxima are compared with the threshold once at the end (max >= t is the same
+// test as "some entry >= t") and stored as 16 mask words per row chunk.
+// Pass 2 (k_detect_finish): one block ORs the row-chunk masks, scans the
+// per-word popcounts and writes the ascending outlier list, the ascending kept
+// list, the per-word prefix and the count. No atomics, no host round trip.
+#include "internal.hpp"
+
+namespace llmint8 {
+
+namespace {
+
+constexpr int kTileCols = 512;
+constexpr int kMaxRowChunks = 64;
+
+__global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restrict__ X, int64_t M,
+                                                        int64_t K, int64_t ldx, float threshold,
+                                                        int rows_per_chunk, int64_t kw,
+                                                        uint32_t *__restrict__ pmask) {
+  const int t = threadIdx.x;
+  const int c = t & 63;   // 16-byte chunk within the tile
+  const int rp = t >> 6;  // row phase 0..3
+  const int64_t col = (int64_t)blockIdx.x * kTileCols + (int64_t)c * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r1 = (r0 + rows_per_chunk < M) ? r0 + rows_per_chunk : M;
+
+  float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col < K) {
+    const uint16_t *p = X + col;
+    int64_t r = r0 + rp;
+    for (; r + 12 < r1; r += 16) {
+      u32x4 v0 = *(const u32x4 *)(p + r * ldx);
+      u32x4 v1 = *(const u32x4 *)(p + (r + 4) * ldx);
+      u32x4 v2 = *(const u32x4 *)(p + (r + 8) * ldx);
+      u32x4 v3 = *(const u32x4 *)(p + (r + 12) * ldx);
+      absmax8(v0, mx);
+      absmax8(v1, mx);
+      absmax8(v2, mx);
+      absmax8(v3, mx);
+    }
+    for (; r < r1; r += 4) absmax8(*(const u32x4 *)(p + r * ldx), mx);
+  }
+  unsigned bits = 0;
+  if (col < K && rp < r1 - r0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (mx[e] >= threshold) bits |= 1u << e;
+  }
+  __shared__ uint8_t sb[4][64];
+  sb[rp][c] = (uint8_t)bits;
+  __syncthreads();
+  if (t < kTileCols / 32) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = 4 * t + j;
+      word |= (uint32_t)(sb[0][ch] | sb[1][ch] | sb[2][ch] | sb[3][ch]) << (8 * j);
+    }
+    const int64_t w = (int64_t)blockIdx.x * (kTileCols / 32) + t;
+    if (w < kw) pmask[(int64_t)blockIdx.y * kw + w] = word;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restrict__ pmask,
+                                                        int row_chunks, int64_t K, int64_t kw,
+                                                        DetectOut out) {
+  const int t = threadIdx.x;
+  const int64_t per = (kw + 1023) / 1024;
+  const int64_t w0 = (int64_t)t * per;
+  const int64_t w1 = (w0 + per < kw) ? w0 + per : kw;
+
+  int local = 0;
+  for (int64_t w = w0; w < w1; ++w) {
+    uint32_t v = 0;
+    for (int rc = 0; rc < row_chunks; ++rc) v |= pmask[(int64_t)rc * kw + w];
+    const int64_t valid = K - 32 * w;  // columns of this word inside K
+    if (valid < 32) v &= (1u << valid) - 1u;
+    out.omask[w] = v;
+    local += __builtin_popcount(v);
+  }
+
+  // Block-wide exclusive scan of the per-thread counts.
+  __shared__ int wsum[16];
+  const int lane = t & 63, wv = t >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    before += (i < wv) ? wsum[i] : 0;
+    total += wsum[i];
+  }
+  int pos = before + incl - local;
+
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t v = out.omask[w];
+    out.wprefix[w] = pos;
+    const int nb = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
+    for (int b = 0; b < nb; ++b) {
+      const int32_t k = (int32_t)(32 * w + b);
+      if (v & (1u << b))
+        out.idx[pos++] = k;
+      else
+        out.nidx[k - pos] = k;
+    }
+  }
+  if (t == 0) {
+    *out.count = total;
+    if (out.count_copy) *out.count_copy = total;
+  }
+}
+
+}  // namespace
+
+DetectPlan detect_plan(int64_t M, int64_t K) {
+  DetectPlan p;
+  p.kw = (K + 31) / 32;
+  p.col_tiles = (int)((K + kTileCols - 1) / kTileCols);
+  // Aim for >= 8 rows per block phase and at most kMaxRowChunks partial masks.
+  int64_t chunks = (M + 31) / 32;
+  if (chunks > kMaxRowChunks) chunks = kMaxRowChunks;
+  if (chunks < 1) chunks = 1;
+  p.rows_per_chunk = (int)((M + chunks - 1) / chunks);
+  p.row_chunks = (int)((M + p.rows_per_chunk - 1) / p.rows_per_chunk);
+  return p;
+}
+
+hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
+                         const DetectPlan &plan, const DetectOut &out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_detect_partial, dim3(plan.col_tiles, plan.row_chunks), dim3(256), 0, stream,
+                     X, M, K, ldx, threshold, plan.rows_per_chunk, plan.kw, out.pmask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_detect_finish, dim3(1), dim3(1024), 0, stream, (const uint32_t *)out.pmask,
+                     plan.row_chunks, K, plan.kw, out);
+  return hipGetLastError();
+}
+
+}  // namespace llmint8

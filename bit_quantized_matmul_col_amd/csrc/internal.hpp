@@ -1,0 +1,72 @@
+// Internal launchers of the gfx950 kernels. Each returns hipSuccess or the
+// error of its launch; none synchronizes.
+#pragma once
+
+#include "common.hpp"
+
+namespace llmint8 {
+
+// Outlier detection is split over row chunks: each (column tile, row chunk)
+// block writes one partial column bitmask; a single block ORs them.
+struct DetectPlan {
+  int row_chunks;
+  int rows_per_chunk;
+  int col_tiles;
+  int64_t kw;  // 32-bit mask words covering K columns
+};
+DetectPlan detect_plan(int64_t M, int64_t K);
+
+struct DetectOut {
+  uint32_t *pmask;   // [row_chunks x kw] partial masks (scratch)
+  uint32_t *omask;   // [kw] outlier bitmask, bit k%32 of word k/32
+  int32_t *wprefix;  // [kw] outliers in words before w
+  int32_t *idx;      // [K] ascending outlier columns
+  int32_t *nidx;     // [K] ascending kept columns
+  int32_t *count;    // [1]
+  int32_t *count_copy;  // optional second copy of the count
+};
+
+hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
+                         const DetectPlan &plan, const DetectOut &out, hipStream_t stream);
+
+// Row quantization for the public call: outlier columns from an index list.
+hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                               const int32_t *idx, const int32_t *count, int8_t *Xq, float *m,
+                               hipStream_t stream);
+
+// Row quantization inside the layer: outlier columns from the detection
+// bitmask; also gathers the outlier columns into xo [M x ldo] and, when the
+// outlier share calls for it, writes compacted rows (K - |O| kept columns).
+hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                 const uint32_t *omask, const int32_t *wprefix,
+                                 const int32_t *count, int8_t *Xq, float *m, uint16_t *xo,
+                                 int64_t ldo, hipStream_t stream);
+
+// Column absmax + quantize + transpose of W [K x N] into Wq [N x K].
+hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
+                          float *s, hipStream_t stream);
+
+// Compacted copy Wqc [N x K] (first K - |O| bytes of each row) of Wq without
+// the outlier columns; a no-op unless the outlier share calls for it.
+hipError_t launch_compact_wq(const int8_t *Wq, int64_t K, int64_t N, const uint32_t *omask,
+                             const int32_t *wprefix, const int32_t *count, int8_t *Wqc,
+                             hipStream_t stream);
+
+struct GemmArgs {
+  const int8_t *xq;      // [M x K] int8 (compacted rows when compaction is on)
+  const int8_t *wq;      // [N x K] int8, caller's
+  const int8_t *wqc;     // [N x K] int8 compacted copy (workspace)
+  const float *m;        // [M]
+  const float *s;        // [N]
+  const uint16_t *xo;    // [M x ldo] fp16 gathered outlier columns
+  const uint16_t *w;     // [K x ldw] fp16 original weight (rows in O are read)
+  const int32_t *idx;    // [K] outlier columns
+  const int32_t *count;  // [1]
+  uint16_t *y;           // [M x ldy] fp16
+  int32_t *cdbg;         // optional [M x N] int32
+  int64_t M, N, K, ldo, ldw, ldy;
+};
+
+hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
+
+}  // namespace llmint8

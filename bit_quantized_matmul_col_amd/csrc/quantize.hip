@@ -1,0 +1,345 @@
+// Vector-wise int8 quantization kernels for gfx950 (all HBM-bound).
+//
+// The quantizer is the symmetric absmax one of the "LLM.int8() pitfalls" page
+// (codearts), section 1: q = round(x * 127 / absmax), with the round-then-clamp
+// order and the [-127, 127] range of the INT8-to-QLoRA page (cnnetsun),
+// sections 3.2 and 3.3. Vector-wise scales are per row of X and per column
+// (output channel) of W ("LLM.int8()" walkthrough, 2kiu.com, section 2.1); the
+// row scale of X ignores the outlier columns, which go the 16-bit way (same
+// page, section 2.3).
+#include "internal.hpp"
+
+namespace llmint8 {
+
+namespace {
+
+// Reduction of one float per thread to a block-wide max (256 threads).
+__device__ inline float block_max256(float v, float *red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// Outlier bits of the 8 columns of chunk ch (columns 8ch .. 8ch+7).
+__device__ inline unsigned chunk_bits(const uint32_t *mask, int64_t ch) {
+  return (mask[ch >> 2] >> ((ch & 3) * 8)) & 0xffu;
+}
+
+// Codes of the 8 fp16 of a chunk, outlier columns zeroed, packed little-endian.
+__device__ inline u32x2 quant_chunk(const u32x4 &v, unsigned obits, float inv, bool zero_row) {
+  u32x2 out = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = v[e >> 1];
+    const float x = (e & 1) ? fp16_hi(w) : fp16_lo(w);
+    int q = 0;
+    if (!zero_row && !((obits >> e) & 1u)) q = quant_i8(x, inv);
+    out[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+  }
+  return out;
+}
+
+// Public row quantization: one block per row; the outlier set is given as an
+// index list, turned into an LDS bitmask first.
+__global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict__ X, int64_t K,
+                                                      int64_t ldx, const int32_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ count_ptr,
+                                                      int8_t *__restrict__ Xq,
+                                                      float *__restrict__ m) {
+  extern __shared__ uint32_t smask[];
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t kw = (K + 31) / 32;
+  for (int64_t w = t; w < kw; w += 256) smask[w] = 0u;
+  __syncthreads();
+  int count = count_ptr ? *count_ptr : 0;
+  if (count > K) count = (int)K;
+  for (int p = t; p < count; p += 256) {
+    const int k = idx[p];
+    if (k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
+  }
+  __syncthreads();
+
+  const uint16_t *row = X + i * ldx;
+  const int64_t nch = K / 8;
+  float mx = 0.f;
+  for (int64_t ch = t; ch < nch; ch += 256) {
+    const u32x4 v = *(const u32x4 *)(row + ch * 8);
+    const unsigned ob = chunk_bits(smask, ch);
+    float c8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    absmax8(v, c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!((ob >> e) & 1u)) mx = __builtin_fmaxf(mx, c8[e]);
+  }
+  mx = block_max256(mx, red);
+  if (t == 0) m[i] = mx;
+  const bool zero_row = !(mx > 0.f);
+  const float inv = zero_row ? 0.f : inv_scale(mx);
+  int8_t *qrow = Xq + i * K;
+  for (int64_t ch = t; ch < nch; ch += 256) {
+    const u32x4 v = *(const u32x4 *)(row + ch * 8);
+    *(u32x2 *)(qrow + ch * 8) = quant_chunk(v, chunk_bits(smask, ch), inv, zero_row);
+  }
+}
+
+// Row quantization inside the layer. One block per row. Besides Xq and m it
+// gathers the row's outlier entries into xo (position = rank of the column in
+// the ascending outlier list) and, in compaction mode, writes the kept codes
+// contiguously (staged in LDS so the global stores stay 16-byte wide) with a
+// zeroed tail up to the next 16 bytes.
+__global__ __launch_bounds__(256) void k_rowquant_layer(
+    const uint16_t *__restrict__ X, int64_t K, int64_t ldx, const uint32_t *__restrict__ omask,
+    const int32_t *__restrict__ wprefix, const int32_t *__restrict__ count_ptr,
+    int8_t *__restrict__ Xq, float *__restrict__ m, uint16_t *__restrict__ xo, int64_t ldo) {
+  extern __shared__ u32x4 srow_v[];
+  uint8_t *srow = (uint8_t *)srow_v;
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const int t = threadIdx.x;
+  const int count = *count_ptr;
+  const bool compact = use_compaction(count, K);
+
+  const uint16_t *row = X + i * ldx;
+  const int64_t nch = K / 8;
+  float mx = 0.f;
+  for (int64_t ch = t; ch < nch; ch += 256) {
+    const u32x4 v = *(const u32x4 *)(row + ch * 8);
+    const unsigned ob = chunk_bits(omask, ch);
+    float c8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    absmax8(v, c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!((ob >> e) & 1u)) mx = __builtin_fmaxf(mx, c8[e]);
+  }
+  mx = block_max256(mx, red);
+  if (t == 0) m[i] = mx;
+  const bool zero_row = !(mx > 0.f);
+  const float inv = zero_row ? 0.f : inv_scale(mx);
+  int8_t *qrow = Xq + i * K;
+  uint16_t *orow = xo + i * ldo;
+
+  for (int64_t ch = t; ch < nch; ch += 256) {
+    const u32x4 v = *(const u32x4 *)(row + ch * 8);
+    const unsigned ob = chunk_bits(omask, ch);
+    const u32x2 q = quant_chunk(v, ob, inv, zero_row);
+    // rank of column 8ch in the outlier list
+    const int64_t wd = ch >> 2;
+    const int sh = (int)(ch & 3) * 8;
+    int before = wprefix[wd] + __builtin_popcount(sh ? (omask[wd] & ((1u << sh) - 1u)) : 0u);
+    if (!compact) *(u32x2 *)(qrow + ch * 8) = q;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t k = ch * 8 + e;
+      if ((ob >> e) & 1u) {
+        const uint32_t w = v[e >> 1];
+        orow[before] = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+        ++before;
+      } else if (compact) {
+        srow[k - before] = (uint8_t)((q[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      }
+    }
+  }
+  if (compact) {
+    const int64_t kk = K - count;
+    const int64_t kpad = (kk + 15) & ~(int64_t)15;
+    for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
+    __syncthreads();
+    for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
+      *(u32x4 *)(qrow + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
+  }
+}
+
+// Column absmax of W [K x N]: a block owns 512 columns of a row chunk, like the
+// detection pass; maxima are merged with an integer atomic max on the fp32 bit
+// patterns (order-independent for non-negative values, so deterministic).
+__global__ __launch_bounds__(256) void k_colabsmax(const uint16_t *__restrict__ W, int64_t K,
+                                                   int64_t N, int64_t ldw, int rows_per_chunk,
+                                                   unsigned *__restrict__ sbits) {
+  const int t = threadIdx.x;
+  const int c = t & 63, rp = t >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 512 + (int64_t)c * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r1 = (r0 + rows_per_chunk < K) ? r0 + rows_per_chunk : K;
+  float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col < N) {
+    const uint16_t *p = W + col;
+    int64_t r = r0 + rp;
+    for (; r + 12 < r1; r += 16) {
+      u32x4 v0 = *(const u32x4 *)(p + r * ldw);
+      u32x4 v1 = *(const u32x4 *)(p + (r + 4) * ldw);
+      u32x4 v2 = *(const u32x4 *)(p + (r + 8) * ldw);
+      u32x4 v3 = *(const u32x4 *)(p + (r + 12) * ldw);
+      absmax8(v0, mx);
+      absmax8(v1, mx);
+      absmax8(v2, mx);
+      absmax8(v3, mx);
+    }
+    for (; r < r1; r += 4) absmax8(*(const u32x4 *)(p + r * ldw), mx);
+  }
+  __shared__ float sm[4][512];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[rp][c * 8 + e] = mx[e];
+  __syncthreads();
+  for (int j = t; j < 512; j += 256) {
+    const int64_t n = (int64_t)blockIdx.x * 512 + j;
+    if (n < N) {
+      const float v = __builtin_fmaxf(__builtin_fmaxf(sm[0][j], sm[1][j]),
+                                      __builtin_fmaxf(sm[2][j], sm[3][j]));
+      atomicMax(&sbits[n], __builtin_bit_cast(unsigned, v));
+    }
+  }
+}
+
+__global__ void k_fill_u32(unsigned *__restrict__ p, int64_t n, unsigned v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Quantize and transpose a 128 (k) x 64 (n) tile of W into Wq [N x K]: read
+// 128-byte row segments of W, transpose the int8 codes through LDS, write
+// 128-byte segments of Wq rows.
+__global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W, int64_t K,
+                                                  int64_t N, int64_t ldw,
+                                                  const float *__restrict__ s,
+                                                  int8_t *__restrict__ Wq) {
+  constexpr int TK = 128, TN = 64, PITCH = TK + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t st[TN * PITCH];
+  __shared__ float sinv[TN];
+  __shared__ uint8_t szero[TN];
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * TK;
+  const int64_t n0 = (int64_t)blockIdx.y * TN;
+  if (t < TN) {
+    const int64_t n = n0 + t;
+    const float a = (n < N) ? s[n] : 0.f;
+    szero[t] = !(a > 0.f);
+    sinv[t] = (a > 0.f) ? inv_scale(a) : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = t + 256 * u;
+    const int r = q >> 3, ch = q & 7;
+    const int64_t k = k0 + r, n = n0 + ch * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k < K && n < N) v = *(const u32x4 *)(W + k * ldw + n);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int nl = ch * 8 + e;
+      const uint32_t w = v[e >> 1];
+      const float x = (e & 1) ? fp16_hi(w) : fp16_lo(w);
+      const int code = szero[nl] ? 0 : quant_i8(x, sinv[nl]);
+      st[nl * PITCH + r] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = t + 256 * u;
+    const int nl = q >> 3, ch = q & 7;
+    const int64_t n = n0 + nl, k = k0 + ch * 16;
+    if (n < N && k < K) *(u32x4 *)(Wq + n * K + k) = *(const u32x4 *)(st + nl * PITCH + ch * 16);
+  }
+}
+
+// Compacted copy of Wq rows without the outlier columns. One row per block
+// iteration: each thread compresses 32 bytes (one mask word) into LDS, then
+// the row goes out with 16-byte stores, its tail zeroed up to 16 bytes.
+__global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ Wq, int64_t K,
+                                                    int64_t N, const uint32_t *__restrict__ omask,
+                                                    const int32_t *__restrict__ wprefix,
+                                                    const int32_t *__restrict__ count_ptr,
+                                                    int8_t *__restrict__ Wqc) {
+  extern __shared__ u32x4 srow_v[];
+  uint8_t *srow = (uint8_t *)srow_v;
+  const int count = *count_ptr;
+  if (!use_compaction(count, K)) return;
+  const int t = threadIdx.x;
+  const int64_t kw = (K + 31) / 32;
+  const int64_t kk = K - count;
+  const int64_t kpad = (kk + 15) & ~(int64_t)15;
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    const int8_t *row = Wq + n * K;
+    for (int64_t w = t; w < kw; w += 256) {
+      const uint32_t v = omask[w];
+      int64_t dst = 32 * w - wprefix[w];
+      const int nb = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
+      for (int h = 0; h < nb; h += 16) {
+        const u32x4 d = *(const u32x4 *)(row + 32 * w + h);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (!((v >> (h + e)) & 1u)) {
+            srow[dst] = (uint8_t)((d[e >> 2] >> (8 * (e & 3))) & 0xffu);
+            ++dst;
+          }
+        }
+      }
+    }
+    for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
+    __syncthreads();
+    int8_t *out = Wqc + n * K;
+    for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
+      *(u32x4 *)(out + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                               const int32_t *idx, const int32_t *count, int8_t *Xq, float *m,
+                               hipStream_t stream) {
+  const size_t lds = (size_t)((K + 31) / 32) * sizeof(uint32_t);
+  hipLaunchKernelGGL(k_rowquant_idx, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx, idx,
+                     count, Xq, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                 const uint32_t *omask, const int32_t *wprefix,
+                                 const int32_t *count, int8_t *Xq, float *m, uint16_t *xo,
+                                 int64_t ldo, hipStream_t stream) {
+  const size_t lds = (K <= kCompactMaxK) ? (size_t)K : 0;
+  hipLaunchKernelGGL(k_rowquant_layer, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx, omask,
+                     wprefix, count, Xq, m, xo, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
+                          float *s, hipStream_t stream) {
+  unsigned *sbits = (unsigned *)s;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, sbits, N,
+                     0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int col_tiles = (int)((N + 511) / 512);
+  int64_t chunks = (K + 127) / 128;  // ~128 rows per block
+  if (chunks > 256) chunks = 256;
+  const int rows_per_chunk = (int)((K + chunks - 1) / chunks);
+  const int row_chunks = (int)((K + rows_per_chunk - 1) / rows_per_chunk);
+  hipLaunchKernelGGL(k_colabsmax, dim3(col_tiles, row_chunks), dim3(256), 0, stream, W, K, N, ldw,
+                     rows_per_chunk, sbits);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_colquant, dim3((unsigned)((K + 127) / 128), (unsigned)((N + 63) / 64)),
+                     dim3(256), 0, stream, W, K, N, ldw, (const float *)s, Wq);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_wq(const int8_t *Wq, int64_t K, int64_t N, const uint32_t *omask,
+                             const int32_t *wprefix, const int32_t *count, int8_t *Wqc,
+                             hipStream_t stream) {
+  if (K > kCompactMaxK) return hipSuccess;  // compaction never applies
+  int64_t blocks = N < 4096 ? N : 4096;
+  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)K, stream, Wq, K, N,
+                     omask, wprefix, count, Wqc);
+  return hipGetLastError();
+}
+
+}  // namespace llmint8

@@ -1,0 +1,132 @@
+/*
+ * llmint8.h - C ABI of the MI355X (gfx950) LLM.int8() mixed-precision linear layer.
+ *
+ * The layer computes Y = X . W for an fp16 activation X [M x K] and an fp16
+ * weight W [K x N] the way LLM.int8() does ("8-bit quantization of giant
+ * language models: LLM.int8()" walkthrough, 2kiu.com, sections 2.1 and 2.3;
+ * "LLM.int8() pitfalls" page, codearts.csdn.net, sections 1 and 3):
+ *
+ *   1. the outlier columns O of X are those with some |X[i, k]| >= threshold;
+ *   2. X without those columns is quantized per row:   m[i] = max_{k not in O} |X[i, k]|,
+ *      Xq[i, k] = clamp(rint(X[i, k] * fl32(127 / m[i])), -127, 127), Xq[i, O] = 0;
+ *   3. W is quantized per column (output channel):     s[n] = max_k |W[k, n]|,
+ *      Wq[n, k] = clamp(rint(W[k, n] * fl32(127 / s[n])), -127, 127);
+ *   4. C = Xq . Wq^T with int32 accumulation (exact);
+ *   5. Y[i, n] = fp16( C[i, n] * m[i] * s[n] / 127^2 + sum_{k in O} X[i, k] W[k, n] ),
+ *      the second term an fp16 product with fp32 accumulation.
+ * rint rounds half to even; a zero absmax gives an all-zero row/column.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is a DEVICE pointer unless stated otherwise. fp16 data is
+ *     passed as uint16_t IEEE binary16 bit patterns. `stream` is a hipStream_t
+ *     (NULL = the default stream).
+ *   - Matrices are row-major with an explicit leading dimension in elements.
+ *   - The caller owns and allocates every buffer, including the workspace. The
+ *     library never allocates device memory, keeps no state between calls and
+ *     is re-entrant; calls that share a workspace must be ordered on one stream.
+ *   - Calls are asynchronous: they enqueue kernels on `stream` and return.
+ *     Results are valid once the caller synchronizes with the stream. Inputs
+ *     and outputs must not overlap.
+ *   - Shape/alignment rules (else LLMINT8_ERR_UNSUPPORTED): every pointer is
+ *     16-byte aligned; K is a multiple of 16; N is a multiple of 8; ldx, ldw and
+ *     ldy are multiples of 8. M >= 1 is unrestricted.
+ *   - Arguments are validated before any HIP call is made. A failed check
+ *     enqueues nothing and leaves every output untouched. Device faults surface
+ *     at the caller's next synchronization.
+ *   - Inputs must be finite (an infinite entry makes its column an outlier; NaN
+ *     inputs give unspecified results).
+ */
+#ifndef LLMINT8_H_
+#define LLMINT8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning call. */
+#define LLMINT8_OK 0
+#define LLMINT8_ERR_INVALID_ARG 1  /* NULL required pointer, size <= 0, ld < row length, NaN threshold */
+#define LLMINT8_ERR_UNSUPPORTED 2  /* alignment / multiple-of rule above is broken */
+#define LLMINT8_ERR_OVERFLOW 3     /* K > LLMINT8_MAX_K: an int32 accumulator could overflow */
+#define LLMINT8_ERR_WORKSPACE 4    /* workspace NULL or smaller than the size query returns */
+#define LLMINT8_ERR_HIP 5          /* a HIP launch or runtime call failed */
+
+/* Largest K for which 127 * 127 * K fits in int32. */
+#define LLMINT8_MAX_K 133144
+
+/*
+ * Weight quantization, run once per weight at load time (walkthrough page,
+ * section 2.1: one scale per column of W; section 6: quantize once, reuse).
+ *   W          [K x N] fp16, row-major, leading dimension ldw >= N.
+ *   Wq         [N x K] int8 output: row n is output channel n, K-contiguous.
+ *   col_absmax [N] fp32 output: s[n] = max_k |W[k, n]| over all K rows.
+ * Bit-exact with the definition above (fp32 scale, round half to even).
+ */
+int llmint8_quantize_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                             int8_t *Wq, float *col_absmax, void *stream);
+
+/*
+ * Outlier-column detection (walkthrough page, sections 2.3 and 4.2: a column
+ * whose absolute maximum reaches the threshold, default 6.0, goes the 16-bit
+ * way; rescanned on every call).
+ *   X         [M x K] fp16, leading dimension ldx >= K.
+ *   threshold  host float; +inf gives no outliers, <= 0 makes every column one.
+ *   idx       [K] int32 output: the outlier columns in ascending order in
+ *             idx[0 .. *count); entries beyond *count are unspecified.
+ *   count     [1] int32 output (device): |O|.
+ *   workspace  device scratch of at least llmint8_find_outliers_workspace_size(M, K) bytes.
+ */
+size_t llmint8_find_outliers_workspace_size(int64_t M, int64_t K);
+int llmint8_find_outliers(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
+                          int32_t *idx, int32_t *count, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * Row-wise (per-token) quantization of X without its outlier columns
+ * (walkthrough page, sections 2.1 and 2.3; codearts page, section 1).
+ *   X          [M x K] fp16, leading dimension ldx >= K.
+ *   idx, count outlier columns as produced by llmint8_find_outliers (device).
+ *              Both NULL means no outlier columns.
+ *   Xq         [M x K] int8 output, leading dimension K; outlier columns are 0.
+ *   row_absmax [M] fp32 output: m[i] = max over non-outlier k of |X[i, k]|.
+ */
+int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                             const int32_t *idx, const int32_t *count, int8_t *Xq,
+                             float *row_absmax, void *stream);
+
+/*
+ * The whole layer: detection, row quantization of X, int8 GEMM with int32
+ * accumulation, fp16 outlier product and the dequantize-and-add merge, on one
+ * stream with no host synchronization (the outlier count never leaves the GPU).
+ *   X          [M x K] fp16, leading dimension ldx >= K.
+ *   Wq, col_absmax  from llmint8_quantize_colwise (Wq [N x K], K-contiguous).
+ *   W          [K x N] fp16, leading dimension ldw >= N: the original weight,
+ *              whose rows k in O feed the 16-bit product. May be NULL only when
+ *              threshold is +inf.
+ *   threshold  host float, default in the pages 6.0.
+ *   Y          [M x N] fp16 output, leading dimension ldy >= N.
+ *   outlier_count_out  optional [1] int32 output (device): |O|.
+ *   C_debug    optional [M x N] int32 output (leading dimension N): the exact
+ *              int32 accumulators of step 4.
+ *   workspace  device scratch of at least llmint8_workspace_size(M, K, N) bytes.
+ * When the outlier share is large, the int8 GEMM runs over the K - |O| kept
+ * columns only (compacted operands); the result is identical either way.
+ */
+size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N);
+int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                   const int8_t *Wq, const float *col_absmax,
+                   const uint16_t *W, int64_t ldw, int64_t N, float threshold,
+                   uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *llmint8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLMINT8_H_ */

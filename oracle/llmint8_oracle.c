@@ -86,23 +86,22 @@ static int8_t ora_quant(float x, float inv)
 void ora_quantize_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
                           int8_t *Wq, float *s)
 {
-    for (int64_t n = 0; n < N; ++n) {
-        float m = 0.0f;
-        for (int64_t k = 0; k < K; ++k) {
+    /* s[n] = max over all K rows of |W[k, n]| (rows visited in memory order) */
+    for (int64_t n = 0; n < N; ++n)
+        s[n] = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
             float a = fabsf(ora_half(W[k * ldw + n]));
-            if (a > m)
-                m = a;
+            if (a > s[n])
+                s[n] = a;
         }
-        s[n] = m;
-        if (m == 0.0f) {
-            for (int64_t k = 0; k < K; ++k)
-                Wq[n * K + k] = 0;
-            continue;
-        }
-        float inv = 127.0f / m;
-        for (int64_t k = 0; k < K; ++k)
-            Wq[n * K + k] = ora_quant(ora_half(W[k * ldw + n]), inv);
-    }
+    float *inv = malloc((size_t)N * sizeof(float));
+    for (int64_t n = 0; n < N; ++n)
+        inv[n] = s[n] > 0.0f ? 127.0f / s[n] : 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Wq[n * K + k] = s[n] > 0.0f ? ora_quant(ora_half(W[k * ldw + n]), inv[n]) : 0;
+    free(inv);
 }
 
 /* Outlier columns of X ([P2] section 2.3 and 4.2): column k is an outlier when
@@ -111,15 +110,16 @@ void ora_quantize_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
 int32_t ora_find_outliers(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                           float threshold, int32_t *idx)
 {
-    int32_t count = 0;
-    for (int64_t k = 0; k < K; ++k) {
-        int hit = 0;
-        for (int64_t i = 0; i < M && !hit; ++i)
+    unsigned char *hit = calloc((size_t)(K > 0 ? K : 1), 1);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
             if (fabsf(ora_half(X[i * ldx + k])) >= threshold)
-                hit = 1;
-        if (hit)
+                hit[k] = 1;
+    int32_t count = 0;
+    for (int64_t k = 0; k < K; ++k)
+        if (hit[k])
             idx[count++] = (int32_t)k;
-    }
+    free(hit);
     return count;
 }
 
@@ -180,15 +180,21 @@ void ora_merge(const int32_t *C, const float *m, const float *s,
                const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
                const int32_t *idx, int32_t count, int64_t M, int64_t N, double *Y)
 {
-    for (int64_t i = 0; i < M; ++i)
-        for (int64_t n = 0; n < N; ++n) {
-            double yo = 0.0;
-            for (int32_t p = 0; p < count; ++p) {
-                int64_t k = idx[p];
-                yo += (double)ora_half(X[i * ldx + k]) * (double)ora_half(W[k * ldw + n]);
-            }
-            Y[i * N + n] = (double)C[i * N + n] * (double)m[i] * (double)s[n] / 16129.0 + yo;
+    double *yo = malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t n = 0; n < N; ++n)
+            yo[n] = 0.0;
+        /* outlier terms of every Y[i, n] summed in ascending k */
+        for (int32_t p = 0; p < count; ++p) {
+            int64_t k = idx[p];
+            double x = (double)ora_half(X[i * ldx + k]);
+            for (int64_t n = 0; n < N; ++n)
+                yo[n] += x * (double)ora_half(W[k * ldw + n]);
         }
+        for (int64_t n = 0; n < N; ++n)
+            Y[i * N + n] = (double)C[i * N + n] * (double)m[i] * (double)s[n] / 16129.0 + yo[n];
+    }
+    free(yo);
 }
 
 /* One whole layer call, step by step in the order the pages give: find the

@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports what include/llmint8.h
+declares, and rejects bad arguments with the documented status before making
+any HIP call. The rejection checks run in a child process with every GPU
+hidden, so even a wrongly accepted call could not reach a device."""
+import ctypes as C
+import json
+import math
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llmint8.h")
+LIB = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "libllmint8.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="HIP library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llmint8_\w+)\s*\(", text)))
+
+
+def test_header_is_plain_c():
+    subprocess.run(["gcc", "-fsyntax-only", "-Wall", "-Werror", "-x", "c", HEADER], check=True)
+    subprocess.run(["g++", "-fsyntax-only", "-Wall", "-Werror", "-x", "c++", HEADER], check=True)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"llmint8_quantize_rowwise", "llmint8_quantize_colwise", "llmint8_find_outliers",
+            "llmint8_linear"} <= set(names)
+    lib = C.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted(set(re.findall(r"\bT (llmint8_\w+)", out)))
+    assert exported == names
+
+
+CHILD = r"""
+import ctypes as C, json, math, sys
+L = C.CDLL(sys.argv[1])
+p, i64, f32, sz = C.c_void_p, C.c_int64, C.c_float, C.c_size_t
+L.llmint8_quantize_colwise.argtypes = [p, i64, i64, i64, p, p, p]
+L.llmint8_find_outliers.argtypes = [p, i64, i64, i64, f32, p, p, p, sz, p]
+L.llmint8_quantize_rowwise.argtypes = [p, i64, i64, i64, p, p, p, p, p]
+L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p, sz, p]
+L.llmint8_workspace_size.argtypes = [i64, i64, i64]
+L.llmint8_workspace_size.restype = sz
+L.llmint8_find_outliers_workspace_size.argtypes = [i64, i64]
+L.llmint8_find_outliers_workspace_size.restype = sz
+A, B, MIS = 0x100000, 0x200000, 0x300008   # 16-byte aligned fakes and a misaligned one
+N0 = None
+inf = math.inf
+res = {}
+def colwise(name, W=A, K=64, N=32, ldw=32, Wq=B, s=A):
+    res[name] = L.llmint8_quantize_colwise(W, K, N, ldw, Wq, s, None)
+def find(name, X=A, M=4, K=64, ldx=64, t=6.0, idx=B, cnt=B, ws=A, wsb=0):
+    res[name] = L.llmint8_find_outliers(X, M, K, ldx, t, idx, cnt, ws, wsb, None)
+def rowq(name, X=A, M=4, K=64, ldx=64, idx=N0, cnt=N0, Xq=B, m=A):
+    res[name] = L.llmint8_quantize_rowwise(X, M, K, ldx, idx, cnt, Xq, m, None)
+def linear(name, X=A, M=4, K=64, ldx=64, Wq=B, s=A, W=A, ldw=32, N=32, t=6.0, Y=B, ldy=32,
+           cnt=N0, cdbg=N0, ws=A, wsb=0):
+    res[name] = L.llmint8_linear(X, M, K, ldx, Wq, s, W, ldw, N, t, Y, ldy, cnt, cdbg, ws, wsb, None)
+colwise("colwise_null_W", W=N0)
+colwise("colwise_K0", K=0)
+colwise("colwise_ld_short", ldw=16)
+colwise("colwise_ld_not_mult8", ldw=36)
+colwise("colwise_misaligned_W", W=MIS)
+colwise("colwise_K_not_mult16", K=72)
+colwise("colwise_N_not_mult8", N=30, ldw=32)
+colwise("colwise_K_too_big", K=133152)
+colwise("colwise_null_Wq", Wq=N0)
+find("find_nan_threshold", t=math.nan)
+find("find_null_idx", idx=N0)
+find("find_no_workspace", ws=N0, wsb=1 << 20)
+find("find_workspace_small", wsb=16)
+find("find_neg_M", M=-1)
+rowq("rowq_idx_without_count", idx=A)
+rowq("rowq_null_Xq", Xq=N0)
+rowq("rowq_misaligned_m", m=MIS)
+rowq("rowq_K_too_big", K=200000, ldx=200000)
+linear("linear_null_W_finite_threshold", W=N0)
+linear("linear_null_W_inf_threshold_small_ws", W=N0, t=inf)
+linear("linear_null_Y", Y=N0)
+linear("linear_ldy_short", ldy=8)
+linear("linear_nan_threshold", t=math.nan)
+linear("linear_misaligned_cdbg", cdbg=MIS, wsb=1 << 40)
+linear("linear_workspace_small", wsb=100)
+linear("linear_K_not_mult16", K=40, ldx=48)
+linear("linear_N0", N=0)
+res["ws_size_ok"] = L.llmint8_workspace_size(32, 4096, 4096)
+res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
+res["find_ws_ok"] = L.llmint8_find_outliers_workspace_size(8192, 8192)
+res["find_ws_bad"] = L.llmint8_find_outliers_workspace_size(8, 133160)
+print(json.dumps(res))
+"""
+
+EXPECTED = {
+    "colwise_null_W": 1, "colwise_K0": 1, "colwise_ld_short": 1, "colwise_ld_not_mult8": 2,
+    "colwise_misaligned_W": 2, "colwise_K_not_mult16": 2, "colwise_N_not_mult8": 2,
+    "colwise_K_too_big": 3, "colwise_null_Wq": 1,
+    "find_nan_threshold": 1, "find_null_idx": 1, "find_no_workspace": 4,
+    "find_workspace_small": 4, "find_neg_M": 1,
+    "rowq_idx_without_count": 1, "rowq_null_Xq": 1, "rowq_misaligned_m": 2, "rowq_K_too_big": 3,
+    "linear_null_W_finite_threshold": 1, "linear_null_W_inf_threshold_small_ws": 4,
+    "linear_null_Y": 1, "linear_ldy_short": 1, "linear_nan_threshold": 1,
+    "linear_misaligned_cdbg": 2, "linear_workspace_small": 4, "linear_K_not_mult16": 2,
+    "linear_N0": 1,
+}
+
+
+def test_invalid_arguments_are_rejected_before_any_hip_call():
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    out = subprocess.run([sys.executable, "-c", CHILD, LIB], capture_output=True, text=True,
+                         env=env, timeout=120)
+    assert out.returncode == 0, out.stderr
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    for name, code in EXPECTED.items():
+        assert res[name] == code, (name, res[name], code)
+    assert res["ws_size_ok"] > 32 * 4096 * 3 + 4096 * 4096
+    assert res["ws_size_bad"] == 0
+    assert res["find_ws_ok"] > 0 and res["find_ws_bad"] == 0
+
+
+def test_status_strings():
+    lib = C.CDLL(LIB)
+    lib.llmint8_status_string.restype = C.c_char_p
+    for code in range(6):
+        assert lib.llmint8_status_string(code).decode().startswith("LLMINT8_")
+    assert b"unknown" in lib.llmint8_status_string(99)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import bit_quantized_matmul_col_amd as b
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(ImportError):
+        b.lib()

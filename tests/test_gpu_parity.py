@@ -1,0 +1,215 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle.
+
+Integer results (outlier indices and count, int8 tensors, absmax scales and
+int32 accumulators) must be bit-exact. The fp16 output Y must satisfy
+|Y_gpu - Y_oracle| <= 1e-2 + 1e-2 * |Y_oracle| element-wise against the
+oracle's fp64 result. At full workload sizes the oracle computes every integer
+intermediate except C, and C and Y on sampled rows (rows are independent once
+the outlier set is known).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    import bit_quantized_matmul_col_amd as lm
+    lm.lib()
+    return torch, lm
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_gpu(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_y_close(y_gpu, y_ref, what):
+    y = y_gpu.astype(np.float64)
+    err = np.abs(y - y_ref)
+    bad = err > ATOL + RTOL * np.abs(y_ref)
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    assert not bad.any(), (f"{what}: {bad.sum()} elements out of tolerance, max abs err "
+                           f"{err.max():.3g}")
+
+
+def run_all(torch, lm, X, W, threshold, rows=None, check_colwise=True, ref_w=None):
+    """Run the four entry points on (X, W) and compare them with the oracle."""
+    M, K = X.shape
+    N = W.shape[1]
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+
+    Wq_d, s_d = lm.llmint8_quantize_colwise(Wd)
+    if ref_w is None:
+        ref_w = oracle.quantize_colwise(W)
+    Wq_r, s_r = ref_w
+    if check_colwise:
+        assert np.array_equal(Wq_d.cpu().numpy(), Wq_r), "Wq differs"
+        assert np.array_equal(s_d.cpu().numpy().view(np.uint32), s_r.view(np.uint32)), "s differs"
+
+    idx_d, cnt_d = lm.llmint8_find_outliers(Xd, threshold)
+    idx_r = oracle.find_outliers(X, threshold)
+    cnt = int(cnt_d.cpu().item())
+    assert cnt == idx_r.size, f"count {cnt} vs {idx_r.size}"
+    assert np.array_equal(idx_d.cpu().numpy()[:cnt], idx_r), "outlier indices differ"
+
+    Xq_d, m_d = lm.llmint8_quantize_rowwise(Xd, idx_d, cnt_d)
+    Xq_r, m_r = oracle.quantize_rowwise(X, idx_r)
+    assert np.array_equal(m_d.cpu().numpy().view(np.uint32), m_r.view(np.uint32)), "m differs"
+    assert np.array_equal(Xq_d.cpu().numpy(), Xq_r), "Xq differs"
+
+    cnt_lin = torch.empty(1, dtype=torch.int32, device="cuda")
+    C_d = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y_d = lm.llmint8_linear(Xd, Wq_d, s_d, Wd, threshold, outlier_count=cnt_lin, C_debug=C_d)
+    torch.cuda.synchronize()
+    assert int(cnt_lin.cpu().item()) == idx_r.size
+    if rows is None:
+        C_r = oracle.gemm_i8(Xq_r, Wq_r)
+        Y_r = oracle.merge(C_r, m_r, s_r, X, W, idx_r)
+        assert np.array_equal(C_d.cpu().numpy(), C_r), "int32 accumulators differ"
+        assert_y_close(Y_d.cpu().numpy(), Y_r, "Y")
+    else:
+        rows = np.asarray(rows)
+        ref = oracle.linear_rows(X, W, threshold, rows, Wq=Wq_r, s=s_r)
+        rt = torch.from_numpy(rows).cuda()
+        assert np.array_equal(C_d.index_select(0, rt).cpu().numpy(), ref["C"]), "C rows differ"
+        assert_y_close(Y_d.index_select(0, rt).cpu().numpy(), ref["Y"], "Y rows")
+    return dict(count=cnt, Y=Y_d)
+
+
+SMALL = [
+    (1, 16, 8, 0), (7, 272, 200, 1), (33, 256, 136, 2), (64, 512, 264, 3), (65, 528, 392, 4),
+    (77, 1040, 200, 5), (130, 256, 264, 6), (257, 784, 520, 7),
+]
+
+
+@pytest.mark.parametrize("M,K,N,seed", SMALL)
+@pytest.mark.parametrize("threshold", [6.0, math.inf, 2.5, 0.0])
+def test_small_shapes(dev, M, K, N, seed, threshold):
+    torch, lm = dev
+    say(f"case small M={M} K={K} N={N} seed={seed} threshold={threshold}")
+    X, W, _ = workloads.random_case(M, K, N, seed, n_out=3)
+    run_all(torch, lm, X, W, threshold)
+
+
+def test_edge_values(dev):
+    torch, lm = dev
+    say("case edge values")
+    rng = np.random.default_rng(21)
+    M, K, N = 70, 96, 72
+    X = (rng.standard_normal((M, K)) * 0.5).astype(np.float16)
+    X[3, :] = 0                                   # zero row
+    X[4, :] = np.float16(6e-8)                    # fp16 subnormals only
+    X[5, 10] = np.float16(6.0)                    # exactly the threshold
+    X[6, 0] = np.float16(-65504.0)                # largest fp16, outlier at column 0
+    X[7, K - 1] = np.float16(7.5)                 # outlier at the last column
+    X[8, :8] = np.float16(2.0 ** -20)             # subnormals next to normals
+    W = (rng.standard_normal((K, N)) * 0.01).astype(np.float16)
+    W[:, 5] = 0                                   # zero weight column
+    W[:, 6] = np.float16(1e-7)                    # subnormal weight column
+    W[0, :] = np.float16(1e-3)                    # small weights against the -65504 outlier
+    out = run_all(torch, lm, X, W, 6.0)
+    assert out["count"] == 3
+
+
+def test_threshold_inf_without_fp16_weight(dev):
+    torch, lm = dev
+    say("case threshold inf, W omitted")
+    X, W, _ = workloads.random_case(40, 256, 64, 9, n_out=2)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    y_with = lm.llmint8_linear(Xd, Wq, s, Wd, math.inf)
+    y_without = lm.llmint8_linear(Xd, Wq, s, None, math.inf)
+    assert torch.equal(y_with, y_without)
+    ref = oracle.linear(X, W, math.inf)
+    assert_y_close(y_without.cpu().numpy(), ref["Y"], "Y")
+
+
+def test_deterministic(dev):
+    torch, lm = dev
+    say("case determinism")
+    X, W, _ = workloads.random_case(300, 1024, 520, 13, n_out=8)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    y1 = lm.llmint8_linear(Xd, Wq, s, Wd, 2.5)
+    y2 = lm.llmint8_linear(Xd, Wq, s, Wd, 2.5)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_strided_inputs(dev):
+    torch, lm = dev
+    say("case strided leading dimensions")
+    X, W, _ = workloads.random_case(50, 128, 40, 14, n_out=2)
+    Xd_big = torch.zeros((50, 160), dtype=torch.float16, device="cuda")
+    Xd_big[:, :128] = to_gpu(torch, X)
+    Wd_big = torch.zeros((128, 56), dtype=torch.float16, device="cuda")
+    Wd_big[:, :40] = to_gpu(torch, W)
+    Xv, Wv = Xd_big[:, :128], Wd_big[:, :40]
+    Wq, s = lm.llmint8_quantize_colwise(Wv)
+    Yd_big = torch.full((50, 48), 7.0, dtype=torch.float16, device="cuda")
+    lm.llmint8_linear(Xv, Wq, s, Wv, 6.0, Y=Yd_big[:, :40])
+    ref = oracle.linear(X, W, 6.0)
+    assert_y_close(Yd_big[:, :40].cpu().numpy(), ref["Y"], "Y")
+    assert torch.all(Yd_big[:, 40:] == 7.0)
+
+
+# --- the five workloads ----------------------------------------------------------
+
+def sample_rows(M, n=8):
+    rows = {0, M - 1}
+    rows.update(np.random.default_rng(M).choice(M, size=min(n, M), replace=False).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_workload_full(dev, name):
+    torch, lm = dev
+    wl = workloads.WORKLOADS[name]
+    say(f"case workload {name} (full oracle)")
+    X, W = workloads.make_x(wl), workloads.make_w(wl)
+    out = run_all(torch, lm, X, W, wl.threshold)
+    assert out["count"] >= len(workloads.planted_columns(wl))
+
+
+@pytest.mark.parametrize("name", ["prefill", "13b"])
+def test_workload_sampled(dev, name):
+    torch, lm = dev
+    wl = workloads.WORKLOADS[name]
+    say(f"case workload {name} (sampled rows)")
+    X, W = workloads.make_x(wl), workloads.make_w(wl)
+    out = run_all(torch, lm, X, W, wl.threshold, rows=sample_rows(wl.M))
+    assert out["count"] >= len(workloads.planted_columns(wl))
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def w70(dev):
+    wl = workloads.WORKLOADS["70b"]
+    W = workloads.make_w(wl)
+    return W, oracle.quantize_colwise(W)
+
+
+@pytest.mark.parametrize("threshold,call", [(6.0, 0), (math.inf, 1), (4.0, 2)])
+def test_workload_70b(dev, w70, threshold, call):
+    torch, lm = dev
+    wl = workloads.WORKLOADS["70b"]
+    say(f"case workload 70b threshold={threshold} call={call} (sampled rows)")
+    W, ref_w = w70
+    X = workloads.make_x(wl, call)
+    run_all(torch, lm, X, W, threshold, rows=sample_rows(wl.M, 6), check_colwise=(call == 0),
+            ref_w=ref_w)
+    torch.cuda.empty_cache()
