@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the LLM.int8() mixed-precision linear layer on one MI355X.
+
+A step is one llmint8_linear call: outlier detection, row-wise quantization of
+X, K-compaction when the outlier share calls for it, the int8 GEMM with its
+fused fp16 outlier product, dequantization and merge. Weights are quantized
+once before timing (the method quantizes them at load), and that pass is
+reported on its own. Inputs are resident in HBM when the timed region starts.
+To keep the 256 MB Infinity Cache from serving the weights, consecutive steps
+cycle through distinct copies of the weight set (and of the activation).
+
+Prints one JSON line. `value` is the whole-step rate in the workload's unit:
+GB/s of algorithmic bytes for the HBM-bound decode and tiny shapes, TOPS of
+algorithmic work (int8 ops + fp16 flops) for the prefill shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LLM.int8() linear TOPS & GB/s at 7B/13B shapes; % of int8 MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+FP16_PEAK_TFLOPS = 2500.0
+HBM_BOUND = ("tiny", "decode")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc", f)
+                  for f in ("gemm.hip", "common.hpp", "internal.hpp")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"gemm_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def step_work(M, K, N, n_out, compacted):
+    """Algorithmic bytes and work of one layer call, and of its GEMM kernel."""
+    k_int8 = K - n_out
+    call_bytes = 2 * M * K + K * N + 4 * N + 2 * n_out * N + 2 * M * N
+    k_loop = k_int8 if compacted else K
+    gemm_bytes = (N * k_loop + 4 * N + M * k_loop + 4 * M + 2 * M * n_out + 2 * n_out * N
+                  + 4 * n_out + 2 * M * N)
+    int8_ops = 2 * M * N * k_int8
+    fp16_flops = 2 * M * N * n_out
+    return call_bytes, gemm_bytes, int8_ops, fp16_flops
+
+
+def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out):
+    """The oracle as it stands, single-threaded, on a bounded sample. Its weight
+    quantization (load time, like the GPU's) is done first and not timed."""
+    import numpy as np
+    import oracle
+
+    Wq, s = oracle.quantize_colwise(W)
+    rows = wl.M
+    if not hbm_bound:
+        rows = 4
+    sample_rows = np.arange(rows)
+    reps, elapsed = 0, 0.0
+    while reps == 0 or (elapsed < budget_s and reps < 50):
+        t0 = time.perf_counter()
+        oracle.linear_rows(X, W, threshold, sample_rows, Wq=Wq, s=s)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    per = elapsed / reps
+    if hbm_bound:
+        call_bytes = step_work(wl.M, wl.K, wl.N, n_out, False)[0]
+        value, unit = call_bytes / per / 1e9, "GB/s"
+        sample = f"{reps} whole layer calls on the {wl.M}x{wl.K}x{wl.N} workload"
+    else:
+        work = 2 * rows * wl.N * wl.K
+        value, unit = work / per / 1e12, "TOPS"
+        sample = (f"outlier scan over all {wl.M} rows + rows 0..{rows - 1} of the "
+                  f"{wl.M}x{wl.K}x{wl.N} workload, {reps} repetitions")
+    return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(elapsed, 2)}
+
+
+def main():
+    import workloads
+
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
+              "(multi-GPU sharding is a design note, not a measured path). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_matmul_col_amd as lm
+
+    lm.lib()
+    wl = workloads.WORKLOADS[args.workload]
+    threshold = wl.threshold if args.threshold is None else args.threshold
+    hbm_bound = args.workload in HBM_BOUND
+    steps = args.steps if args.steps is not None else (2000 if hbm_bound else 100)
+    warmup = args.warmup if args.warmup is not None else max(10, steps // 10)
+    dev = torch.device("cuda:0")
+
+    # inputs: weight sets and activations, resident before timing
+    W_host = workloads.make_w(wl)
+    W0 = torch.from_numpy(W_host).to(dev)
+    wq_bytes = wl.N * wl.K
+    n_sets = max(2, min(32, math.ceil(600e6 / wq_bytes)))
+    x_pool = 4
+    X_host = [workloads.make_x(wl, c) for c in range(x_pool)] if wl.per_call else \
+        [workloads.make_x(wl)]
+    Xs = [torch.from_numpy(X_host[c % len(X_host)]).to(dev) for c in range(x_pool)]
+
+    # load-time weight quantization, timed on its own
+    Wq0, s0 = lm.llmint8_quantize_colwise(W0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        lm.llmint8_quantize_colwise(W0)
+    e1.record()
+    torch.cuda.synchronize()
+    colwise_ms = e0.elapsed_time(e1) / reps
+    colwise_bytes = 3 * wl.K * wl.N + 4 * wl.N
+
+    sets = [(Wq0, s0, W0)] + [(Wq0.clone(), s0.clone(), W0.clone()) for _ in range(n_sets - 1)]
+    Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    ws = torch.empty((lm.llmint8_workspace_size(wl.M, wl.K, wl.N),), dtype=torch.uint8,
+                     device=dev)
+    cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    # GEMM timing events, recorded by the library around its GEMM launch
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in ev_b + ev_e:
+        e.record()  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    opts = [lm.LinearOpts(gemm_begin_event=ev_b[i].cuda_event, gemm_end_event=ev_e[i].cuda_event)
+            for i in range(steps)]
+
+    def step(i, timed):
+        Wq, s, W = sets[i % n_sets]
+        lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
+                          outlier_count=cnt, opts=opts[i] if timed else None)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(i, True)
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = total_ms / steps
+    gemm_ms = sum(ev_b[i].elapsed_time(ev_e[i]) for i in range(steps)) / steps
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        a = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    n_out = int(cnt.item())
+    compacted = n_out > 0 and wl.K <= 32768 and n_out * 100 >= wl.K * 5
+    call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted)
+    if hbm_bound:
+        value, unit = call_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        value, unit = (int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, "TOPS"
+        # fp16 flops weigh double: the fp16 MFMA peak is half the int8 one
+        achieved = (int8_ops + 2 * fp16_flops) / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    roof["traffic"] = read_traffic(args.workload)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "threshold": threshold, "outlier_columns": n_out,
+                   "k_compacted": compacted, "weight_sets_cycled": n_sets,
+                   "activation_pool": x_pool, "parallelism": "single GPU"},
+        "roofline": roof,
+        "gemm_kernel_ms": round(gemm_ms, 6),
+        "whole_step": {"algorithmic_bytes": call_bytes, "int8_ops": int8_ops,
+                       "fp16_flops": fp16_flops,
+                       "GB_per_s": round(call_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+                       "TOPS": round((int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, 3),
+                       "wall_s": round(wall, 4)},
+        "quantize_colwise": {"ms": round(colwise_ms, 5), "algorithmic_bytes": colwise_bytes,
+                             "GB_per_s": round(colwise_bytes / (colwise_ms * 1e-3) / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, X_host[0], W_host, threshold, args.cpu_seconds,
+                                           hbm_bound, n_out)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,15 @@ LLMINT8_MAX_K = 133144
 _lib = None
 
 
+class LinearOpts(C.Structure):
+    """Mirror of llmint8_linear_opts."""
+    _fields_ = [("struct_size", C.c_size_t), ("gemm_begin_event", C.c_void_p),
+                ("gemm_end_event", C.c_void_p)]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=C.sizeof(LinearOpts), **kw)
+
+
 class Llmint8Error(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
@@ -54,10 +63,11 @@ def lib() -> C.CDLL:
         L.llmint8_workspace_size.restype = sz
         L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p,
                                      sz, p]
+        L.llmint8_linear_ex.argtypes = L.llmint8_linear.argtypes + [p]
         L.llmint8_status_string.argtypes = [C.c_int]
         L.llmint8_status_string.restype = C.c_char_p
         for name in ("llmint8_quantize_colwise", "llmint8_find_outliers",
-                     "llmint8_quantize_rowwise", "llmint8_linear"):
+                     "llmint8_quantize_rowwise", "llmint8_linear", "llmint8_linear_ex"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -151,7 +161,8 @@ def llmint8_workspace_size(M: int, K: int, N: int) -> int:
 def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
                    W: torch.Tensor | None, threshold: float = 6.0, *, Y=None, workspace=None,
                    outlier_count: torch.Tensor | None = None,
-                   C_debug: torch.Tensor | None = None) -> torch.Tensor:
+                   C_debug: torch.Tensor | None = None,
+                   opts: LinearOpts | None = None) -> torch.Tensor:
     """The whole LLM.int8() layer: fp16 X [M, K] with Wq [N, K], col_absmax [N] and the
     fp16 weight W [K, N] (rows in the outlier set feed the 16-bit product) -> fp16 Y [M, N]."""
     _need(X, "X", torch.float16, 2)
@@ -176,8 +187,11 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
     if workspace is None:
         workspace = torch.empty((llmint8_workspace_size(M, K, N),), dtype=torch.uint8,
                                 device=X.device)
-    _check(lib().llmint8_linear(
-        _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
-        _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
-        _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X)))
+    args = (_ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
+            _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
+            _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X))
+    if opts is None:
+        _check(lib().llmint8_linear(*args))
+    else:
+        _check(lib().llmint8_linear_ex(*args, C.byref(opts)))
     return Y

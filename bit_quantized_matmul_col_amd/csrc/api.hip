@@ -134,11 +134,13 @@ LLMINT8_EXPORT size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N) {
   return make_layout(M, K, N, true).total;
 }
 
-LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                                  const int8_t *Wq, const float *col_absmax, const uint16_t *W,
-                                  int64_t ldw, int64_t N, float threshold, uint16_t *Y,
-                                  int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
-                                  void *workspace, size_t workspace_bytes, void *stream) {
+LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                     const int8_t *Wq, const float *col_absmax, const uint16_t *W,
+                                     int64_t ldw, int64_t N, float threshold, uint16_t *Y,
+                                     int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                                     void *workspace, size_t workspace_bytes, void *stream,
+                                     const llmint8_linear_opts *opts) {
+  if (opts && opts->struct_size != sizeof(llmint8_linear_opts)) return LLMINT8_ERR_INVALID_ARG;
   int st = check_matrix(X, M, K, ldx);
   if (st) return st;
   if ((st = check_matrix(Y, M, N, ldy))) return st;
@@ -172,7 +174,19 @@ LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64
   if (e == hipSuccess) e = launch_compact_wq(Wq, K, N, omask, wprefix, count, wqc, s);
   if (e == hipSuccess) {
     GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, W, idx, count, Y, C_debug, M, N, K, K, ldw, ldy};
-    e = launch_gemm(g, s);
+    if (opts && opts->gemm_begin_event) e = hipEventRecord((hipEvent_t)opts->gemm_begin_event, s);
+    if (e == hipSuccess) e = launch_gemm(g, s);
+    if (e == hipSuccess && opts && opts->gemm_end_event)
+      e = hipEventRecord((hipEvent_t)opts->gemm_end_event, s);
   }
   return hip_status(e);
+}
+
+LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                  const int8_t *Wq, const float *col_absmax, const uint16_t *W,
+                                  int64_t ldw, int64_t N, float threshold, uint16_t *Y,
+                                  int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  return llmint8_linear_ex(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
+                           outlier_count_out, C_debug, workspace, workspace_bytes, stream, nullptr);
 }

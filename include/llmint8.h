@@ -122,6 +122,30 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                    uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Options of llmint8_linear_ex. Zero-initialize, set struct_size =
+ * sizeof(llmint8_linear_opts), then fill the fields you use; NULL fields are
+ * off. The struct is read during the call only.
+ *   gemm_begin_event, gemm_end_event  optional hipEvent_t handles (created by
+ *       the caller) recorded on `stream` immediately before and after the GEMM
+ *       kernel, so a caller can time the dominant kernel of the layer with
+ *       hipEventElapsedTime.
+ */
+typedef struct llmint8_linear_opts {
+  size_t struct_size;
+  void *gemm_begin_event;
+  void *gemm_end_event;
+} llmint8_linear_opts;
+
+/* llmint8_linear with options; opts == NULL is exactly llmint8_linear. A
+ * struct_size other than sizeof(llmint8_linear_opts) is LLMINT8_ERR_INVALID_ARG. */
+int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                      const int8_t *Wq, const float *col_absmax,
+                      const uint16_t *W, int64_t ldw, int64_t N, float threshold,
+                      uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      const llmint8_linear_opts *opts);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *llmint8_status_string(int status);
 

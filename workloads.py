@@ -70,7 +70,7 @@ WORKLOADS = {
         n_out=51,
         description="13B-scale prefill 4096x5120x13824, X~N(0,1.5), 51 planted columns"),
     "70b": Workload(
-        "70b", 8192, 8192, 28672, 1.0, 0.01, 6.0, 100.0, (4.0, 6.0, INF), 4,
+        "70b", 8192, 8192, 28672, 1.0, 0.01, 6.0, 100.0, (6.0, 4.0, INF), 4,
         per_call=True,
         description="70B-scale layer 8192x8192x28672, outlier set re-drawn per call"),
 }
