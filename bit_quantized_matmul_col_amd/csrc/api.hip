@@ -20,10 +20,28 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Offsets (bytes) of the regions a call carves out of its workspace.
 struct Layout {
-  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, total;
+  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, part, counters, total;
 };
 
+// Small-M layer calls: preparation outputs, split-K partial sums, counters.
+Layout make_decode_layout(int64_t M, int64_t K, int64_t N) {
+  const DecodePlan p = decode_plan(M, K, N);
+  Layout L{};
+  size_t o = 0;
+  L.omask = o;
+  o += up((size_t)((K + 31) / 32) * 4);
+  L.pmask = o;  // partial row maxima [det_blocks x M] fp32
+  o += up((size_t)p.det_blocks * (size_t)M * 4);
+  L.m = o;
+  o += up((size_t)M * 4);
+  L.part = o;
+  o += up((size_t)p.kb * (size_t)M * (size_t)N * 4);
+  L.total = o;
+  return L;
+}
+
 Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer) {
+  if (layer && M <= kDecodeMaxM) return make_decode_layout(M, K, N);
   const DetectPlan p = detect_plan(M, K);
   Layout L{};
   size_t o = 0;
@@ -157,6 +175,21 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
+  const GemmEvents ev{opts ? opts->gemm_begin_event : nullptr,
+                      opts ? opts->gemm_end_event : nullptr};
+
+  if (M <= kDecodeMaxM) {
+    const DecodePlan dp = decode_plan(M, K, N);
+    const int64_t kw = (K + 31) / 32;
+    uint32_t *omask = (uint32_t *)(ws + L.omask);
+    float *pmax = (float *)(ws + L.pmask);
+    DecodeDetectArgs det{X, (int)M, K, ldx, kw, threshold, omask, pmax};
+    DecodeGemmArgs g{X, Wq, col_absmax, omask, pmax, W, (int32_t *)(ws + L.part),
+                     (float *)(ws + L.m), outlier_count_out, Y, C_debug,
+                     M, N, K, kw, dp.kc, ldx, ldw, ldy, dp.det_blocks, dp.kb};
+    return hip_status(launch_decode(det, g, dp, ev, s));
+  }
+
   const DetectPlan plan = detect_plan(M, K);
   uint32_t *omask = (uint32_t *)(ws + L.omask);
   int32_t *wprefix = (int32_t *)(ws + L.wprefix);
@@ -171,13 +204,12 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
               outlier_count_out};
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
   if (e == hipSuccess) e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, m, xo, K, s);
-  if (e == hipSuccess) e = launch_compact_wq(Wq, K, N, omask, wprefix, count, wqc, s);
+  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, s);
   if (e == hipSuccess) {
     GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, W, idx, count, Y, C_debug, M, N, K, K, ldw, ldy};
-    if (opts && opts->gemm_begin_event) e = hipEventRecord((hipEvent_t)opts->gemm_begin_event, s);
+    if (ev.begin) e = hipEventRecord((hipEvent_t)ev.begin, s);
     if (e == hipSuccess) e = launch_gemm(g, s);
-    if (e == hipSuccess && opts && opts->gemm_end_event)
-      e = hipEventRecord((hipEvent_t)opts->gemm_end_event, s);
+    if (e == hipSuccess && ev.end) e = hipEventRecord((hipEvent_t)ev.end, s);
   }
   return hip_status(e);
 }

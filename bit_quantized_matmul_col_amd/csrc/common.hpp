@@ -19,15 +19,20 @@ constexpr int kWave = 64;
 // Workspace regions are carved at this alignment.
 constexpr size_t kAlign = 256;
 
-// Outlier share above which the int8 GEMM runs on compacted operands (the K - |O|
-// kept columns only): |O| * 100 >= K * kCompactPct. Compaction also needs the
-// compacted row to fit in LDS (K <= kCompactMaxK).
-constexpr int kCompactPct = 5;
+// When the int8 GEMM runs on compacted operands (the K - |O| kept columns only).
+// Compacting costs one pass over Wq plus writing the compacted copy, about
+// (2K - |O|) * N bytes at HBM speed; it saves 2 * M * N * |O| int8 MFMA ops.
+// With ~4 TB/s and ~2.5 POPS that pays off when M * |O| > 312.5 * (2K - |O|),
+// which small-M (decode) calls never reach. The compacted row is staged in LDS,
+// so K is also capped.
 constexpr int kCompactMaxK = 32768;
 
-__host__ __device__ inline bool use_compaction(int count, int64_t K) {
-  return count > 0 && K <= kCompactMaxK && (int64_t)count * 100 >= K * kCompactPct;
+__host__ __device__ inline bool use_compaction(int count, int64_t K, int64_t M) {
+  return count > 0 && K <= kCompactMaxK && M * (int64_t)count * 16 > 5000 * (2 * K - count);
 }
+
+// Row count up to which the layer takes the small-M (decode) path.
+constexpr int kDecodeMaxM = 64;
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }

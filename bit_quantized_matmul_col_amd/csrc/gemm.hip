@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
   const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * BN;
 
   const int count = *a.count;
-  const bool compact = use_compaction(count, a.K);
+  const bool compact = use_compaction(count, a.K, a.M);
   const int8_t *B = compact ? a.wqc : a.wq;
   const int64_t K = a.K;
   const int64_t Kl = compact ? K - count : K;
@@ -216,104 +216,9 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
     }
 }
 
-// Small-M kernel (M <= 16 * MB): the layer is bound by streaming Wq from HBM.
-// A block owns 16 output columns for all K; its 4 waves take interleaved
-// 128-byte k steps, each lane loading 32 contiguous bytes of one Wq row (and of
-// the matching Xq row), U steps in flight at once. The four partial int32
-// accumulators meet in LDS; the epilogue adds the 16-bit outlier terms with
-// fp32 FMAs (products of two fp16 are exact in fp32).
-template <int MB, int U>
-__global__ __launch_bounds__(256) void k_gemm_decode(GemmArgs a) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-
-  const int count = *a.count;
-  const bool compact = use_compaction(count, a.K);
-  const int8_t *B = compact ? a.wqc : a.wq;
-  const int64_t K = a.K;
-  const int64_t Kl = compact ? K - count : K;
-  const int64_t nsteps = (Kl + 127) / 128;
-
-  const int64_t bn = (n0 + r16 < a.N) ? n0 + r16 : a.N - 1;
-  const int8_t *brow = B + bn * K;
-  const int8_t *arow[MB];
-  bool aval[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int64_t row = mb * 16 + r16;
-    aval[mb] = row < a.M;
-    arow[mb] = a.xq + (aval[mb] ? row : 0) * K;
-  }
-
-  i32x4 acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = (i32x4){0, 0, 0, 0};
-
-  for (int64_t s0 = wv; s0 < nsteps; s0 += 4 * U) {
-    u32x4 bv[U][2], av[U][MB][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (s0 + 4 * u) * 128 + 32 * g;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool ok = k + 16 * h < Kl;
-        bv[u][h] = ok ? *(const u32x4 *)(brow + k + 16 * h) : zero4();
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          av[u][mb][h] = (ok && aval[mb]) ? *(const u32x4 *)(arow[mb] + k + 16 * h) : zero4();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              __builtin_bit_cast(i32x4, av[u][mb][h]), __builtin_bit_cast(i32x4, bv[u][h]),
-              acc[mb], 0, 0, 0);
-  }
-
-  __shared__ i32x4 red[4][MB][64];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) red[wv][mb][lane] = acc[mb];
-  __syncthreads();
-  for (int mb = wv; mb < MB; mb += 4) {
-    const i32x4 c = red[0][mb][lane] + red[1][mb][lane] + red[2][mb][lane] + red[3][mb][lane];
-    const int64_t col = n0 + r16;
-    if (col >= a.N) continue;
-    const float sc = a.s[col] * (1.0f / 16129.0f);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = mb * 16 + 4 * g + r;
-      if (row >= a.M) continue;
-      if (a.cdbg) a.cdbg[row * a.N + col] = c[r];
-      float y = (float)c[r] * (a.m[row] * sc);
-      if (a.w) {
-        const uint16_t *xo = a.xo + row * a.ldo;
-        for (int p = 0; p < count; ++p)
-          y += h2f(xo[p]) * h2f(a.w[(int64_t)a.idx[p] * a.ldw + col]);
-      }
-      a.y[row * a.ldy + col] = f2h(y);
-    }
-  }
-}
-
-template <int MB>
-hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_decode<MB, 4>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0,
-                     stream, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode<1>(a, stream);
-  if (a.M <= 32) return launch_decode<2>(a, stream);
-  if (a.M <= 48) return launch_decode<3>(a, stream);
-  if (a.M <= 64) return launch_decode<4>(a, stream);
   constexpr int BM = 128, BN = 128;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (BM + BN) * P8;

@@ -48,9 +48,9 @@ hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, 
 
 // Compacted copy Wqc [N x K] (first K - |O| bytes of each row) of Wq without
 // the outlier columns; a no-op unless the outlier share calls for it.
-hipError_t launch_compact_wq(const int8_t *Wq, int64_t K, int64_t N, const uint32_t *omask,
-                             const int32_t *wprefix, const int32_t *count, int8_t *Wqc,
-                             hipStream_t stream);
+hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                             const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
+                             int8_t *Wqc, hipStream_t stream);
 
 struct GemmArgs {
   const int8_t *xq;      // [M x K] int8 (compacted rows when compaction is on)
@@ -67,6 +67,52 @@ struct GemmArgs {
   int64_t M, N, K, ldo, ldw, ldy;
 };
 
+// Large-M tiled GEMM with the fused dequantize + outlier epilogue.
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
+
+// Caller-supplied events recorded around the GEMM kernel (may be null).
+struct GemmEvents {
+  void *begin;
+  void *end;
+};
+
+// Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
+// its slice of X itself.
+struct DecodeDetectArgs {
+  const uint16_t *X;
+  int M;
+  int64_t K, ldx, kw;
+  float threshold;
+  uint32_t *omask;    // [kw] outlier bitmask
+  float *pmax;        // [det_blocks x M] row absmax over each block's kept columns
+};
+
+struct DecodeGemmArgs {
+  const uint16_t *X;
+  const int8_t *wq;
+  const float *s;
+  const uint32_t *omask;
+  const float *pmax;
+  const uint16_t *w;
+  int32_t *part;      // [kb x M x N] int32 partial sums
+  float *m;           // [M] row absmax
+  int32_t *count_out; // optional [1] outlier count
+  uint16_t *y;
+  int32_t *cdbg;
+  int64_t M, N, K, kw, kc, ldx, ldw, ldy;
+  int det_blocks;
+  int kb;             // K splits (partial sums per output)
+};
+
+struct DecodePlan {
+  int tiles;       // 64-column tiles
+  int kb;          // K splits
+  int det_blocks;  // detection blocks (256 columns each)
+  int64_t kc;      // k bytes per split (multiple of 64)
+};
+DecodePlan decode_plan(int64_t M, int64_t K, int64_t N);
+
+hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
+                         const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream);
 
 }  // namespace llmint8

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
 // contiguously (staged in LDS so the global stores stay 16-byte wide) with a
 // zeroed tail up to the next 16 bytes.
 __global__ __launch_bounds__(256) void k_rowquant_layer(
-    const uint16_t *__restrict__ X, int64_t K, int64_t ldx, const uint32_t *__restrict__ omask,
+    const uint16_t *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
+    const uint32_t *__restrict__ omask,
     const int32_t *__restrict__ wprefix, const int32_t *__restrict__ count_ptr,
     int8_t *__restrict__ Xq, float *__restrict__ m, uint16_t *__restrict__ xo, int64_t ldo) {
   extern __shared__ u32x4 srow_v[];
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
   const int count = *count_ptr;
-  const bool compact = use_compaction(count, K);
+  const bool compact = use_compaction(count, K, M);
 
   const uint16_t *row = X + i * ldx;
   const int64_t nch = K / 8;
@@ -251,15 +252,16 @@ __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W
 // Compacted copy of Wq rows without the outlier columns. One row per block
 // iteration: each thread compresses 32 bytes (one mask word) into LDS, then
 // the row goes out with 16-byte stores, its tail zeroed up to 16 bytes.
-__global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ Wq, int64_t K,
-                                                    int64_t N, const uint32_t *__restrict__ omask,
+__global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ Wq, int64_t M,
+                                                    int64_t K, int64_t N,
+                                                    const uint32_t *__restrict__ omask,
                                                     const int32_t *__restrict__ wprefix,
                                                     const int32_t *__restrict__ count_ptr,
                                                     int8_t *__restrict__ Wqc) {
   extern __shared__ u32x4 srow_v[];
   uint8_t *srow = (uint8_t *)srow_v;
   const int count = *count_ptr;
-  if (!use_compaction(count, K)) return;
+  if (!use_compaction(count, K, M)) return;
   const int t = threadIdx.x;
   const int64_t kw = (K + 31) / 32;
   const int64_t kk = K - count;
@@ -306,8 +308,8 @@ hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_
                                  const int32_t *count, int8_t *Xq, float *m, uint16_t *xo,
                                  int64_t ldo, hipStream_t stream) {
   const size_t lds = (K <= kCompactMaxK) ? (size_t)K : 0;
-  hipLaunchKernelGGL(k_rowquant_layer, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx, omask,
-                     wprefix, count, Xq, m, xo, ldo);
+  hipLaunchKernelGGL(k_rowquant_layer, dim3((unsigned)M), dim3(256), lds, stream, X, M, K, ldx,
+                     omask, wprefix, count, Xq, m, xo, ldo);
   return hipGetLastError();
 }
 
@@ -332,13 +334,13 @@ hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, 
   return hipGetLastError();
 }
 
-hipError_t launch_compact_wq(const int8_t *Wq, int64_t K, int64_t N, const uint32_t *omask,
-                             const int32_t *wprefix, const int32_t *count, int8_t *Wqc,
-                             hipStream_t stream) {
-  if (K > kCompactMaxK) return hipSuccess;  // compaction never applies
+hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                             const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
+                             int8_t *Wqc, hipStream_t stream) {
+  if (!use_compaction((int)K, K, M)) return hipSuccess;  // never applies at this shape
   int64_t blocks = N < 4096 ? N : 4096;
-  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)K, stream, Wq, K, N,
-                     omask, wprefix, count, Wqc);
+  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)K, stream, Wq, M, K,
+                     N, omask, wprefix, count, Wqc);
   return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ linear("linear_workspace_small", wsb=100)
 linear("linear_K_not_mult16", K=40, ldx=48)
 linear("linear_N0", N=0)
 res["ws_size_ok"] = L.llmint8_workspace_size(32, 4096, 4096)
+res["ws_size_prefill"] = L.llmint8_workspace_size(2048, 4096, 11008)
 res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
 res["find_ws_ok"] = L.llmint8_find_outliers_workspace_size(8192, 8192)
 res["find_ws_bad"] = L.llmint8_find_outliers_workspace_size(8, 133160)
@@ -125,7 +126,10 @@ def test_invalid_arguments_are_rejected_before_any_hip_call():
     res = json.loads(out.stdout.strip().splitlines()[-1])
     for name, code in EXPECTED.items():
         assert res[name] == code, (name, res[name], code)
-    assert res["ws_size_ok"] > 32 * 4096 * 3 + 4096 * 4096
+    # small M: int8 + fp16 copies of X and the split-K partial sums
+    assert res["ws_size_ok"] >= 32 * 4096 * 3 + 32 * 4096 * 4
+    # large M: int8 + fp16 copies of X and room for a compacted Wq
+    assert res["ws_size_prefill"] >= 2048 * 4096 * 3 + 11008 * 4096
     assert res["ws_size_bad"] == 0
     assert res["find_ws_ok"] > 0 and res["find_ws_bad"] == 0
 

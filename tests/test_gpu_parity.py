@@ -93,8 +93,21 @@ def run_all(torch, lm, X, W, threshold, rows=None, check_colwise=True, ref_w=Non
 
 SMALL = [
     (1, 16, 8, 0), (7, 272, 200, 1), (33, 256, 136, 2), (64, 512, 264, 3), (65, 528, 392, 4),
-    (77, 1040, 200, 5), (130, 256, 264, 6), (257, 784, 520, 7),
+    (77, 1040, 200, 5), (130, 256, 264, 6), (257, 784, 520, 7), (17, 2064, 72, 8),
+    (48, 4096, 1032, 9),
 ]
+
+
+@pytest.mark.parametrize("M,K,N,threshold", [
+    (600, 256, 136, 3.0), (1100, 512, 264, 3.2), (700, 1008, 200, 3.0), (2000, 96, 40, 2.0)])
+def test_compacted_inner_dimension(dev, M, K, N, threshold):
+    # outlier shares this large make the int8 GEMM run on compacted operands
+    torch, lm = dev
+    say(f"case compaction M={M} K={K} N={N} threshold={threshold}")
+    X, W, _ = workloads.random_case(M, K, N, seed=M + K, n_out=2)
+    count = oracle.find_outliers(X, threshold).size
+    assert M * count * 16 > 5000 * (2 * K - count), "case does not reach compaction"
+    run_all(torch, lm, X, W, threshold)
 
 
 @pytest.mark.parametrize("M,K,N,seed", SMALL)
