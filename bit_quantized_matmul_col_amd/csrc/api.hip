@@ -14,13 +14,18 @@ using namespace llmint8;
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxTileLd = (int64_t)1 << 21;  // 256 rows x 4 bytes x 2^21 = 2^31
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Row pitches of the padded int8 (bytes) and fp16 outlier (elements) copies of X.
+int64_t pitch_q(int64_t K) { return (K + 127) / 128 * 128; }
+int64_t pitch_o(int64_t K) { return (K + 63) / 64 * 64; }
+
 // Offsets (bytes) of the regions a call carves out of its workspace.
 struct Layout {
-  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, part, counters, total;
+  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, wot, part, total;
 };
 
 // Small-M layer calls: preparation outputs, split-K partial sums, counters.
@@ -58,14 +63,17 @@ Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer) {
     o += up((size_t)K * 4);
     L.count = o;
     o += up(64);
+    const size_t ldq = (size_t)pitch_q(K), ldo = (size_t)pitch_o(K);
     L.xq = o;
-    o += up((size_t)M * (size_t)K);
+    o += up((size_t)M * ldq);
     L.m = o;
     o += up((size_t)M * 4);
     L.xo = o;
-    o += up((size_t)M * (size_t)K * 2);
+    o += up((size_t)M * ldo * 2);
     L.wqc = o;
-    o += up((size_t)N * (size_t)K);
+    o += up((size_t)N * ldq);
+    L.wot = o;
+    o += up((size_t)N * ldo * 2);
   }
   L.total = o;
   return L;
@@ -169,6 +177,8 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   if (N % 8 != 0 || !aligned16(Wq) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
   if ((outlier_count_out && !aligned16(outlier_count_out)) || (C_debug && !aligned16(C_debug)))
     return LLMINT8_ERR_UNSUPPORTED;
+  // the GEMM addresses a 256-row output tile with 32-bit byte offsets
+  if (ldy >= kMaxTileLd || N >= kMaxTileLd) return LLMINT8_ERR_UNSUPPORTED;
   const Layout L = make_layout(M, K, N, true);
   if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
@@ -202,11 +212,16 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
 
   DetectOut d{(uint32_t *)(ws + L.pmask), omask, wprefix, idx, (int32_t *)(ws + L.nidx), count,
               outlier_count_out};
+  const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
+  uint16_t *wot = (uint16_t *)(ws + L.wot);
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
-  if (e == hipSuccess) e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, m, xo, K, s);
-  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, s);
+  if (e == hipSuccess)
+    e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, ldq, m, xo, ldo, s);
+  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, ldq, s);
+  if (e == hipSuccess && W) e = launch_gather_wot(W, ldw, N, idx, count, wot, ldo, s);
   if (e == hipSuccess) {
-    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, W, idx, count, Y, C_debug, M, N, K, K, ldw, ldy};
+    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, W, count, Y, C_debug, M, N, K, ldq, ldo, ldw,
+               ldy};
     if (ev.begin) e = hipEventRecord((hipEvent_t)ev.begin, s);
     if (e == hipSuccess) e = launch_gemm(g, s);
     if (e == hipSuccess && ev.end) e = hipEventRecord((hipEvent_t)ev.end, s);

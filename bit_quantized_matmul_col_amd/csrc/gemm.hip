@@ -1,119 +1,214 @@
-// int8 GEMM + fused epilogue of the LLM.int8() linear layer on gfx950 MFMA.
+// Large-M GEMM of the LLM.int8() linear layer on gfx950 MFMA, with the
+// dequantize-and-add epilogue fused in.
 //
 // C = Xq . Wq^T with int32 accumulation (the int8 x int8 -> int32 matmul of the
-// "8-Bit LLM Quantization with Lightning Fabric" page, section 2.2), then
+// "8-Bit LLM Quantization with Lightning Fabric" page, section 2.2); then
 // Y = C * m[i] * s[n] / 127^2 + X_O . W_O, the 16-bit outlier product added to
 // the dequantized int8 result ("LLM.int8() pitfalls" page, section 3.3;
-// "LLM.int8()" walkthrough, section 2.3). Both operands of the int8 product are
-// K-contiguous, so both stream into LDS with 16-byte loads.
+// "LLM.int8()" walkthrough, section 2.3), accumulated in fp32.
 //
-// MFMA lane layouts (gfx950, checked on hardware): for v_mfma_*_32x32x32_i8 and
-// v_mfma_f32_32x32x16_f16 lane l supplies row (A) / column (B) l % 32 and the
-// k-group l / 32 of 16 bytes (8 fp16); the 32x32 result sits in 16 registers,
-// register r of lane l holding row 8(r/4) + 4(l/32) + r%4, column l % 32. The
-// 16x16x64_i8 form has lane l supply row/column l % 16, k-group l / 16, and
-// result register r holding row 4(l/16) + r, column l % 16. Only the pairing
-// of A and B k-groups matters for an exact integer dot product, and both
-// operands use the same one.
+// Design (one 256-thread block per BM x BN output tile, 4 waves of
+// BM/2 x BN/2, 32x32 MFMA blocks):
+//  * Operands stream through LDS in stages of 128 bytes of k per row (128 int8
+//    or 64 fp16), two stages deep, filled by buffer_load_dwordx4 ... lds: lane
+//    l of a wave instruction lands at base + 16 l, so each instruction moves
+//    8 rows x 128 B with no register staging. Each operand tile is one buffer
+//    resource starting at the tile's first row; a lane keeps one 32-bit offset
+//    per 8-row group and the stage's k offset is scalar. Rows past the matrix
+//    end lie past the resource's record count and read as zero, so there is no
+//    bounds arithmetic in the loop. The k-loop issues stage t + 1 before the
+//    MFMAs of stage t.
+//  * The 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), so the
+//    16 rows that lanes 0..15 read for one MFMA operand fall in 16 different
+//    bank groups.
+//  * The int8 operand Xq is zero from column K (or K - |O|) to its padded
+//    pitch, so whatever the other operand holds there adds nothing.
+//  * After the int8 k-loop the int32 accumulators are scaled to fp32 in place
+//    and a second k-loop with v_mfma_f32_32x32x16_f16 adds X_O . W_O over the
+//    gathered outlier columns (X_O [M x ldo] and the pre-transposed W_O^T
+//    [N x ldo], both zero-padded to 64 columns).
+//  * Blocks are renumbered so each XCD (blocks are dealt to the 8 XCDs round
+//    robin) works on a contiguous, M-grouped range of tiles and shares operand
+//    stages through its own L2.
+//
+// MFMA lane layouts (gfx950, checked on hardware): for v_mfma_i32_32x32x32_i8
+// and v_mfma_f32_32x32x16_f16 lane l supplies row (A) / column (B) l % 32 and
+// k-group l / 32 of 16 bytes; register r of the 32x32 result holds row
+// 8(r/4) + 4(l/32) + r%4, column l % 32. Both operands use the same k-groups,
+// which is all an exact integer dot product needs.
 #include "internal.hpp"
 
 namespace llmint8 {
 
 namespace {
 
-constexpr int BK = 64;              // int8 k per main-loop step
-constexpr int P8 = BK + 16;         // LDS row pitch (bytes) of int8 tiles
-constexpr int OKC = 32;             // fp16 outlier columns per chunk
-constexpr int P16 = OKC + 8;        // LDS row pitch (fp16 elements) of outlier tiles
+constexpr int SK = 128;     // bytes of k per stage and row
+constexpr int kXcds = 8;    // XCDs of the MI355X
+constexpr int kGroupM = 8;  // tile rows per ordering group
 
-__device__ inline u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
 
-// Outlier product for one output tile, accumulated into fp32 MFMA registers.
-// X_O [BM x 32] comes from the gathered outlier columns; W_O [32 x BN] are the
-// fp16 weight rows idx[p], transposed into LDS so both operands are k-contiguous.
-template <int BM, int BN, int WM, int WN>
-__device__ inline void outlier_product(const GemmArgs &a, int count, int64_t m0, int64_t n0,
-                                       int wm, int wn, uint16_t *sXO, uint16_t *sWO,
-                                       f32x16 (&accf)[WM / 32][WN / 32]) {
-  constexpr int MI = WM / 32, NI = WN / 32;
-  const int t = threadIdx.x, lane = t & 63;
-  for (int p0 = 0; p0 < count; p0 += OKC) {
-    for (int q = t; q < BM * (OKC / 8); q += 256) {
-      const int row = q / (OKC / 8), pc = q % (OKC / 8);
-      const int64_t gm = m0 + row;
-      const int p = p0 + pc * 8;
-      u32x4 v = zero4();
-      if (gm < a.M && p < count) {
-        v = *(const u32x4 *)(a.xo + gm * a.ldo + p);
+// Raw buffer resource over [base, base + bytes): 32-bit word count, data format
+// field set as gfx9 raw dword access requires.
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offset of logical 16-byte chunk c of row r inside a stage.
+__device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ ((r >> 1) & 7)); }
+
+// One operand tile: ROWS rows from row0 of a row-major matrix. Wave w loads the
+// 8-row groups w, w + 4, ...; lane l of a group fetches the logical chunk that
+// belongs at physical slot l % 8 of row l / 8.
+template <int ROWS>
+struct OperandTile {
+  static constexpr int G = ROWS / 32;  // 8-row groups per wave
+  rsrc_t rs;
+  int voff[G];
+
+  __device__ void init(const void *base, int64_t ld_bytes, int64_t row0, int64_t nrows) {
+    int64_t rows = nrows - row0;
+    rows = rows < ROWS ? rows : ROWS;
+    rs = make_rsrc((const uint8_t *)base + row0 * ld_bytes, rows * ld_bytes);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (p + e >= count) v[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-      }
-      *(u32x4 *)(sXO + row * P16 + pc * 8) = v;
+    for (int j = 0; j < G; ++j) {
+      const int r = (wv + 4 * j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[j] = r * (int)ld_bytes + 16 * c;
     }
-    for (int q = t; q < OKC * (BN / 8); q += 256) {
-      const int pr = q / (BN / 8), c = q % (BN / 8);
-      const int p = p0 + pr;
-      const int64_t n = n0 + c * 8;
-      u32x4 v = zero4();
-      if (p < count && n < a.N) v = *(const u32x4 *)(a.w + (int64_t)a.idx[p] * a.ldw + n);
+  }
+
+  __device__ void load(uint8_t *stage, int kbyte) const {
+    const int wv = threadIdx.x >> 6;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = v[e >> 1];
-        sWO[(c * 8 + e) * P16 + pr] = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-      }
-    }
-    __syncthreads();
+    for (int j = 0; j < G; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + 4 * j) * 8 * SK), 16,
+                                                voff[j], kbyte, 0, 0);
+  }
+};
+
+template <int BM, int BN>
+struct TileCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int MI = WM / 32, NI = WN / 32;
+  static constexpr int STAGE = (BM + BN) * SK;
+  static constexpr int LDS = 2 * STAGE + (BM + BN) * 4;
+};
+
+// Tile coordinates of this block after the XCD-aware renumbering.
+__device__ inline void tile_of_block(int64_t tiles_m, int64_t tiles_n, int64_t &tm, int64_t &tn) {
+  const int64_t nb = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t x = bid % kXcds, q = nb / kXcds, rem = nb % kXcds;
+  const int64_t v = x * q + (x < rem ? x : rem) + bid / kXcds;
+  const int64_t group = kGroupM * tiles_n;
+  const int64_t first_m = (v / group) * kGroupM;
+  const int64_t gm = (tiles_m - first_m < kGroupM) ? tiles_m - first_m : kGroupM;
+  tm = first_m + (v % group) % gm;
+  tn = (v % group) / gm;
+}
+
+// The MFMAs of one 128-byte stage (4 k-steps of 32 bytes): int8 operands.
+template <int BM, int BN, int MI, int NI>
+__device__ inline void stage_mfma_i8(const uint8_t *cur, int wm, int wn, int li, int lg,
+                                     i32x16 (&acc)[MI][NI]) {
+  constexpr int WM = BM / 2, WN = BN / 2;
 #pragma unroll
-    for (int kk = 0; kk < OKC; kk += 16) {
-      f16x8 xa[MI], wb[NI];
+  for (int ks = 0; ks < 4; ++ks) {
+    i32x4 av[MI], bv[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        xa[mi] = *(const f16x8 *)(sXO + (wm * WM + mi * 32 + (lane & 31)) * P16 + kk +
-                                  8 * (lane >> 5));
+    for (int mi = 0; mi < MI; ++mi)
+      av[mi] = *(const i32x4 *)(cur + swz(wm * WM + mi * 32 + li, 2 * ks + lg));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      bv[ni] = *(const i32x4 *)(cur + BM * SK + swz(wn * WN + ni * 32 + li, 2 * ks + lg));
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        wb[ni] = *(const f16x8 *)(sWO + (wn * WN + ni * 32 + (lane & 31)) * P16 + kk +
-                                  8 * (lane >> 5));
+        acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// The same stage geometry with fp16 operands (64 fp16 per row, 4 k-steps of 16).
+template <int BM, int BN, int MI, int NI>
+__device__ inline void stage_mfma_f16(const uint8_t *cur, int wm, int wn, int li, int lg,
+                                      i32x16 (&acc)[MI][NI]) {
+  constexpr int WM = BM / 2, WN = BN / 2;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+  for (int ks = 0; ks < 4; ++ks) {
+    f16x8 av[MI], bv[NI];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          accf[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[mi], wb[ni], accf[mi][ni], 0, 0, 0);
+    for (int mi = 0; mi < MI; ++mi)
+      av[mi] = *(const f16x8 *)(cur + swz(wm * WM + mi * 32 + li, 2 * ks + lg));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      bv[ni] = *(const f16x8 *)(cur + BM * SK + swz(wn * WN + ni * 32 + li, 2 * ks + lg));
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_bit_cast(
+            i32x16, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        av[mi], bv[ni], __builtin_bit_cast(f32x16, acc[mi][ni]), 0, 0, 0));
+  }
+}
+
+// Two-stage pipelined k-loop over nstages 128-byte stages of A and B: the next
+// stage's loads are in flight while the MFMAs consume the current one. fp16
+// selects the outlier-product MFMAs (uniform across the block).
+template <int BM, int BN, int MI, int NI>
+__device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const OperandTile<BN> &B,
+                             int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
+                             i32x16 (&acc)[MI][NI]) {
+  constexpr int STAGE = (BM + BN) * SK;
+  if (nstages <= 0) return;
+  A.load(smem, 0);
+  B.load(smem + BM * SK, 0);
+  wait_vm();
+  __syncthreads();
+  for (int64_t it = 0; it < nstages; ++it) {
+    const uint8_t *cur = smem + (it & 1) * STAGE;
+    if (it + 1 < nstages) {
+      uint8_t *nxt = smem + ((it + 1) & 1) * STAGE;
+      A.load(nxt, (int)((it + 1) * SK));
+      B.load(nxt + BM * SK, (int)((it + 1) * SK));
     }
+    if (fp16)
+      stage_mfma_f16<BM, BN, MI, NI>(cur, wm, wn, li, lg, acc);
+    else
+      stage_mfma_i8<BM, BN, MI, NI>(cur, wm, wn, li, lg, acc);
+    wait_vm();
     __syncthreads();
   }
 }
 
-// Tiled kernel for prefill shapes: a 256-thread block computes a BM x BN tile,
-// its 4 waves a WM x WN sub-tile each from 32x32 MFMA blocks. Operand tiles
-// are double-buffered in LDS; the next tile's global loads are in flight while
-// the current one feeds the MFMAs.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
-  constexpr int WGN = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves per block");
-  constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int CPR = BK / 16;                // 16-byte chunks per tile row
-  constexpr int A_CH = BM * CPR / 256;
-  constexpr int B_CH = BN * CPR / 256;
+template <int BM, int BN, bool DBG>
+__global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
+  using T = TileCfg<BM, BN>;
+  constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
   extern __shared__ u32x4 smem_v[];
   uint8_t *smem = (uint8_t *)smem_v;
-  uint8_t *sA = smem;
-  uint8_t *sB = smem + 2 * BM * P8;
+  float *sm = (float *)(smem + 2 * T::STAGE);
+  float *ss = sm + BM;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wm = wv / WGN, wn = wv % WGN;
-  const int64_t tiles_m = (a.M + BM - 1) / BM;
-  const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * BM;
-  const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * BN;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int li = lane & 31, lg = lane >> 5;
+  int64_t tm, tn;
+  tile_of_block((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int count = *a.count;
   const bool compact = use_compaction(count, a.K, a.M);
-  const int8_t *B = compact ? a.wqc : a.wq;
-  const int64_t K = a.K;
-  const int64_t Kl = compact ? K - count : K;
+  const int64_t Kl = compact ? a.K - count : a.K;
+
+  for (int i = t; i < BM; i += 256) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
+  for (int i = t; i < BN; i += 256) ss[i] = (n0 + i < a.N) ? a.s[n0 + i] * (1.0f / 16129.0f) : 0.f;
 
   i32x16 acc[MI][NI];
 #pragma unroll
@@ -121,110 +216,145 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = (i32x16){};
 
-  u32x4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int u = 0; u < A_CH; ++u) {
-      const int q = t + 256 * u;
-      const int64_t gm = m0 + q / CPR, gk = k0 + (q % CPR) * 16;
-      ra[u] = (gm < a.M && gk < Kl) ? *(const u32x4 *)(a.xq + gm * K + gk) : zero4();
-    }
-#pragma unroll
-    for (int u = 0; u < B_CH; ++u) {
-      const int q = t + 256 * u;
-      const int64_t gn = n0 + q / CPR, gk = k0 + (q % CPR) * 16;
-      rb[u] = (gn < a.N && gk < Kl) ? *(const u32x4 *)(B + gn * K + gk) : zero4();
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < A_CH; ++u) {
-      const int q = t + 256 * u;
-      *(u32x4 *)(sA + (buf * BM + q / CPR) * P8 + (q % CPR) * 16) = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < B_CH; ++u) {
-      const int q = t + 256 * u;
-      *(u32x4 *)(sB + (buf * BN + q / CPR) * P8 + (q % CPR) * 16) = rb[u];
-    }
-  };
-
-  const int64_t nk = (Kl + BK - 1) / BK;
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int64_t it = 0; it < nk; ++it) {
-    const int buf = (int)(it & 1);
-    if (it + 1 < nk) gload((it + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      i32x4 af[MI], bf[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *(const i32x4 *)(sA + (buf * BM + wm * WM + mi * 32 + (lane & 31)) * P8 + kk +
-                                  16 * (lane >> 5));
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        bf[ni] = *(const i32x4 *)(sB + (buf * BN + wn * WN + ni * 32 + (lane & 31)) * P8 + kk +
-                                  16 * (lane >> 5));
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (it + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+  {
+    OperandTile<BM> A;
+    OperandTile<BN> B;
+    A.init(a.xq, a.ldq, m0, a.M);
+    if (compact)
+      B.init(a.wqc, a.ldq, n0, a.N);
+    else
+      B.init(a.wq, a.K, n0, a.N);
+    kloop<BM, BN, MI, NI>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg, acc);
   }
 
-  // Dequantize: C * m[i] * s[n] / 127^2 (exact int32 kept for the debug copy).
-  f32x16 accf[MI][NI];
+  // dequantize in place: C * m[i] * s[n] / 127^2
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int64_t col = n0 + wn * WN + ni * 32 + (lane & 31);
-      const float sc = (col < a.N) ? a.s[col] * (1.0f / 16129.0f) : 0.f;
+      const int cl = wn * WN + ni * 32 + li;
+      const float sc = ss[cl];
+      f32x16 f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const float mr = (row < a.M) ? a.m[row] : 0.f;
-        if (a.cdbg && row < a.M && col < a.N) a.cdbg[row * a.N + col] = acc[mi][ni][r];
-        accf[mi][ni][r] = (float)acc[mi][ni][r] * (mr * sc);
+        const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        f[r] = (float)acc[mi][ni][r] * (sm[rl] * sc);
       }
+      if constexpr (DBG) {
+        const bool colok = n0 + cl < a.N;
+        int64_t rows = a.M - m0;
+        rows = rows < BM ? rows : BM;
+        const rsrc_t rc = make_rsrc(a.cdbg + m0 * a.N, rows * a.N * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (colok)
+            __builtin_amdgcn_raw_buffer_store_b32(acc[mi][ni][r], rc,
+                                                  (rl * (int)a.N + (int)(n0 + cl)) * 4, 0, 0);
+        }
+      }
+      acc[mi][ni] = __builtin_bit_cast(i32x16, f);
     }
 
+  // fp16 outlier product X_O . W_O over the gathered outlier columns
   if (count > 0 && a.w) {
-    uint16_t *sXO = (uint16_t *)smem;
-    uint16_t *sWO = sXO + BM * P16;
-    outlier_product<BM, BN, WM, WN>(a, count, m0, n0, wm, wn, sXO, sWO, accf);
+    OperandTile<BM> A;
+    OperandTile<BN> B;
+    A.init(a.xo, a.ldo * 2, m0, a.M);
+    B.init(a.wot, a.ldo * 2, n0, a.N);
+    kloop<BM, BN, MI, NI>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg, acc);
   }
 
+  // store Y (fp16, round to nearest even); rows past M fall outside the resource
+  int64_t rows = a.M - m0;
+  rows = rows < BM ? rows : BM;
+  const rsrc_t ry = make_rsrc(a.y + m0 * a.ldy, rows * a.ldy * 2);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int64_t col = n0 + wn * WN + ni * 32 + (lane & 31);
+      const int cl = wn * WN + ni * 32 + li;
+      if (n0 + cl >= a.N) continue;
+      const f32x16 f = __builtin_bit_cast(f32x16, acc[mi][ni]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < a.M && col < a.N) a.y[row * a.ldy + col] = f2h(accf[mi][ni][r]);
+        const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        __builtin_amdgcn_raw_buffer_store_b16(f2h(f[r]), ry,
+                                              (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
       }
     }
 }
 
+// W_O^T [N x ldo] (fp16): row n holds W[idx[p], n] for p < |O|, zeros up to the
+// next multiple of 64. One block per 64 columns of W, 64 outlier rows per step,
+// transposed through LDS.
+__global__ __launch_bounds__(256) void k_gather_wot(const uint16_t *__restrict__ W, int64_t ldw,
+                                                    int64_t N, const int32_t *__restrict__ idx,
+                                                    const int32_t *__restrict__ count_ptr,
+                                                    uint16_t *__restrict__ wot, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t st[64 * 72];  // [n][p], pitch 72
+  const int count = *count_ptr;
+  const int t = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t pad = (count + 63) / 64 * 64;
+  for (int64_t p0 = 0; p0 < pad; p0 += 64) {
+    u32x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int p = q >> 3, ch = q & 7;  // 64 rows x 8 chunks of 8 fp16
+      const int64_t n = n0 + ch * 8;
+      const bool ok = p0 + p < count && n < N;
+      const int64_t src = ok ? (int64_t)idx[p0 + p] * ldw + n : 0;
+      const u32x4 x = *(const u32x4 *)(W + src);
+      v[u] = ok ? x : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int p = q >> 3, ch = q & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = v[u][e >> 1];
+        st[(ch * 8 + e) * 72 + p] = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int nl = q >> 3, ch = q & 7;  // 64 output rows x 8 chunks
+      const int64_t n = n0 + nl;
+      if (n < N) *(u32x4 *)(wot + n * ldo + p0 + ch * 8) = *(const u32x4 *)(st + nl * 72 + ch * 8);
+    }
+    __syncthreads();
+  }
+}
+
+template <bool DBG>
+hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream) {
+  constexpr int BM = 256, BN = 256;
+  using T = TileCfg<BM, BN>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, DBG>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_prefill<BM, BN, DBG>), dim3((unsigned)tiles), dim3(256), T::LDS,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const size_t lds = 2 * (BM + BN) * P8;
-  hipLaunchKernelGGL((k_gemm_tile<BM, BN, 64, 64>), dim3((unsigned)tiles), dim3(256), lds, stream,
-                     a);
+hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const int32_t *idx,
+                             const int32_t *count, uint16_t *wot, int64_t ldo, hipStream_t stream) {
+  hipLaunchKernelGGL(k_gather_wot, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream, W, ldw,
+                     N, idx, count, wot, ldo);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+  return a.cdbg ? launch_prefill<true>(a, stream) : launch_prefill<false>(a, stream);
 }
 
 }  // namespace llmint8

@@ -37,10 +37,13 @@ hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t 
 // Row quantization inside the layer: outlier columns from the detection
 // bitmask; also gathers the outlier columns into xo [M x ldo] and, when the
 // outlier share calls for it, writes compacted rows (K - |O| kept columns).
+// Xq rows have pitch ldq (a multiple of 128) and are zero past their last
+// column up to the next multiple of 128; xo rows have pitch ldo (a multiple of
+// 64) and are zero from |O| up to the next multiple of 64.
 hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                                  const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, int8_t *Xq, float *m, uint16_t *xo,
-                                 int64_t ldo, hipStream_t stream);
+                                 const int32_t *count, int8_t *Xq, int64_t ldq, float *m,
+                                 uint16_t *xo, int64_t ldo, hipStream_t stream);
 
 // Column absmax + quantize + transpose of W [K x N] into Wq [N x K].
 hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
@@ -50,21 +53,26 @@ hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, 
 // the outlier columns; a no-op unless the outlier share calls for it.
 hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
                              const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
-                             int8_t *Wqc, hipStream_t stream);
+                             int8_t *Wqc, int64_t ldq, hipStream_t stream);
+
+// W_O^T [N x ldo] fp16: row n holds W[idx[p], n] for p < |O|, then zeros up to
+// the next multiple of 64.
+hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const int32_t *idx,
+                             const int32_t *count, uint16_t *wot, int64_t ldo, hipStream_t stream);
 
 struct GemmArgs {
-  const int8_t *xq;      // [M x K] int8 (compacted rows when compaction is on)
+  const int8_t *xq;      // [M x ldq] int8 (compacted rows when compaction is on)
   const int8_t *wq;      // [N x K] int8, caller's
-  const int8_t *wqc;     // [N x K] int8 compacted copy (workspace)
+  const int8_t *wqc;     // [N x ldq] int8 compacted copy (workspace)
   const float *m;        // [M]
   const float *s;        // [N]
   const uint16_t *xo;    // [M x ldo] fp16 gathered outlier columns
-  const uint16_t *w;     // [K x ldw] fp16 original weight (rows in O are read)
-  const int32_t *idx;    // [K] outlier columns
+  const uint16_t *wot;   // [N x ldo] fp16 outlier rows of W, transposed
+  const uint16_t *w;     // [K x ldw] fp16 original weight (null: no outlier product)
   const int32_t *count;  // [1]
   uint16_t *y;           // [M x ldy] fp16
   int32_t *cdbg;         // optional [M x N] int32
-  int64_t M, N, K, ldo, ldw, ldy;
+  int64_t M, N, K, ldq, ldo, ldw, ldy;
 };
 
 // Large-M tiled GEMM with the fused dequantize + outlier epilogue.

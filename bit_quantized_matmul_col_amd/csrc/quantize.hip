@@ -91,13 +91,16 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
 // Row quantization inside the layer. One block per row. Besides Xq and m it
 // gathers the row's outlier entries into xo (position = rank of the column in
 // the ascending outlier list) and, in compaction mode, writes the kept codes
-// contiguously (staged in LDS so the global stores stay 16-byte wide) with a
-// zeroed tail up to the next 16 bytes.
+// contiguously (staged in LDS so the global stores stay 16-byte wide). Rows of
+// Xq (pitch ldq) are zero past their last column up to the next multiple of
+// 128 bytes and rows of xo (pitch ldo) from |O| up to the next multiple of 64,
+// so the GEMM can run whole 128-byte k stages.
 __global__ __launch_bounds__(256) void k_rowquant_layer(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const uint32_t *__restrict__ omask,
     const int32_t *__restrict__ wprefix, const int32_t *__restrict__ count_ptr,
-    int8_t *__restrict__ Xq, float *__restrict__ m, uint16_t *__restrict__ xo, int64_t ldo) {
+    int8_t *__restrict__ Xq, int64_t ldq, float *__restrict__ m, uint16_t *__restrict__ xo,
+    int64_t ldo) {
   extern __shared__ u32x4 srow_v[];
   uint8_t *srow = (uint8_t *)srow_v;
   __shared__ float red[4];
@@ -122,8 +125,10 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   if (t == 0) m[i] = mx;
   const bool zero_row = !(mx > 0.f);
   const float inv = zero_row ? 0.f : inv_scale(mx);
-  int8_t *qrow = Xq + i * K;
+  int8_t *qrow = Xq + i * ldq;
   uint16_t *orow = xo + i * ldo;
+  const int64_t opad = (count + 63) / 64 * 64;
+  for (int64_t p = count + t; p < opad; p += 256) orow[p] = 0;
 
   for (int64_t ch = t; ch < nch; ch += 256) {
     const u32x4 v = *(const u32x4 *)(row + ch * 8);
@@ -148,11 +153,14 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   }
   if (compact) {
     const int64_t kk = K - count;
-    const int64_t kpad = (kk + 15) & ~(int64_t)15;
+    const int64_t kpad = (kk + 127) / 128 * 128;
     for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
     __syncthreads();
     for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
       *(u32x4 *)(qrow + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
+  } else {
+    for (int64_t c16 = K / 16 + t; c16 < ldq / 16; c16 += 256)
+      *(u32x4 *)(qrow + c16 * 16) = (u32x4){0u, 0u, 0u, 0u};
   }
 }
 
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ W
                                                     const uint32_t *__restrict__ omask,
                                                     const int32_t *__restrict__ wprefix,
                                                     const int32_t *__restrict__ count_ptr,
-                                                    int8_t *__restrict__ Wqc) {
+                                                    int8_t *__restrict__ Wqc, int64_t ldq) {
   extern __shared__ u32x4 srow_v[];
   uint8_t *srow = (uint8_t *)srow_v;
   const int count = *count_ptr;
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ W
   const int t = threadIdx.x;
   const int64_t kw = (K + 31) / 32;
   const int64_t kk = K - count;
-  const int64_t kpad = (kk + 15) & ~(int64_t)15;
+  const int64_t kpad = (kk + 127) / 128 * 128;
   for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
     const int8_t *row = Wq + n * K;
     for (int64_t w = t; w < kw; w += 256) {
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ W
     }
     for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
     __syncthreads();
-    int8_t *out = Wqc + n * K;
+    int8_t *out = Wqc + n * ldq;
     for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
       *(u32x4 *)(out + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
     __syncthreads();
@@ -305,11 +313,11 @@ hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t 
 
 hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                                  const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, int8_t *Xq, float *m, uint16_t *xo,
-                                 int64_t ldo, hipStream_t stream) {
-  const size_t lds = (K <= kCompactMaxK) ? (size_t)K : 0;
+                                 const int32_t *count, int8_t *Xq, int64_t ldq, float *m,
+                                 uint16_t *xo, int64_t ldo, hipStream_t stream) {
+  const size_t lds = (K <= kCompactMaxK) ? (size_t)ldq : 0;
   hipLaunchKernelGGL(k_rowquant_layer, dim3((unsigned)M), dim3(256), lds, stream, X, M, K, ldx,
-                     omask, wprefix, count, Xq, m, xo, ldo);
+                     omask, wprefix, count, Xq, ldq, m, xo, ldo);
   return hipGetLastError();
 }
 
@@ -336,11 +344,11 @@ hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, 
 
 hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
                              const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
-                             int8_t *Wqc, hipStream_t stream) {
+                             int8_t *Wqc, int64_t ldq, hipStream_t stream) {
   if (!use_compaction((int)K, K, M)) return hipSuccess;  // never applies at this shape
   int64_t blocks = N < 4096 ? N : 4096;
-  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)K, stream, Wq, M, K,
-                     N, omask, wprefix, count, Wqc);
+  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)ldq, stream, Wq, M,
+                     K, N, omask, wprefix, count, Wqc, ldq);
   return hipGetLastError();
 }
 

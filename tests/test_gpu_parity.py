@@ -75,7 +75,10 @@ def run_all(torch, lm, X, W, threshold, rows=None, check_colwise=True, ref_w=Non
     cnt_lin = torch.empty(1, dtype=torch.int32, device="cuda")
     C_d = torch.empty((M, N), dtype=torch.int32, device="cuda")
     Y_d = lm.llmint8_linear(Xd, Wq_d, s_d, Wd, threshold, outlier_count=cnt_lin, C_debug=C_d)
+    # the production path (no int32 copy) must give the same bits
+    Y_p = lm.llmint8_linear(Xd, Wq_d, s_d, Wd, threshold)
     torch.cuda.synchronize()
+    assert torch.equal(Y_d.view(torch.int16), Y_p.view(torch.int16)), "debug/production Y differ"
     assert int(cnt_lin.cpu().item()) == idx_r.size
     if rows is None:
         C_r = oracle.gemm_i8(Xq_r, Wq_r)
