@@ -9,9 +9,9 @@
 // so every wave load is a fully coalesced 1 KB row segment. The running column
 // maxima are compared with the threshold once at the end (max >= t is the same
 // test as "some entry >= t") and stored as 16 mask words per row chunk.
-// Pass 2 (k_detect_finish): one block ORs the row-chunk masks, scans the
-// per-word popcounts and writes the ascending outlier list, the ascending kept
-// list, the per-word prefix and the count. No atomics, no host round trip.
+// Pass 2 (k_detect_finish): one block ORs the row-chunk masks into LDS (all
+// partial-mask loads in flight at once), scans the per-word popcounts and writes
+// the ascending outlier and kept lists, the per-word prefix and the count.
 #include "internal.hpp"
 
 namespace llmint8 {
@@ -72,17 +72,37 @@ __global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restri
 __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restrict__ pmask,
                                                         int row_chunks, int64_t K, int64_t kw,
                                                         DetectOut out) {
+  extern __shared__ uint32_t smask[];  // [kw]
   const int t = threadIdx.x;
+  for (int64_t w = t; w < kw; w += 1024) smask[w] = 0u;
+  __syncthreads();
+  // OR the row-chunk masks: every thread issues a batch of independent loads,
+  // then merges the non-zero words (rare) into LDS.
+  constexpr int kBatch = 8;
+  const int64_t total_words = (int64_t)row_chunks * kw;
+  for (int64_t base = 0; base < total_words; base += 1024 * kBatch) {
+    uint32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t q = base + t + 1024 * u;
+      const uint32_t x = pmask[q < total_words ? q : 0];
+      v[u] = q < total_words ? x : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (v[u]) atomicOr(&smask[(base + t + 1024 * u) % kw], v[u]);
+  }
+  __syncthreads();
+
   const int64_t per = (kw + 1023) / 1024;
   const int64_t w0 = (int64_t)t * per;
   const int64_t w1 = (w0 + per < kw) ? w0 + per : kw;
-
   int local = 0;
   for (int64_t w = w0; w < w1; ++w) {
-    uint32_t v = 0;
-    for (int rc = 0; rc < row_chunks; ++rc) v |= pmask[(int64_t)rc * kw + w];
+    uint32_t v = smask[w];
     const int64_t valid = K - 32 * w;  // columns of this word inside K
     if (valid < 32) v &= (1u << valid) - 1u;
+    smask[w] = v;
     out.omask[w] = v;
     local += __builtin_popcount(v);
   }
@@ -107,7 +127,7 @@ __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restri
   int pos = before + incl - local;
 
   for (int64_t w = w0; w < w1; ++w) {
-    const uint32_t v = out.omask[w];
+    const uint32_t v = smask[w];
     out.wprefix[w] = pos;
     const int nb = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
     for (int b = 0; b < nb; ++b) {
@@ -145,7 +165,8 @@ hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, f
                      X, M, K, ldx, threshold, plan.rows_per_chunk, plan.kw, out.pmask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_detect_finish, dim3(1), dim3(1024), 0, stream, (const uint32_t *)out.pmask,
+  hipLaunchKernelGGL(k_detect_finish, dim3(1), dim3(1024), (size_t)plan.kw * 4, stream,
+                     (const uint32_t *)out.pmask,
                      plan.row_chunks, K, plan.kw, out);
   return hipGetLastError();
 }

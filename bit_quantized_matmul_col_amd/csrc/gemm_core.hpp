@@ -1,0 +1,315 @@
+// Large-M GEMM of the LLM.int8() linear layer on gfx950 MFMA, with the
+// dequantize-and-add epilogue fused in (kernel templates; each tile shape is
+// instantiated in its own translation unit).
+//
+// C = Xq . Wq^T with int32 accumulation (the int8 x int8 -> int32 matmul of the
+// "8-Bit LLM Quantization with Lightning Fabric" page, section 2.2); then
+// Y = C * m[i] * s[n] / 127^2 + X_O . W_O, the 16-bit outlier product added to
+// the dequantized int8 result ("LLM.int8() pitfalls" page, section 3.3;
+// "LLM.int8()" walkthrough, section 2.3), accumulated in fp32.
+//
+// Design (one 256-thread block per BM x BN output tile, 4 waves of
+// BM/2 x BN/2, 32x32 MFMA blocks):
+//  * Operands stream through LDS in stages of 128 bytes of k per row (128 int8
+//    or 64 fp16), two stages deep, filled by buffer_load_dwordx4 ... lds: lane
+//    l of a wave instruction lands at base + 16 l, so each instruction moves
+//    8 rows x 128 B with no register staging. Each operand tile is one buffer
+//    resource starting at the tile's first row; a lane keeps one 32-bit offset
+//    per 8-row group and the stage's k offset is scalar. Rows past the matrix
+//    end lie past the resource's record count and read as zero, so there is no
+//    bounds arithmetic in the loop. The k-loop issues stage t + 1 before the
+//    MFMAs of stage t.
+//  * The 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), so the
+//    16 rows that lanes 0..15 read for one MFMA operand fall in 16 different
+//    bank groups.
+//  * The int8 operand Xq is zero from column K (or K - |O|) to its padded
+//    pitch, so whatever the other operand holds there adds nothing.
+//  * After the int8 k-loop the int32 accumulators are scaled to fp32 in place
+//    and a second k-loop with v_mfma_f32_32x32x16_f16 adds X_O . W_O over the
+//    gathered outlier columns (X_O [M x ldo] and the pre-transposed W_O^T
+//    [N x ldo], both zero-padded to 64 columns).
+//  * Blocks are renumbered so each XCD (blocks are dealt to the 8 XCDs round
+//    robin) works on a contiguous, M-grouped range of tiles and shares operand
+//    stages through its own L2.
+//
+// MFMA lane layouts (gfx950, checked on hardware): for v_mfma_i32_32x32x32_i8
+// and v_mfma_f32_32x32x16_f16 lane l supplies row (A) / column (B) l % 32 and
+// k-group l / 32 of 16 bytes; register r of the 32x32 result holds row
+// 8(r/4) + 4(l/32) + r%4, column l % 32. Both operands use the same k-groups,
+// which is all an exact integer dot product needs.
+#pragma once
+
+#include "internal.hpp"
+
+namespace llmint8 {
+namespace gemm_detail {
+
+
+constexpr int SK = 128;     // bytes of k per stage and row
+constexpr int kXcds = 8;    // XCDs of the MI355X
+constexpr int kGroupM = 8;  // tile rows per ordering group
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// Raw buffer resource over [base, base + bytes): 32-bit word count, data format
+// field set as gfx9 raw dword access requires.
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offset of logical 16-byte chunk c of row r inside a stage.
+__device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ ((r >> 1) & 7)); }
+
+// One operand tile: ROWS rows from row0 of a row-major matrix. Wave w loads the
+// 8-row groups w, w + 4, ...; lane l of a group fetches the logical chunk that
+// belongs at physical slot l % 8 of row l / 8.
+template <int ROWS>
+struct OperandTile {
+  static constexpr int G = ROWS / 32;  // 8-row groups per wave
+  const uint8_t *base;  // first row of the tile
+  int bytes;            // bytes from base to the end of the matrix rows in the tile
+  int voff[G];
+
+  __device__ void init(const void *mat, int64_t ld_bytes, int64_t row0, int64_t nrows) {
+    int64_t rows = nrows - row0;
+    rows = rows < ROWS ? rows : ROWS;
+    base = (const uint8_t *)mat + row0 * ld_bytes;
+    bytes = (int)(rows * ld_bytes);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int r = (wv + 4 * j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[j] = r * (int)ld_bytes + 16 * c;
+    }
+  }
+
+  __device__ void load(uint8_t *stage, int kbyte) const {
+    const int wv = threadIdx.x >> 6;
+    const rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + 4 * j) * 8 * SK), 16,
+                                                voff[j], kbyte, 0, 0);
+  }
+};
+
+template <int BM, int BN>
+struct TileCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int MI = WM / 32, NI = WN / 32;
+  static constexpr int STAGE = (BM + BN) * SK;
+  static constexpr int LDS = 2 * STAGE + (BM + BN) * 4;
+};
+
+// Tile coordinates of this block after the XCD-aware renumbering.
+__device__ inline void tile_of_block(int64_t tiles_m, int64_t tiles_n, int64_t &tm, int64_t &tn) {
+  const int64_t nb = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t x = bid % kXcds, q = nb / kXcds, rem = nb % kXcds;
+  const int64_t v = x * q + (x < rem ? x : rem) + bid / kXcds;
+  const int64_t group = kGroupM * tiles_n;
+  const int64_t first_m = (v / group) * kGroupM;
+  const int64_t gm = (tiles_m - first_m < kGroupM) ? tiles_m - first_m : kGroupM;
+  tm = first_m + (v % group) % gm;
+  tn = (v % group) / gm;
+}
+
+// The MFMAs of one 128-byte stage (4 k-steps of 32 bytes). The operand
+// fragments of k-step ks + 1 are read from LDS (into the second of two
+// fragment buffers) before the MFMAs of k-step ks are issued; scheduling
+// barriers keep the compiler from sinking those reads next to their use, so
+// their latency hides behind the current k-step's MFMAs.
+template <typename V>
+__device__ inline V lds_frag(const uint8_t *p) {
+  return *(const V *)p;
+}
+
+template <int BM, int BN, int MI, int NI, typename V, typename MFMA>
+__device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, int lg,
+                                  i32x16 *acc, MFMA mfma) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  V av[2][MI], bv[2][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) av[0][mi] = lds_frag<V>(cur + swz(wm * WM + mi * 32 + li, lg));
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    bv[0][ni] = lds_frag<V>(cur + BM * SK + swz(wn * WN + ni * 32 + li, lg));
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int b = ks & 1;
+    if (ks + 1 < 4) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        av[b ^ 1][mi] = lds_frag<V>(cur + swz(wm * WM + mi * 32 + li, 2 * (ks + 1) + lg));
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        bv[b ^ 1][ni] =
+            lds_frag<V>(cur + BM * SK + swz(wn * WN + ni * 32 + li, 2 * (ks + 1) + lg));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = mfma(av[b][mi], bv[b][ni], acc[mi * NI + ni]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+struct MfmaI8 {
+  __device__ i32x16 operator()(i32x4 a, i32x4 b, i32x16 c) const {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+};
+
+struct MfmaF16 {
+  __device__ i32x16 operator()(f16x8 a, f16x8 b, i32x16 c) const {
+    return __builtin_bit_cast(i32x16, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                          a, b, __builtin_bit_cast(f32x16, c), 0, 0, 0));
+  }
+};
+
+// Two-stage pipelined k-loop over nstages 128-byte stages of A and B: the next
+// stage's loads are in flight while the MFMAs consume the current one. fp16
+// selects the outlier-product MFMAs (uniform across the block).
+template <int BM, int BN, int MI, int NI>
+__device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const OperandTile<BN> &B,
+                             int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
+                             i32x16 *acc) {
+  constexpr int STAGE = (BM + BN) * SK;
+  if (nstages <= 0) return;
+  A.load(smem, 0);
+  B.load(smem + BM * SK, 0);
+  wait_vm();
+  __syncthreads();
+  for (int64_t it = 0; it < nstages; ++it) {
+    const uint8_t *cur = smem + (it & 1) * STAGE;
+    if (it + 1 < nstages) {
+      uint8_t *nxt = smem + ((it + 1) & 1) * STAGE;
+      A.load(nxt, (int)((it + 1) * SK));
+      B.load(nxt + BM * SK, (int)((it + 1) * SK));
+    }
+    if (fp16)
+      stage_mfma<BM, BN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16());
+    else
+      stage_mfma<BM, BN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8());
+    wait_vm();
+    __syncthreads();
+  }
+}
+
+template <int BM, int BN, bool DBG>
+__global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
+  using T = TileCfg<BM, BN>;
+  constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
+  extern __shared__ u32x4 smem_v[];
+  uint8_t *smem = (uint8_t *)smem_v;
+  float *sm = (float *)(smem + 2 * T::STAGE);
+  float *ss = sm + BM;
+
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int li = lane & 31, lg = lane >> 5;
+  int64_t tm, tn;
+  tile_of_block((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int count = *a.count;
+  const bool compact = use_compaction(count, a.K, a.M);
+  const int64_t Kl = compact ? a.K - count : a.K;
+
+  for (int i = t; i < BM; i += 256) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
+  for (int i = t; i < BN; i += 256) ss[i] = (n0 + i < a.N) ? a.s[n0 + i] * (1.0f / 16129.0f) : 0.f;
+
+  i32x16 acc[MI * NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = (i32x16){};
+
+  {
+    OperandTile<BM> A;
+    OperandTile<BN> B;
+    A.init(a.xq, a.ldq, m0, a.M);
+    if (compact)
+      B.init(a.wqc, a.ldq, n0, a.N);
+    else
+      B.init(a.wq, a.K, n0, a.N);
+    kloop<BM, BN, MI, NI>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg, acc);
+  }
+
+  // dequantize in place: C * m[i] * s[n] / 127^2
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int cl = wn * WN + ni * 32 + li;
+      const float sc = ss[cl];
+      f32x16 f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        f[r] = (float)acc[mi * NI + ni][r] * (sm[rl] * sc);
+      }
+      if constexpr (DBG) {
+        const bool colok = n0 + cl < a.N;
+        int64_t rows = a.M - m0;
+        rows = rows < BM ? rows : BM;
+        const rsrc_t rc = make_rsrc(a.cdbg + m0 * a.N, rows * a.N * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (colok)
+            __builtin_amdgcn_raw_buffer_store_b32(acc[mi * NI + ni][r], rc,
+                                                  (rl * (int)a.N + (int)(n0 + cl)) * 4, 0, 0);
+        }
+      }
+      acc[mi * NI + ni] = __builtin_bit_cast(i32x16, f);
+    }
+
+  // fp16 outlier product X_O . W_O over the gathered outlier columns
+  if (count > 0 && a.w) {
+    OperandTile<BM> A;
+    OperandTile<BN> B;
+    A.init(a.xo, a.ldo * 2, m0, a.M);
+    B.init(a.wot, a.ldo * 2, n0, a.N);
+    kloop<BM, BN, MI, NI>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg, acc);
+  }
+
+  // store Y (fp16, round to nearest even); rows past M fall outside the resource
+  int64_t rows = a.M - m0;
+  rows = rows < BM ? rows : BM;
+  const rsrc_t ry = make_rsrc(a.y + m0 * a.ldy, rows * a.ldy * 2);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int cl = wn * WN + ni * 32 + li;
+      if (n0 + cl >= a.N) continue;
+      const f32x16 f = __builtin_bit_cast(f32x16, acc[mi * NI + ni]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        __builtin_amdgcn_raw_buffer_store_b16(f2h(f[r]), ry,
+                                              (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
+      }
+    }
+}
+
+template <int BM, int BN, bool DBG>
+hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream) {
+  using T = TileCfg<BM, BN>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, DBG>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_prefill<BM, BN, DBG>), dim3((unsigned)tiles), dim3(256), T::LDS,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gemm_detail
+}  // namespace llmint8

@@ -1,0 +1,11 @@
+// 256x128-tile instantiation of the large-M GEMM (its own translation unit).
+#include "gemm_core.hpp"
+
+namespace llmint8 {
+
+hipError_t launch_gemm_narrow(const GemmArgs &a, hipStream_t stream) {
+  return a.cdbg ? gemm_detail::launch_prefill<256, 128, true>(a, stream)
+                : gemm_detail::launch_prefill<256, 128, false>(a, stream);
+}
+
+}  // namespace llmint8

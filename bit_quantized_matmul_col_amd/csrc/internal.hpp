@@ -75,8 +75,11 @@ struct GemmArgs {
   int64_t M, N, K, ldq, ldo, ldw, ldy;
 };
 
-// Large-M tiled GEMM with the fused dequantize + outlier epilogue.
+// Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
+// tile shape (256x256 or 256x128) from the problem size.
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
+hipError_t launch_gemm_wide(const GemmArgs &args, hipStream_t stream);
+hipError_t launch_gemm_narrow(const GemmArgs &args, hipStream_t stream);
 
 // Caller-supplied events recorded around the GEMM kernel (may be null).
 struct GemmEvents {

@@ -346,7 +346,7 @@ hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
                              const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
                              int8_t *Wqc, int64_t ldq, hipStream_t stream) {
   if (!use_compaction((int)K, K, M)) return hipSuccess;  // never applies at this shape
-  int64_t blocks = N < 4096 ? N : 4096;
+  int64_t blocks = N < 1024 ? N : 1024;
   hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)ldq, stream, Wq, M,
                      K, N, omask, wprefix, count, Wqc, ldq);
   return hipGetLastError();
