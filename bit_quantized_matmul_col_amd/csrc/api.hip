@@ -222,9 +222,7 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   if (e == hipSuccess) {
     GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, W, count, Y, C_debug, M, N, K, ldq, ldo, ldw,
                ldy};
-    if (ev.begin) e = hipEventRecord((hipEvent_t)ev.begin, s);
-    if (e == hipSuccess) e = launch_gemm(g, s);
-    if (e == hipSuccess && ev.end) e = hipEventRecord((hipEvent_t)ev.end, s);
+    e = launch_gemm(g, ev, s);
   }
   return hip_status(e);
 }

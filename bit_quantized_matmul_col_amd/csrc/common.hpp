@@ -1,6 +1,7 @@
 // Device helpers shared by the gfx950 kernels of the LLM.int8() linear layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -2,10 +2,12 @@
 //
 // With M <= 64 rows the layer is bound by streaming the int8 weight Wq from
 // HBM (the decode regime of the INT8-vs-FP8 page, section one: every step
-// re-reads all weights). The path is three kernels; none waits on a chain of
-// dependent loads and none communicates across blocks inside a kernel (on
-// gfx950 each XCD has its own L2, so an agent-scope fence writes back and
-// invalidates a whole L2; stream order between kernels is the cheap handoff).
+// re-reads all weights). The path is three kernels. None communicates across
+// blocks inside a kernel (on gfx950 each XCD has its own L2, so an agent-scope
+// fence writes back and invalidates a whole L2; stream order between kernels
+// is the cheap handoff), and every load of a kernel is issued unconditionally
+// (clamped address, result masked afterwards) so that all of a thread's loads are in
+// flight before its first wait.
 //
 // k_decode_detect: block b owns 256 columns of X over all M rows. It writes the
 //   outlier bits of its columns (8 mask words) and, per row, the absmax over
@@ -25,9 +27,15 @@ namespace {
 constexpr int kDetCols = 256;      // columns per detection block
 constexpr int kDetRows = 8;        // row phases per detection block (32 x 8 threads)
 constexpr int kTileN = 64;         // output columns per GEMM / epilogue block
-constexpr int kSubK = 512;         // k bytes staged per GEMM block iteration
+constexpr int kSubK = 512;         // k bytes staged per GEMM stage
 constexpr int kXPitch = kSubK + 16;
-constexpr int kOutBatch = 16;      // outlier columns staged per epilogue round
+constexpr int kPmaxUnroll = 8;     // detection partials per thread loaded up front
+constexpr int kTargetBlocks = 256; // GEMM blocks aimed for (one per CU)
+constexpr int kMaxSplits = 16;
+constexpr int kListWords = 256;    // mask words scanned per epilogue window
+constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
+
+__device__ inline u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
 
 __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   __shared__ float scol[kDetRows][kDetCols];
@@ -36,14 +44,15 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   const int c = t & 31, ph = t >> 5;
   const int64_t col0 = (int64_t)blockIdx.x * kDetCols + c * 8;
   const bool colok = col0 < a.K;
+  const uint16_t *base = a.X + (colok ? col0 : 0);
 
-  // every (row phase, chunk) load of the block is in flight at once
   u32x4 v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int row = ph + kDetRows * j;
-    v[j] = (u32x4){0u, 0u, 0u, 0u};
-    if (colok && row < a.M) v[j] = *(const u32x4 *)(a.X + (int64_t)row * a.ldx + col0);
+    const bool ok = colok && row < a.M;
+    const u32x4 x = *(const u32x4 *)(base + (ok ? (int64_t)row * a.ldx : 0));
+    v[j] = ok ? x : zero4();
   }
   float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = (e & 1) ? fp16_hi(v[j][e >> 1]) : fp16_lo(v[j][e >> 1]);
-      if (!((ob >> e) & 1u)) mx = __builtin_fmaxf(mx, __builtin_fabsf(x));
+      mx = ((ob >> e) & 1u) ? mx : __builtin_fmaxf(mx, __builtin_fabsf(x));
     }
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -88,14 +97,98 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   }
 }
 
-// Block (tile, kb). Wave w owns 16 output columns; lane (c16 = l % 16,
-// g = l / 16) loads, for MFMA step j, the 16 bytes at k = 64 j + 16 g of its
-// Wq row, and reads the matching Xq bytes from LDS. MB 16-row blocks cover M.
+// Four int8 codes of the fp16 pairs (w0, w1) for the scale inv, packed in
+// byte order. The fp32 product x * inv is rounded first; adding 1.5 * 2^23 then
+// rounds it to the nearest integer, ties to even (the sum's unit in the last
+// place is 1), and leaves that integer in two's complement in the low bits of
+// the sum. The product never exceeds 127 in magnitude by more than a few ulps
+// (|x| <= absmax of its row), so no clamp is needed.
+__device__ inline uint32_t codes4(uint32_t w0, uint32_t w1, float inv) {
+#pragma clang fp contract(off)
+  const float kMagic = 12582912.0f;
+  const uint32_t q0 = __builtin_bit_cast(uint32_t, fp16_lo(w0) * inv + kMagic);
+  const uint32_t q1 = __builtin_bit_cast(uint32_t, fp16_hi(w0) * inv + kMagic);
+  const uint32_t q2 = __builtin_bit_cast(uint32_t, fp16_lo(w1) * inv + kMagic);
+  const uint32_t q3 = __builtin_bit_cast(uint32_t, fp16_hi(w1) * inv + kMagic);
+  return (q0 & 0xffu) | ((q1 & 0xffu) << 8) | ((q2 & 0xffu) << 16) | (q3 << 24);
+}
+
+// 0xff in byte e of the result when bit e of the low four bits of n is clear.
+__device__ inline uint32_t keep_bytes(uint32_t n4) {
+  return ~(((n4 * 0x00204081u) & 0x01010101u) * 0xffu);
+}
+
+// One GEMM stage: a 512-byte K range of X (all rows of the block) and of the
+// wave's 16 Wq rows. Loads past the end of the range read clamped addresses
+// and are neutralised afterwards: their X codes are masked to zero (so the
+// Wq bytes they meet do not matter), rows past M have a zero scale.
 template <int MB>
+struct DecodeStage {
+  u32x4 x[4 * MB];       // X chunk: row wv + 4 u, columns k0 + 8 lane .. + 8
+  u32x4 b[kSubK / 64];   // Wq bytes k0 + 64 j + 16 g .. + 16 of column ncol
+  uint32_t mw;           // outlier mask word of column k0 + 8 lane
+  bool kok;              // column k0 + 8 lane lies inside the K range
+};
+
+template <int MB>
+__device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
+                                   int64_t k_end, const int8_t *brow, int wv, int lane, int g) {
+  const int64_t kx = k0 + 8 * lane;
+  st.kok = kx < k_end;
+  const int64_t kxc = st.kok ? kx : 0;
+  st.mw = a.omask[kxc >> 5];
+#pragma unroll
+  for (int u = 0; u < 4 * MB; ++u) {
+    const int row = wv + 4 * u;
+    st.x[u] = *(const u32x4 *)(a.X + (int64_t)(row < a.M ? row : 0) * a.ldx + kxc);
+  }
+#pragma unroll
+  for (int j = 0; j < kSubK / 64; ++j) {
+    const int64_t k = k0 + 64 * j + 16 * g;
+    st.b[j] = *(const u32x4 *)(brow + (k < k_end ? k : 0));
+  }
+}
+
+// Quantize the stage's X chunks into LDS, then contract them with the Wq bytes.
+template <int MB>
+__device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const float *sinv,
+                                   i32x4 *acc, int wv, int lane, int c16, int g) {
+  __syncthreads();  // sinv ready; the previous stage's MFMAs are done with sx
+  const uint32_t ob = st.kok ? (st.mw >> (8 * (lane & 3))) & 0xffu : 0xffu;
+  const uint32_t keep_lo = keep_bytes(ob & 0xfu), keep_hi = keep_bytes(ob >> 4);
+#pragma unroll
+  for (int u = 0; u < 4 * MB; ++u) {
+    const int row = wv + 4 * u;
+    const float inv = sinv[row];
+    u32x2 out;
+    out[0] = codes4(st.x[u][0], st.x[u][1], inv) & keep_lo;
+    out[1] = codes4(st.x[u][2], st.x[u][3], inv) & keep_hi;
+    *(u32x2 *)(sx + row * kXPitch + 8 * lane) = out;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSubK / 64; ++j)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const i32x4 av = *(const i32x4 *)(sx + (mb * 16 + c16) * kXPitch + 64 * j + 16 * g);
+      acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4, st.b[j]),
+                                                       acc[mb], 0, 0, 0);
+    }
+}
+
+// Block (tile, kb). Wave w owns 16 output columns; lane (c16 = l % 16,
+// g = l / 16) supplies, for MFMA step j, the 16 Wq bytes at k = 64 j + 16 g of
+// its column and reads the matching Xq bytes from LDS. MB 16-row blocks cover M.
+// NST is the number of 512-byte stages of the block's K range when it is 1 or
+// 2 (straight-line code, all loads issued before the first wait), 0 for any
+// count. Two register stages alternate so that the next stage's loads are in
+// flight while the current one is quantized and contracted; no load is issued
+// under a branch that the following waits would have to merge.
+template <int MB, int NST>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sx[MB * 16 * kXPitch];
-  __shared__ float sinv[MB * 16];
-  __shared__ int s_cnt[4];
+  __shared__ float spart[4][64];
+  __shared__ float sinv[64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * kTileN;
@@ -106,159 +199,192 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   const int64_t ncol = n0 + wv * 16 + c16;
   const int8_t *brow = a.wq + ((ncol < a.N) ? ncol : a.N - 1) * K;
 
-  // row absmax over all kept columns = max of the detection blocks' partials
-  if (t < a.M) {
-    float mx = 0.f;
-    int s = 0;
-    for (; s + 4 <= a.det_blocks; s += 4) {
-      const float p0 = a.pmax[(int64_t)s * a.M + t], p1 = a.pmax[(int64_t)(s + 1) * a.M + t];
-      const float p2 = a.pmax[(int64_t)(s + 2) * a.M + t], p3 = a.pmax[(int64_t)(s + 3) * a.M + t];
-      mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(p0, p1), __builtin_fmaxf(p2, p3)));
-    }
-    for (; s < a.det_blocks; ++s) mx = __builtin_fmaxf(mx, a.pmax[(int64_t)s * a.M + t]);
-    sinv[t] = (mx > 0.f) ? inv_scale(mx) : 0.f;
-    if (kb == 0 && blockIdx.x == 0) a.m[t] = mx;
+  // detection partials of row `lane`, blocks wv + 4 i (first kPmaxUnroll up front)
+  const int prow = lane < a.M ? lane : 0;
+  float pv[kPmaxUnroll];
+#pragma unroll
+  for (int i = 0; i < kPmaxUnroll; ++i) {
+    const int s = wv + 4 * i;
+    const float p = a.pmax[(int64_t)(s < a.det_blocks ? s : 0) * a.M + prow];
+    pv[i] = s < a.det_blocks ? p : 0.f;
   }
-  if (kb == 0 && blockIdx.x == 0 && a.count_out) {
-    int cnt = 0;
-    for (int64_t w = t; w < a.kw; w += 256) cnt += __builtin_popcount(a.omask[w]);
-    cnt = wave_sum(cnt);
-    if (lane == 0) s_cnt[wv] = cnt;
-    __syncthreads();
-    if (t == 0) *a.count_out = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+
+  DecodeStage<MB> s0, s1;
+  decode_load<MB>(a, s0, k_begin, k_end, brow, wv, lane, g);
+  if constexpr (NST == 2) decode_load<MB>(a, s1, k_begin + kSubK, k_end, brow, wv, lane, g);
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first wait
+
+  float pm = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPmaxUnroll; ++i) pm = __builtin_fmaxf(pm, pv[i]);
+  for (int s = wv + 4 * kPmaxUnroll; s < a.det_blocks; s += 4)
+    pm = __builtin_fmaxf(pm, a.pmax[(int64_t)s * a.M + prow]);
+  spart[wv][lane] = pm;
+  __syncthreads();
+  if (t < 64) {
+    const float mx = __builtin_fmaxf(__builtin_fmaxf(spart[0][t], spart[1][t]),
+                                     __builtin_fmaxf(spart[2][t], spart[3][t]));
+    sinv[t] = (t < a.M && mx > 0.f) ? inv_scale(mx) : 0.f;
+    if (kb == 0 && blockIdx.x == 0 && t < a.M) a.m[t] = mx;
   }
 
   i32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (i32x4){0, 0, 0, 0};
 
-  constexpr int XCH = MB * 16 * (kSubK / 8) / 256;  // fp16 chunks of X per thread
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += kSubK) {
-    u32x4 b[kSubK / 64];
-#pragma unroll
-    for (int j = 0; j < kSubK / 64; ++j) {
-      const int64_t k = k0 + 64 * j + 16 * g;
-      b[j] = (k < k_end) ? *(const u32x4 *)(brow + k) : (u32x4){0u, 0u, 0u, 0u};
+  if constexpr (NST == 1) {
+    decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+  } else if constexpr (NST == 2) {
+    decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+    decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
+  } else {
+    const int nst = (int)((k_end - k_begin + kSubK - 1) / kSubK);
+    int64_t k0 = k_begin;
+    int i = 0;
+    for (; i + 2 < nst; i += 2, k0 += 2 * kSubK) {  // stages i + 1 and i + 2 exist
+      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
+      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+      decode_load<MB>(a, s0, k0 + 2 * kSubK, k_end, brow, wv, lane, g);
+      decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
     }
-    u32x4 xv[XCH];
-#pragma unroll
-    for (int u = 0; u < XCH; ++u) {
-      const int q = t + 256 * u;
-      const int row = q / (kSubK / 8);
-      const int64_t k = k0 + 8 * (q % (kSubK / 8));
-      xv[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (row < a.M && k < k_end) xv[u] = *(const u32x4 *)(a.X + (int64_t)row * a.ldx + k);
+    if (nst - i == 2) {
+      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
+      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
+    } else {
+      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
     }
-    __syncthreads();  // sinv ready; previous iteration done with sx
-#pragma unroll
-    for (int u = 0; u < XCH; ++u) {
-      const int q = t + 256 * u;
-      const int row = q / (kSubK / 8), cc = q % (kSubK / 8);
-      const int64_t k = k0 + 8 * cc;
-      u32x2 out = {0u, 0u};
-      if (row < a.M && k < k_end) {
-        const unsigned ob = (a.omask[k >> 5] >> (k & 31)) & 0xffu;
-        const float inv = sinv[row];
-        if (inv != 0.f) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = (e & 1) ? fp16_hi(xv[u][e >> 1]) : fp16_lo(xv[u][e >> 1]);
-            const int qv = ((ob >> e) & 1u) ? 0 : quant_i8(x, inv);
-            out[e >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (e & 3));
-          }
-        }
-      }
-      *(u32x2 *)(sx + row * kXPitch + 8 * cc) = out;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSubK / 64; ++j)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const i32x4 av = *(const i32x4 *)(sx + (mb * 16 + c16) * kXPitch + 64 * j + 16 * g);
-        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4, b[j]),
-                                                         acc[mb], 0, 0, 0);
-      }
   }
 
   // partial sums: lane holds rows 4g + r of each 16-row block, column ncol
+  if (ncol < a.N) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = mb * 16 + 4 * g + r;
-      if (row < a.M && ncol < a.N) a.part[((int64_t)kb * a.M + row) * a.N + ncol] = acc[mb][r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int row = mb * 16 + 4 * g + r;
+        if (row < a.M) a.part[((int64_t)kb * a.M + row) * a.N + ncol] = acc[mb][r];
+      }
+  }
 }
 
-// Block (tile, row group of 16): 64 columns x 16 rows, 4 outputs per thread.
+// Block (tile, row group of 16): 64 columns x 16 rows, 4 outputs per thread
+// (rows wv + 4 i, column lane). KB is the number of K splits.
+template <int KB>
 __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
-  __shared__ int slist[2048];                        // outlier columns of one round
-  __shared__ uint16_t sxo[16 * kOutBatch];           // [row][p]
-  __shared__ uint16_t swo[kOutBatch * kTileN];       // [p][col]
-  __shared__ int s_total;
+  __shared__ int slist[kListWords * 32];             // outlier columns of one window
+  __shared__ int swsum[4];
+  __shared__ float sxo[16][kOutBatch];               // [row][p]
+  __shared__ __attribute__((aligned(16))) uint16_t swo[kOutBatch * kTileN];  // [p][col]
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * kTileN;
   const int64_t col = n0 + lane;
+  const bool colok = col < a.N;
+  const int64_t colc = colok ? col : 0;
   const int rbase = blockIdx.y * 16;
 
-  float y[4];
+  // every independent load first: partial sums, scales, the first mask window
+  int pp[4][KB];
+  float mrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = rbase + wv + 4 * i;
-    y[i] = 0.f;
-    if (row < a.M && col < a.N) {
-      int cacc = 0;
-      for (int k = 0; k < a.kb; ++k) cacc += a.part[((int64_t)k * a.M + row) * a.N + col];
-      if (a.cdbg) a.cdbg[(int64_t)row * a.N + col] = cacc;
-      y[i] = (float)cacc * (a.m[row] * (a.s[col] * (1.0f / 16129.0f)));
-    }
+    const int rowc = row < a.M ? row : 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) pp[i][k] = a.part[((int64_t)k * a.M + rowc) * a.N + colc];
+    mrow[i] = a.m[rowc];
+  }
+  const float scol = a.s[colc];
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
+  uint32_t mw = a.w ? __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0) : 0u;
+
+  float y[4];
+  const float sd = scol * (1.0f / 16129.0f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int cacc = 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) cacc += pp[i][k];
+    const int row = rbase + wv + 4 * i;
+    if (a.cdbg && row < a.M && colok) a.cdbg[(int64_t)row * a.N + col] = cacc;
+    y[i] = (float)cacc * (mrow[i] * sd);
   }
 
-  // fp16 outlier terms, outlier columns in ascending order, kOutBatch at a time
+  // fp16 outlier terms, outlier columns in ascending order
+  int total_all = 0;
   if (a.w) {
-    for (int64_t w0 = 0; w0 < a.kw; w0 += 64) {
-      if (wv == 0) {  // wave 0 lists the outlier columns of 64 mask words
-        const uint32_t mw = (w0 + lane < a.kw) ? a.omask[w0 + lane] : 0u;
-        const int cnt = __builtin_popcount(mw);
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int yv = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += yv;
-        }
-        int pos = incl - cnt;
-        uint32_t mm = mw;
-        while (mm) {
-          slist[pos++] = (int)(32 * (w0 + lane) + __builtin_ctz(mm));
-          mm &= mm - 1u;
-        }
-        if (lane == 63) s_total = incl;
+    for (int64_t w0 = 0; w0 < a.kw; w0 += kListWords) {
+      if (w0 > 0) {
+        __syncthreads();  // the previous window's list is consumed
+        mw = __builtin_amdgcn_raw_buffer_load_b32(mrs, (int)(4 * (w0 + t)), 0, 0);
       }
+      // block-wide exclusive scan of the per-word outlier counts
+      const int cnt = __builtin_popcount(mw);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int yv = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += yv;
+      }
+      if (lane == 63) swsum[wv] = incl;
       __syncthreads();
-      const int total = s_total;
+      int before = 0, total = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        before += (i < wv) ? swsum[i] : 0;
+        total += swsum[i];
+      }
+      int pos = before + incl - cnt;
+      uint32_t mm = mw;
+      while (mm) {
+        slist[pos++] = (int)(32 * (w0 + t) + __builtin_ctz(mm));
+        mm &= mm - 1u;
+      }
+      total_all += total;
+      __syncthreads();
       for (int p0 = 0; p0 < total; p0 += kOutBatch) {
         const int np = (total - p0 < kOutBatch) ? total - p0 : kOutBatch;
-        {
-          const int row = rbase + (t >> 4), p = t & 15;  // 16 x 16 = 256 entries
-          sxo[t] = (row < a.M && p < np) ? a.X[(int64_t)row * a.ldx + slist[p0 + p]] : 0;
+        // W rows and X entries of the batch. Entries past the batch, past N or
+        // past M read clamped addresses: they only reach outputs never stored
+        // or terms never summed.
+        {  // W rows: 32 rows x 8 chunks of 8 columns, one per thread
+          const int p = t >> 3, ch = t & 7;
+          const int64_t cc = n0 + 8 * ch;
+          const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+          *(u32x4 *)(swo + p * kTileN + 8 * ch) =
+              *(const u32x4 *)(a.w + kk * a.ldw + (cc < a.N ? cc : a.N - 8));
         }
-        for (int q = t; q < kOutBatch * kTileN; q += 256) {
-          const int p = q / kTileN;
-          const int64_t cc = n0 + (q % kTileN);
-          swo[q] = (p < np && cc < a.N) ? a.w[(int64_t)slist[p0 + p] * a.ldw + cc] : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // X entries: 16 rows x 32 outliers
+          const int q = t + 256 * h;
+          const int r = q >> 5, p = q & 31;
+          const int row = rbase + r;
+          const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+          sxo[r][p] = h2f(a.X[(int64_t)(row < a.M ? row : a.M - 1) * a.ldx + kk]);
         }
         __syncthreads();
         for (int p = 0; p < np; ++p) {
           const float wval = h2f(swo[p * kTileN + lane]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] += h2f(sxo[(wv + 4 * i) * kOutBatch + p]) * wval;
+          for (int i = 0; i < 4; ++i) y[i] += sxo[wv + 4 * i][p] * wval;
         }
         __syncthreads();
       }
     }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0 && a.count_out) *a.count_out = total_all;
+  } else if (blockIdx.x == 0 && blockIdx.y == 0 && a.count_out) {
+    // no outlier product: count the mask bits only
+    __shared__ int scount[4];
+    int cnt = 0;
+    for (int64_t w = t; w < a.kw; w += 256) cnt += __builtin_popcount(a.omask[w]);
+    cnt = wave_sum(cnt);
+    if (lane == 0) scount[wv] = cnt;
+    __syncthreads();
+    if (t == 0) *a.count_out = scount[0] + scount[1] + scount[2] + scount[3];
   }
-  if (col < a.N) {
+
+  if (colok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rbase + wv + 4 * i;
@@ -268,8 +394,26 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
 }
 
 template <int MB>
-hipError_t launch_decode_gemm(const DecodeGemmArgs &a, int tiles, int kb, hipStream_t stream) {
-  hipLaunchKernelGGL((k_decode_gemm<MB>), dim3(tiles, kb), dim3(256), 0, stream, a);
+hipError_t launch_decode_gemm(const DecodeGemmArgs &a, int tiles, int kb, const GemmEvents &ev,
+                              hipStream_t stream) {
+  const int64_t nst = (a.kc + kSubK - 1) / kSubK;
+  const hipEvent_t b = (hipEvent_t)ev.begin, e = (hipEvent_t)ev.end;
+  if (nst == 1)
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 1>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
+                          a);
+  else if (nst == 2)
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 2>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
+                          a);
+  else
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 0>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
+                          a);
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t launch_decode_epilogue(const DecodeGemmArgs &a, int tiles, hipStream_t stream) {
+  hipLaunchKernelGGL((k_decode_epilogue<KB>), dim3(tiles, (unsigned)((a.M + 15) / 16)), dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 
@@ -280,15 +424,16 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
   DecodePlan p;
   p.tiles = (int)((N + kTileN - 1) / kTileN);
   p.det_blocks = (int)((K + kDetCols - 1) / kDetCols);
-  int64_t kb = (512 + p.tiles - 1) / p.tiles;  // aim for ~512 GEMM blocks
-  const int64_t kmax = (K + 255) / 256;         // at least 256 k bytes per block
-  if (kb > kmax) kb = kmax;
-  if (kb > 16) kb = 16;
-  if (kb < 1) kb = 1;
+  // K splits: a power of two, about kTargetBlocks blocks in all, and at least
+  // one full stage of K per split
+  int kb = 1;
+  while (kb < kMaxSplits && (int64_t)p.tiles * (kb * 2) <= kTargetBlocks &&
+         K / (kb * 2) >= kSubK)
+    kb *= 2;
   int64_t kc = (K + kb - 1) / kb;
   kc = (kc + 63) / 64 * 64;
   p.kc = kc;
-  p.kb = (int)((K + kc - 1) / kc);
+  p.kb = kb;  // a trailing split may be empty; its partial sums are zero
   return p;
 }
 
@@ -297,19 +442,21 @@ hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm
   hipLaunchKernelGGL(k_decode_detect, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev.begin && (e = hipEventRecord((hipEvent_t)ev.begin, stream)) != hipSuccess) return e;
   const int mb = (int)((gemm.M + 15) / 16);
   switch (mb) {
-    case 1: e = launch_decode_gemm<1>(gemm, plan.tiles, plan.kb, stream); break;
-    case 2: e = launch_decode_gemm<2>(gemm, plan.tiles, plan.kb, stream); break;
-    case 3: e = launch_decode_gemm<3>(gemm, plan.tiles, plan.kb, stream); break;
-    default: e = launch_decode_gemm<4>(gemm, plan.tiles, plan.kb, stream); break;
+    case 1: e = launch_decode_gemm<1>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    case 2: e = launch_decode_gemm<2>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    case 3: e = launch_decode_gemm<3>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    default: e = launch_decode_gemm<4>(gemm, plan.tiles, plan.kb, ev, stream); break;
   }
   if (e != hipSuccess) return e;
-  if (ev.end && (e = hipEventRecord((hipEvent_t)ev.end, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_epilogue, dim3(plan.tiles, (unsigned)((gemm.M + 15) / 16)),
-                     dim3(256), 0, stream, gemm);
-  return hipGetLastError();
+  switch (plan.kb) {
+    case 1: return launch_decode_epilogue<1>(gemm, plan.tiles, stream);
+    case 2: return launch_decode_epilogue<2>(gemm, plan.tiles, stream);
+    case 4: return launch_decode_epilogue<4>(gemm, plan.tiles, stream);
+    case 8: return launch_decode_epilogue<8>(gemm, plan.tiles, stream);
+    default: return launch_decode_epilogue<16>(gemm, plan.tiles, stream);
+  }
 }
 
 }  // namespace llmint8

@@ -78,13 +78,14 @@ hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const in
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_wide(const GemmArgs &a, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 256, true>(a, stream)
-                : gemm_detail::launch_prefill<256, 256, false>(a, stream);
+hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  return a.cdbg ? gemm_detail::launch_prefill<256, 256, true>(a, ev, stream)
+                : gemm_detail::launch_prefill<256, 256, false>(a, ev, stream);
 }
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  return narrow_tiles(a.M, a.N) ? launch_gemm_narrow(a, stream) : launch_gemm_wide(a, stream);
+hipError_t launch_gemm(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  return narrow_tiles(a.M, a.N) ? launch_gemm_narrow(a, ev, stream)
+                                : launch_gemm_wide(a, ev, stream);
 }
 
 }  // namespace llmint8

@@ -300,14 +300,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
 }
 
 template <int BM, int BN, bool DBG>
-hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_prefill(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
   using T = TileCfg<BM, BN>;
   hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, DBG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm_prefill<BM, BN, DBG>), dim3((unsigned)tiles), dim3(256), T::LDS,
-                     stream, a);
+  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, DBG>), dim3((unsigned)tiles), dim3(256), T::LDS,
+                        stream, (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();
 }
 

@@ -3,9 +3,9 @@
 
 namespace llmint8 {
 
-hipError_t launch_gemm_narrow(const GemmArgs &a, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 128, true>(a, stream)
-                : gemm_detail::launch_prefill<256, 128, false>(a, stream);
+hipError_t launch_gemm_narrow(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  return a.cdbg ? gemm_detail::launch_prefill<256, 128, true>(a, ev, stream)
+                : gemm_detail::launch_prefill<256, 128, false>(a, ev, stream);
 }
 
 }  // namespace llmint8

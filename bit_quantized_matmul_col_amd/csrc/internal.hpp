@@ -75,17 +75,18 @@ struct GemmArgs {
   int64_t M, N, K, ldq, ldo, ldw, ldy;
 };
 
-// Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
-// tile shape (256x256 or 256x128) from the problem size.
-hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
-hipError_t launch_gemm_wide(const GemmArgs &args, hipStream_t stream);
-hipError_t launch_gemm_narrow(const GemmArgs &args, hipStream_t stream);
-
-// Caller-supplied events recorded around the GEMM kernel (may be null).
+// Caller-supplied events (may be null) that the GEMM kernel's own dispatch
+// stamps when the kernel starts and when it ends.
 struct GemmEvents {
   void *begin;
   void *end;
 };
+
+// Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
+// tile shape (256x256 or 256x128) from the problem size.
+hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
+hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
+hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 
 // Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
 // its slice of X itself.

@@ -127,8 +127,9 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
  * sizeof(llmint8_linear_opts), then fill the fields you use; NULL fields are
  * off. The struct is read during the call only.
  *   gemm_begin_event, gemm_end_event  optional hipEvent_t handles (created by
- *       the caller) recorded on `stream` immediately before and after the GEMM
- *       kernel, so a caller can time the dominant kernel of the layer with
+ *       the caller) that the GEMM kernel's own dispatch on `stream` stamps when
+ *       the kernel starts and when it completes (no separate stream commands),
+ *       so a caller can time the dominant kernel of the layer with
  *       hipEventElapsedTime.
  */
 typedef struct llmint8_linear_opts {

@@ -122,6 +122,25 @@ def test_small_shapes(dev, M, K, N, seed, threshold):
     run_all(torch, lm, X, W, threshold)
 
 
+# Small-M shapes chosen for the small-M path's structure: stage counts per K
+# split of 1, 2, 3, 4 and 5 (the generic stage loop), 1, 2, 4, 8 and 16 K splits,
+# more than 32 detection blocks and a second 8192-column window of the outlier
+# list (K > 8192), 64 rows, and N not a multiple of 64.
+DECODE = [(3, 5632, 4096), (2, 9216, 4096), (9, 8192, 128), (4, 4096, 8192), (64, 2048, 2048),
+          (32, 1088, 72), (1, 12288, 1032)]
+
+
+@pytest.mark.parametrize("M,K,N", DECODE)
+def test_small_m_structure(dev, M, K, N):
+    torch, lm = dev
+    say(f"case small-M M={M} K={K} N={N}")
+    X, W, planted = workloads.random_case(M, K, N, seed=K + N, n_out=3)
+    # outliers in the first and the last 32-column mask word, and past 8192
+    for k in (0, K - 1) + ((8200, K - 40) if K > 8192 else ()):
+        X[M // 2, k] = np.float16(-25.0 if k % 2 else 25.0)
+    run_all(torch, lm, X, W, 6.0)
+
+
 def test_edge_values(dev):
     torch, lm = dev
     say("case edge values")
