@@ -9,6 +9,12 @@ reported on its own. Inputs are resident in HBM when the timed region starts.
 To keep the 256 MB Infinity Cache from serving the weights, consecutive steps
 cycle through distinct copies of the weight set (and of the activation).
 
+The timed region replays a HIP graph that holds one call per weight set and
+activation of that rotation, so the step rate is the GPU's, not that of the
+Python launch loop (the eager rate is reported beside it). The GEMM kernel's
+duration comes from event pairs that the kernel's own dispatch stamps, one pair
+per call, over a run of eager calls.
+
 Prints one JSON line. `value` is the whole-step rate in the workload's unit:
 GB/s of algorithmic bytes for the HBM-bound decode and tiny shapes, TOPS of
 algorithmic work (int8 ops + fp16 flops) for the prefill shapes.
@@ -31,9 +37,12 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 FP16_PEAK_TFLOPS = 2500.0
 HBM_BOUND = ("tiny", "decode")
+DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
 PROFILES = os.path.join(ROOT, "profiles")
+# the sources that define the GEMM kernels (small-M and large-M)
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc", f)
-                  for f in ("gemm.hip", "common.hpp", "internal.hpp")]
+                  for f in ("common.hpp", "internal.hpp", "decode.hip", "gemm_core.hpp",
+                            "gemm.hip", "gemm_narrow.hip")]
 
 
 def kernel_source_digest() -> str:
@@ -64,13 +73,26 @@ def read_traffic(workload: str):
         return None
 
 
+def uses_compaction(M, K, n_out):
+    """The library's rule for running the int8 GEMM on the K - |O| kept columns."""
+    return (M > DECODE_MAX_M and n_out > 0 and K <= 32768
+            and M * n_out * 16 > 5000 * (2 * K - n_out))
+
+
 def step_work(M, K, N, n_out, compacted):
-    """Algorithmic bytes and work of one layer call, and of its GEMM kernel."""
+    """Algorithmic bytes and work of one layer call, and the algorithmic bytes of
+    its GEMM kernel. The small-M GEMM kernel quantizes fp16 X itself and writes
+    int32 sums, so its minimum traffic is Wq + X + C; the large-M kernel reads
+    Xq, Wq (or their compacted copies), the scales and the outlier operands and
+    writes Y."""
     k_int8 = K - n_out
     call_bytes = 2 * M * K + K * N + 4 * N + 2 * n_out * N + 2 * M * N
-    k_loop = k_int8 if compacted else K
-    gemm_bytes = (N * k_loop + 4 * N + M * k_loop + 4 * M + 2 * M * n_out + 2 * n_out * N
-                  + 4 * n_out + 2 * M * N)
+    if M <= DECODE_MAX_M:
+        gemm_bytes = N * K + 2 * M * K + 4 * M * N
+    else:
+        k_loop = k_int8 if compacted else K
+        gemm_bytes = (N * k_loop + 4 * N + M * k_loop + 4 * M + 2 * M * n_out
+                      + 2 * n_out * N + 2 * M * N)
     int8_ops = 2 * M * N * k_int8
     fp16_flops = 2 * M * N * n_out
     return call_bytes, gemm_bytes, int8_ops, fp16_flops
@@ -124,9 +146,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
-              "(multi-GPU sharding is a design note, not a measured path). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures the layer on one GPU; a run on several GPUs is not "
+              "provided (how the layer would shard is described, not measured). "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -171,34 +193,69 @@ def main():
                      device=dev)
     cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
 
-    # GEMM timing events, recorded by the library around its GEMM launch
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for e in ev_b + ev_e:
-        e.record()  # creates the underlying hipEvent
-    torch.cuda.synchronize()
-    opts = [lm.LinearOpts(gemm_begin_event=ev_b[i].cuda_event, gemm_end_event=ev_e[i].cuda_event)
-            for i in range(steps)]
-
-    def step(i, timed):
+    def step(i, opts=None):
         Wq, s, W = sets[i % n_sets]
         lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
-                          outlier_count=cnt, opts=opts[i] if timed else None)
+                          outlier_count=cnt, opts=opts)
 
     for i in range(warmup):
-        step(i, False)
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: replays of a HIP graph holding graph_len consecutive layer
+    # calls (every weight set and activation of the rotation), so the rate is the
+    # GPU's and not the Python launch loop's.
+    graph_len = n_sets * x_pool // math.gcd(n_sets, x_pool)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(graph_len):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(graph_len):
+            step(i)
+    replays = max(1, math.ceil(steps / graph_len))
+    steps = replays * graph_len
+    for _ in range(2):
+        graph.replay()
     torch.cuda.synchronize()
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
-    for i in range(steps):
-        step(i, True)
+    for _ in range(replays):
+        graph.replay()
     t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_stop)
     ms_per_step = total_ms / steps
-    gemm_ms = sum(ev_b[i].elapsed_time(ev_e[i]) for i in range(steps)) / steps
+
+    # The same calls launched one by one from Python (no graph), for reference.
+    eager_steps = min(steps, 1000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(eager_steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / eager_steps
+
+    # GEMM kernel duration: events stamped by the GEMM kernel's own dispatch on
+    # the library's stream, one pair per call, over eager calls.
+    kt_steps = min(steps, 500)
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(kt_steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(kt_steps)]
+    for e in ev_b + ev_e:
+        e.record()  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    for i in range(kt_steps):
+        step(i, lm.LinearOpts(gemm_begin_event=ev_b[i].cuda_event,
+                              gemm_end_event=ev_e[i].cuda_event))
+    torch.cuda.synchronize()
+    gemm_ms = sum(ev_b[i].elapsed_time(ev_e[i]) for i in range(kt_steps)) / kt_steps
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -210,7 +267,7 @@ def main():
         torch.cuda.synchronize()
 
     n_out = int(cnt.item())
-    compacted = n_out > 0 and wl.K <= 32768 and n_out * 100 >= wl.K * 5
+    compacted = uses_compaction(wl.M, wl.K, n_out)
     call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted)
     if hbm_bound:
         value, unit = call_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
@@ -236,6 +293,10 @@ def main():
                    "activation_pool": x_pool, "parallelism": "single GPU"},
         "roofline": roof,
         "gemm_kernel_ms": round(gemm_ms, 6),
+        "timing": {"timed_region": f"{replays} replays of a HIP graph of {graph_len} layer calls",
+                   "eager_ms_per_step": round(eager_ms, 6),
+                   "gemm_kernel_timing": f"dispatch-stamped events around the GEMM kernel "
+                                         f"of {kt_steps} eager calls"},
         "whole_step": {"algorithmic_bytes": call_bytes, "int8_ops": int8_ops,
                        "fp16_flops": fp16_flops,
                        "GB_per_s": round(call_bytes / (ms_per_step * 1e-3) / 1e9, 2),
