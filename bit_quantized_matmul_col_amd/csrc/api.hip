@@ -95,6 +95,29 @@ int check_k(int64_t K) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LLMINT8_OK : LLMINT8_ERR_HIP; }
 
+// Value of a non-negative binary16 pattern (0 .. 0x7c00 = +inf), exactly.
+float half_value(uint32_t p) {
+  if (p >= 0x7c00u) return INFINITY;
+  if (p < 0x400u) return std::ldexp((float)p, -24);
+  return std::ldexp((float)(1024u + (p & 0x3ffu)), (int)(p >> 10) - 25);
+}
+
+// Smallest binary16 magnitude pattern whose value is >= threshold, so that for
+// every fp16 x, |x| >= threshold exactly when (bits(x) & 0x7fff) >= the result
+// (non-negative fp16 values are ordered like their patterns).
+uint32_t fp16_threshold_bits(float threshold) {
+  if (!(threshold > 0.f)) return 0u;
+  uint32_t lo = 0u, hi = 0x7c00u;  // half_value(hi) >= threshold always holds
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (half_value(mid) >= threshold)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
 }  // namespace
 
 LLMINT8_EXPORT const char *llmint8_status_string(int status) {
@@ -188,6 +211,11 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   const GemmEvents ev{opts ? opts->gemm_begin_event : nullptr,
                       opts ? opts->gemm_end_event : nullptr};
 
+  if (fused_decode_fits(M, K, ldx)) {
+    const FusedArgs f{X, Wq, col_absmax, W, Y, C_debug, outlier_count_out, ldx, ldw, ldy,
+                      (int)M, (int)K, (int)N, (int)((N + 15) / 16), fp16_threshold_bits(threshold)};
+    return hip_status(launch_decode_fused(f, ev, s));
+  }
   if (M <= kDecodeMaxM) {
     const DecodePlan dp = decode_plan(M, K, N);
     const int64_t kw = (K + 31) / 32;

@@ -1,0 +1,480 @@
+// Single-kernel small-M path of the LLM.int8() linear layer on gfx950.
+//
+// For decode-shaped calls with up to 16 rows and K in {1024, 2048, 4096} the
+// whole layer runs in one kernel. The layer is bound by streaming the int8
+// weight Wq from HBM (the decode regime of the INT8-vs-FP8 page, section one),
+// and on gfx950 every extra dependent kernel costs about 3 us. Cross-block
+// handoffs through agent-scope fences cost more than a kernel boundary, so this
+// kernel needs none: every block recomputes what it needs from X.
+//
+// Block b (512 threads, persistent over the 16-column tiles b, b + G, ...):
+//  1. loads all of X into registers, then issues the Wq loads of its first tile
+//     (they stream while 2-5 run);
+//  2. X in registers: thread (c, h) holds the 16-byte chunk c
+//     (columns 8c .. 8c+7) of rows h, h + R, ... (R = 512 / (K / 8));
+//  3. column absmax over all rows with packed 16-bit max on the magnitude bits
+//     (for non-negative fp16 the bit patterns order like the values), compared
+//     with the smallest fp16 pattern >= threshold: the outlier bits ("LLM.int8()"
+//     walkthrough, sections 2.3 and 4.2);
+//  4. row absmax over the kept columns the same way, reduced across the block;
+//     fl32(127 / m) per row (pitfalls page, section 1);
+//  5. int8 codes of every row into LDS (outlier columns zero), once per block;
+//  6. per tile: 16x16x64 int8 MFMAs with the wave's eighth of K, a fixed-order
+//     sum of the eight wave partials in LDS (exact int32 C), dequantize by
+//     m_i * s_j / 127^2, add the fp16 outlier terms X_O . W_O in fp32 (pitfalls
+//     page, section 3.3) and store Y.
+#include "internal.hpp"
+
+namespace llmint8 {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileCols = 16;
+constexpr int kBatch = 64;     // outlier columns staged per round of the fp16 product
+
+// Four int8 codes of the fp16 pairs (w0, w1) for the scale inv, packed in byte
+// order. v_fma_mix_f32 multiplies the fp16 half by inv with one fp32 rounding
+// (adding +0 changes nothing but the sign of a zero product, which the next
+// step ignores). Adding 1.5 * 2^23 then rounds that product to the nearest
+// integer, ties to even, and leaves it in two's complement in the low bits.
+// |x| <= absmax of its row keeps the product within 127 * (1 + 2^-22), so no
+// clamp is needed.
+__device__ inline float mul_lo(uint32_t w, float inv) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(inv));
+  return r;
+}
+__device__ inline float mul_hi(uint32_t w, float inv) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(inv));
+  return r;
+}
+__device__ inline uint32_t codes4(uint32_t w0, uint32_t w1, float inv) {
+#pragma clang fp contract(off)
+  const float kMagic = 12582912.0f;
+  const uint32_t q0 = __builtin_bit_cast(uint32_t, mul_lo(w0, inv) + kMagic);
+  const uint32_t q1 = __builtin_bit_cast(uint32_t, mul_hi(w0, inv) + kMagic);
+  const uint32_t q2 = __builtin_bit_cast(uint32_t, mul_lo(w1, inv) + kMagic);
+  const uint32_t q3 = __builtin_bit_cast(uint32_t, mul_hi(w1, inv) + kMagic);
+  return (q0 & 0xffu) | ((q1 & 0xffu) << 8) | ((q2 & 0xffu) << 16) | (q3 << 24);
+}
+
+// 0xff in byte e of the result when bit e of the low four bits of n is clear.
+__device__ inline uint32_t keep_bytes(uint32_t n4) {
+  return ~(((n4 * 0x00204081u) & 0x01010101u) * 0xffu);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pmax16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Layout of the dynamic LDS (byte offsets); P = K + 16 is the Xq row pitch
+// (16 rows that one MFMA operand reads fall in distinct bank groups).
+struct FusedLds {
+  int xq, red, list, inv, m, bits, rmax, xo0, misc, total;
+};
+
+__host__ __device__ constexpr FusedLds fused_lds(int K, int MB) {
+  FusedLds L{};
+  const int P = K + 16;
+  int o = 0;
+  L.xq = o;
+  o += MB * 16 * P;
+  o = (o + 15) & ~15;
+  L.red = o;  // wave partials [8][MB * 256] int32; also column-max scratch and
+  o += kWaves * MB * 256 * 4;  // the fp16 staging of the outlier product
+  L.list = o;  // ascending outlier columns, uint16
+  o += K * 2;
+  o = (o + 15) & ~15;
+  L.inv = o;
+  o += 64 * 4;
+  L.m = o;
+  o += 64 * 4;
+  L.bits = o;  // outlier bits of each 8-column chunk
+  o += K / 8;
+  o = (o + 15) & ~15;
+  L.rmax = o;  // per-wave row maxima [8][32]
+  o += kWaves * 32 * 4;
+  L.xo0 = o;  // X entries of the first outlier batch [16][64] fp32
+  o += 16 * MB * kBatch * 4;
+  L.misc = o;
+  o += 64;
+  L.total = o;
+  return L;
+}
+
+// Reduce v[0..MR) over the 64 lanes of a wave so that, afterwards, lane l holds
+// in v[0] the maximum for row index j(l) = sum of (l bit (5 - s)) * MR / 2^(s+1)
+// over the log2(MR) halving steps s (the same value in all lanes sharing those
+// bits). Each step halves the values a lane carries and swaps the other half
+// with the lane across.
+template <int MR>
+__device__ inline uint32_t wave_rows_max(uint32_t *v, int lane) {
+  int off = 32;
+#pragma unroll
+  for (int n = MR; n > 1; n >>= 1, off >>= 1) {
+    // bitwise selects: a conditional on the two elements would be turned into
+    // a run-time index into v, i.e. a compare-and-select over every element
+    const uint32_t upm = (lane & off) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const uint32_t send = (v[i] & upm) | (v[i + n / 2] & ~upm);
+      const uint32_t keep = (v[i + n / 2] & upm) | (v[i] & ~upm);
+      const uint32_t recv = (uint32_t)__shfl_xor((int)send, off, 64);
+      v[i] = keep > recv ? keep : recv;
+    }
+  }
+  uint32_t r = v[0];
+  for (; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
+    r = r > o ? r : o;
+  }
+  return r;
+}
+
+template <int K, int MB>
+__global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
+  constexpr int C = K / 8;               // 16-byte chunks per X row
+  constexpr int R = kThreads / C;        // threads sharing a chunk
+  constexpr int MR = MB * 16 / R;        // rows per thread
+  constexpr int P = K + 16;
+  constexpr int KW = K / kWaves;         // k bytes per wave in the MFMA phase
+  constexpr int KS = KW / 64;            // MFMA steps per wave
+  static_assert(C * R == kThreads && MR * R == MB * 16 && KS * 64 * kWaves == K, "shape");
+  static_assert(MR >= 1 && (MR & (MR - 1)) == 0 && MR <= 32, "rows per thread");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr FusedLds L = fused_lds(K, MB);
+  uint8_t *sxq = lds + L.xq;
+  int32_t *sred = (int32_t *)(lds + L.red);
+  uint16_t *slist = (uint16_t *)(lds + L.list);
+  float *sinv = (float *)(lds + L.inv);
+  float *sm = (float *)(lds + L.m);
+  uint8_t *sbits = lds + L.bits;
+  uint32_t *srmax = (uint32_t *)(lds + L.rmax);
+  int *stotal = (int *)(lds + L.misc);
+
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int G = gridDim.x;
+
+  // Per-tile registers: the wave's Wq bytes (wave wv owns k bytes [wv * KW,
+  // (wv + 1) * KW)), the column scale of the thread's output and, for threads
+  // t < 128, 16 bytes of the W rows of the first batch of outlier columns.
+  static_assert(MB == 1, "one output per thread");
+  struct TileRegs {
+    u32x4 b[KS];
+    float sc;
+    u32x4 wo;
+  };
+  auto load_b = [&](TileRegs &tr, int tile) {
+    const int n = tile * kTileCols + c16;
+    const int8_t *row = a.wq + (int64_t)(n < a.N ? n : a.N - 1) * K + wv * KW + 16 * g;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) tr.b[j] = *(const u32x4 *)(row + 64 * j);
+    const int no = tile * kTileCols + (t & 15);
+    tr.sc = a.s[no < a.N ? no : a.N - 1];
+  };
+  // W rows of outlier columns p0 .. p0 + 63 for the tile: thread t < 128 loads
+  // row p0 + t / 2, columns 8 (t % 2) .. + 8 of the tile
+  auto load_wo = [&](int tile, int p0, int np) {
+    const int p = t >> 1, half = t & 1;
+    const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+    const int nc = tile * kTileCols + 8 * half;
+    return *(const u32x4 *)(a.w + kk * a.ldw + (nc < a.N ? nc : a.N - 8));
+  };
+  // 2. X: chunk c of rows h + R j (rows past M read as zero: harmless for every
+  //    max, and their codes are replaced by zeros). X is issued before Wq: loads
+  //    complete in issue order, and steps 3-5 wait only for X.
+  const int c = t % C, h = t / C;
+  u32x4 xv[MR];
+  {
+    // one buffer resource over rows 0 .. M-1: rows past M read as zero and
+    // cost no memory traffic
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.X, (short)0, (int)(((int64_t)a.M - 1) * a.ldx * 2 + 2 * K), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+      const int r = h + R * j;
+      xv[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(r * a.ldx * 2 + 16 * c), 0, 0));
+    }
+  }
+  TileRegs tr0, tr1;
+  load_b(tr0, blockIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. column magnitudes, as 16-bit patterns, two per 32-bit word
+  uint32_t cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < MR; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cm[e] = pmax16(cm[e], xv[j][e] & 0x7fff7fffu);
+  if constexpr (R > 1) {
+    u32x4 *scm = (u32x4 *)sred;  // [R][C]
+    scm[h * C + c] = (u32x4){cm[0], cm[1], cm[2], cm[3]};
+    __syncthreads();
+    if (h == 0) {
+#pragma unroll
+      for (int q = 1; q < R; ++q) {
+        const u32x4 o = scm[q * C + c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cm[e] = pmax16(cm[e], o[e]);
+      }
+    }
+  }
+  if (h == 0) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bits |= ((cm[e] & 0xffffu) >= a.tcut ? 1u : 0u) << (2 * e);
+      bits |= ((cm[e] >> 16) >= a.tcut ? 1u : 0u) << (2 * e + 1);
+    }
+    sbits[c] = (uint8_t)bits;
+  }
+  __syncthreads();
+
+  // 4. row magnitudes over the kept columns
+  const uint32_t ob = sbits[c];
+  uint32_t keep16[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    keep16[e] = (((ob >> (2 * e)) & 1u) ? 0u : 0x7fffu) |
+                (((ob >> (2 * e + 1)) & 1u) ? 0u : 0x7fff0000u);
+  {
+    uint32_t rm[MR];
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+      uint32_t v = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v = pmax16(v, xv[j][e] & keep16[e]);
+      rm[j] = (v & 0xffffu) > (v >> 16) ? (v & 0xffffu) : (v >> 16);
+    }
+    const uint32_t r = wave_rows_max<MR>(rm, lane);
+    // lane l's result is row index j(l); lanes with the low bits clear publish it
+    int j = 0, off = 32;
+#pragma unroll
+    for (int n = MR; n > 1; n >>= 1, off >>= 1)
+      if (lane & off) j += n / 2;
+    if ((lane & (off * 2 - 1)) == 0) srmax[wv * 32 + j] = r;
+  }
+  __syncthreads();
+  if (t < MB * 16) {
+    // row t is index j = t / R of the waves whose threads have h = t % R
+    const int hr = t % R, jr = t / R;
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if ((w * 64) / C == hr) mb = mb > srmax[w * 32 + jr] ? mb : srmax[w * 32 + jr];
+    const float m = h2f((uint16_t)mb);
+    const bool live = t < a.M && m > 0.f;
+    sinv[t] = live ? inv_scale(m) : 0.f;
+    sm[t] = t < a.M ? m : 0.f;
+  }
+  // outlier list (ascending) from the chunk bits: wave 0, C / 64 chunks per lane
+  if (wv == 0) {
+    constexpr int CPL = C / 64;
+    uint32_t cb[CPL];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      cb[q] = sbits[lane * CPL + q];
+      cnt += __builtin_popcount(cb[q]);
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int pos = incl - cnt;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      uint32_t bb = cb[q];
+      while (bb) {
+        slist[pos++] = (uint16_t)(8 * (lane * CPL + q) + __builtin_ctz(bb));
+        bb &= bb - 1u;
+      }
+    }
+    if (lane == 63) {
+      *stotal = incl;
+      if (blockIdx.x == 0 && a.count_out) *a.count_out = incl;
+    }
+  }
+  __syncthreads();
+
+  // first batch of the fp16 outlier product: its X entries (tile independent)
+  // and the W rows of the first tile, in flight while the codes are computed
+  const int total = *stotal;
+  const bool outl = total > 0 && a.w;
+  const int np0 = total < kBatch ? total : kBatch;
+  float xo0[2] = {0.f, 0.f};
+  if (outl) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // 16 rows x 64 columns, two per thread
+      const int q = t + kThreads * u, r = q / kBatch, p = q % kBatch;
+      const int64_t kk = slist[p < np0 ? p : np0 - 1];
+      xo0[u] = h2f(a.X[(int64_t)(r < a.M ? r : a.M - 1) * a.ldx + kk]);
+    }
+    if (t < 2 * kBatch) tr0.wo = load_wo(blockIdx.x, 0, np0);
+  }
+
+  // 5. int8 codes into LDS; rows M .. MB * 16 - 1 are zero
+  {
+    const uint32_t kl = keep_bytes(ob & 0xfu), kh = keep_bytes(ob >> 4);
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+      const int r = h + R * j;
+      const float inv = sinv[r];
+      u32x2 out;
+      out[0] = codes4(xv[j][0], xv[j][1], inv) & kl;
+      out[1] = codes4(xv[j][2], xv[j][3], inv) & kh;
+      if (r >= a.M) out = (u32x2){0u, 0u};
+      *(u32x2 *)(sxq + r * P + 8 * c) = out;
+    }
+  }
+  float *sxo0 = (float *)(lds + L.xo0);
+  if (outl) {
+    sxo0[t] = xo0[0];
+    sxo0[t + kThreads] = xo0[1];
+  }
+  __syncthreads();
+
+  // 6. tiles
+  auto run_tile = [&](const TileRegs &tr, int tile) {
+    const u32x4 *b = tr.b;
+    i32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = (i32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const i32x4 av =
+            *(const i32x4 *)(sxq + (mb * 16 + c16) * P + wv * KW + 64 * j + 16 * g);
+        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4, b[j]),
+                                                         acc[mb], 0, 0, 0);
+      }
+    // lane holds rows mb * 16 + 4 g + r, column c16
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sred[wv * MB * 256 + (mb * 16 + 4 * g + r) * 16 + c16] = acc[mb][r];
+    __syncthreads();
+    // outputs: index q = t + 512 u (u < OPT) is row q / 16, column q % 16 of the tile
+    constexpr int OPT = (MB * 256 + kThreads - 1) / kThreads;
+    float y[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int q = t + kThreads * u;
+      const int orow = q >> 4, n = tile * kTileCols + (q & 15);
+      y[u] = 0.f;
+      if (q < MB * 256) {
+        int cacc = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) cacc += sred[w * MB * 256 + q];
+        const float sc = tr.sc;
+        if (a.cdbg && orow < a.M && n < a.N) a.cdbg[(int64_t)orow * a.N + n] = cacc;
+        y[u] = (float)cacc * (sm[orow] * (sc * (1.0f / 16129.0f)));
+      }
+    }
+    __syncthreads();  // the partials are consumed; the staging below reuses them
+    if (outl) {
+      float *sxo = (float *)sred;                                   // [16][kBatch]
+      uint16_t *swo = (uint16_t *)(sxo + MB * 16 * kBatch);         // [kBatch][16]
+      for (int p0 = 0; p0 < total; p0 += kBatch) {
+        const int np = (total - p0 < kBatch) ? total - p0 : kBatch;
+        // the first batch was loaded ahead; later ones are loaded here
+        const float *xs = p0 == 0 ? sxo0 : sxo;
+        if (t < 2 * kBatch)
+          *(u32x4 *)(swo + (t >> 1) * 16 + 8 * (t & 1)) = p0 == 0 ? tr.wo : load_wo(tile, p0, np);
+        if (p0 > 0) {
+          for (int q = t; q < MB * 16 * kBatch; q += kThreads) {  // X entries
+            const int r = q / kBatch, p = q % kBatch;
+            const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+            sxo[q] = h2f(a.X[(int64_t)(r < a.M ? r : a.M - 1) * a.ldx + kk]);
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+          const int q = t + kThreads * u;
+          if (q < MB * 256)
+            for (int p = 0; p < np; ++p)
+              y[u] += xs[(q >> 4) * kBatch + p] * h2f(swo[p * 16 + (q & 15)]);
+        }
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int q = t + kThreads * u;
+      const int orow = q >> 4, n = tile * kTileCols + (q & 15);
+      if (q < MB * 256 && orow < a.M && n < a.N) a.y[(int64_t)orow * a.ldy + n] = f2h(y[u]);
+    }
+  };
+
+  for (int tile = blockIdx.x;;) {
+    const int t1 = tile + G;
+    if (t1 < a.tiles) {
+      load_b(tr1, t1);
+      if (outl && t < 2 * kBatch) tr1.wo = load_wo(t1, 0, np0);
+    }
+    run_tile(tr0, tile);
+    if (t1 >= a.tiles) break;
+    const int t2 = t1 + G;
+    if (t2 < a.tiles) {
+      load_b(tr0, t2);
+      if (outl && t < 2 * kBatch) tr0.wo = load_wo(t2, 0, np0);
+    }
+    run_tile(tr1, t1);
+    if (t2 >= a.tiles) break;
+    tile = t2;
+  }
+}
+
+template <int K, int MB>
+hipError_t launch_fused_kmb(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  constexpr FusedLds L = fused_lds(K, MB);
+  hipError_t e = hipFuncSetAttribute((const void *)k_decode_fused<K, MB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int grid = a.tiles < cus ? a.tiles : cus;
+  hipExtLaunchKernelGGL((k_decode_fused<K, MB>), dim3(grid), dim3(kThreads), L.total, stream,
+                        (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
+  return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_fused_k(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  return launch_fused_kmb<K, 1>(a, ev, stream);
+}
+
+}  // namespace
+
+// Up to 16 rows the single kernel beats the three-kernel path (it replicates X
+// into every block, which stops paying beyond one 16-row MFMA block).
+bool fused_decode_fits(int64_t M, int64_t K, int64_t ldx) {
+  if (M < 1 || M > 16) return false;
+  if (M * ldx * 2 >= ((int64_t)1 << 31)) return false;  // 32-bit buffer offsets
+  return K == 4096 || K == 2048 || K == 1024;
+}
+
+hipError_t launch_decode_fused(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  switch (a.K) {
+    case 4096: return launch_fused_k<4096>(a, ev, stream);
+    case 2048: return launch_fused_k<2048>(a, ev, stream);
+    case 1024: return launch_fused_k<1024>(a, ev, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace llmint8

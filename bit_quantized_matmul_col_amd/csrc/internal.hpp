@@ -127,4 +127,22 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N);
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream);
 
+// Single-kernel small-M path (no workspace): for the shapes fused_decode_fits
+// accepts, one kernel detects, quantizes, multiplies and writes Y.
+struct FusedArgs {
+  const uint16_t *X;
+  const int8_t *wq;
+  const float *s;
+  const uint16_t *w;   // null only when no column can be an outlier
+  uint16_t *y;
+  int32_t *cdbg;       // optional [M x N] int32
+  int32_t *count_out;  // optional [1]
+  int64_t ldx, ldw, ldy;
+  int M, K, N;
+  int tiles;           // 16-column output tiles
+  uint32_t tcut;       // smallest fp16 magnitude pattern whose value reaches the threshold
+};
+bool fused_decode_fits(int64_t M, int64_t K, int64_t ldx);
+hipError_t launch_decode_fused(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream);
+
 }  // namespace llmint8

@@ -141,6 +141,47 @@ def test_small_m_structure(dev, M, K, N):
     run_all(torch, lm, X, W, 6.0)
 
 
+# Shapes of the single-kernel small-M path (K in {1024, 2048, 4096}): one and
+# several 16-column tiles per block (N = 11008 gives 688 tiles), partial last
+# tiles, 1 to 64 rows.
+FUSED = [(1, 4096, 8), (5, 4096, 4104), (16, 2048, 24), (17, 2048, 11008), (32, 4096, 11008),
+         (33, 1024, 520), (64, 1024, 4096), (32, 1024, 16)]
+
+
+@pytest.mark.parametrize("M,K,N", FUSED)
+@pytest.mark.parametrize("threshold", [6.0, math.inf, 2.5, 0.0])
+def test_single_kernel_small_m(dev, M, K, N, threshold):
+    torch, lm = dev
+    say(f"case single-kernel small-M M={M} K={K} N={N} threshold={threshold}")
+    X, W, _ = workloads.random_case(M, K, N, seed=3 * K + N + M, n_out=4)
+    run_all(torch, lm, X, W, threshold)
+
+
+def test_single_kernel_threshold_edges(dev):
+    # thresholds that are and are not binary16 values, against entries at,
+    # just below and just above them
+    torch, lm = dev
+    say("case single-kernel threshold edges")
+    X, W, _ = workloads.random_case(4, 1024, 64, seed=77, n_out=0, x_sigma=0.5)
+    below = np.nextafter(np.float16(6.0), np.float16(0))      # 5.99609375
+    above = np.nextafter(np.float16(6.0), np.float16(10))     # 6.00390625
+    X[0, 5], X[1, 9], X[2, 13], X[3, 1023] = np.float16(6.0), below, above, -np.float16(6.0)
+    for threshold in (6.0, 6.001, float(below), float(above), 5.999):
+        run_all(torch, lm, X, W, threshold, check_colwise=False)
+
+
+def test_single_kernel_without_fp16_weight(dev):
+    torch, lm = dev
+    say("case single-kernel threshold inf, W omitted")
+    X, W, _ = workloads.random_case(8, 1024, 64, 19, n_out=2)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    y_with = lm.llmint8_linear(Xd, Wq, s, Wd, math.inf)
+    y_without = lm.llmint8_linear(Xd, Wq, s, None, math.inf)
+    assert torch.equal(y_with, y_without)
+    assert_y_close(y_without.cpu().numpy(), oracle.linear(X, W, math.inf)["Y"], "Y")
+
+
 def test_edge_values(dev):
     torch, lm = dev
     say("case edge values")
