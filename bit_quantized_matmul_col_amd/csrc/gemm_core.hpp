@@ -11,14 +11,15 @@
 // Design (one 256-thread block per BM x BN output tile, 4 waves of
 // BM/2 x BN/2, 32x32 MFMA blocks):
 //  * Operands stream through LDS in stages of 128 bytes of k per row (128 int8
-//    or 64 fp16), two stages deep, filled by buffer_load_dwordx4 ... lds: lane
+//    or 64 fp16), in a ring of three stages (256x128 tiles) or two (256x256,
+//    whose three would not fit in LDS), filled by buffer_load_dwordx4 ... lds: lane
 //    l of a wave instruction lands at base + 16 l, so each instruction moves
 //    8 rows x 128 B with no register staging. Each operand tile is one buffer
 //    resource starting at the tile's first row; a lane keeps one 32-bit offset
 //    per 8-row group and the stage's k offset is scalar. Rows past the matrix
 //    end lie past the resource's record count and read as zero, so there is no
-//    bounds arithmetic in the loop. The k-loop issues stage t + 1 before the
-//    MFMAs of stage t.
+//    bounds arithmetic in the loop. The loads of a later stage are spread over
+//    the k-steps of the current stage's MFMAs.
 //  * The 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), so the
 //    16 rows that lanes 0..15 read for one MFMA operand fall in 16 different
 //    bank groups.
@@ -58,7 +59,20 @@ __device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order, so the older ones have landed).
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the k-loop. __syncthreads() carries a workgroup fence,
+// and the compiler makes that fence wait for every outstanding direct-to-LDS
+// load (vmcnt(0)), which would drain the whole ring at each step. In the
+// k-loop the only LDS writes are those loads, and each wave has already waited
+// for the stage it needs (wait_vm), so the bare barrier is enough; the LDS
+// reads of the previous stage have been consumed by its MFMAs.
+__device__ inline void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Byte offset of logical 16-byte chunk c of row r inside a stage.
 __device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ ((r >> 1) & 7)); }
@@ -88,12 +102,16 @@ struct OperandTile {
   }
 
   __device__ void load(uint8_t *stage, int kbyte) const {
+#pragma unroll
+    for (int j = 0; j < G; ++j) load_group(stage, kbyte, j);
+  }
+
+  // The j-th of the wave's G 8-row groups of one stage.
+  __device__ void load_group(uint8_t *stage, int kbyte, int j) const {
     const int wv = threadIdx.x >> 6;
     const rsrc_t rs = make_rsrc(base, bytes);
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + 4 * j) * 8 * SK), 16,
-                                                voff[j], kbyte, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + 4 * j) * 8 * SK), 16,
+                                              voff[j], kbyte, 0, 0);
   }
 };
 
@@ -102,7 +120,9 @@ struct TileCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int STAGE = (BM + BN) * SK;
-  static constexpr int LDS = 2 * STAGE + (BM + BN) * 4;
+  // stages in the LDS ring: three when they fit in the 160 KB of a CU
+  static constexpr int NST = 3 * STAGE + (BM + BN) * 4 <= 160 * 1024 ? 3 : 2;
+  static constexpr int LDS = NST * STAGE + (BM + BN) * 4;
 };
 
 // Tile coordinates of this block after the XCD-aware renumbering.
@@ -128,9 +148,9 @@ __device__ inline V lds_frag(const uint8_t *p) {
   return *(const V *)p;
 }
 
-template <int BM, int BN, int MI, int NI, typename V, typename MFMA>
+template <int BM, int BN, int MI, int NI, typename V, typename MFMA, typename HOOK>
 __device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, int lg,
-                                  i32x16 *acc, MFMA mfma) {
+                                  i32x16 *acc, MFMA mfma, HOOK after_kstep) {
   constexpr int WM = BM / 2, WN = BN / 2;
   V av[2][MI], bv[2][NI];
 #pragma unroll
@@ -155,6 +175,7 @@ __device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, in
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = mfma(av[b][mi], bv[b][ni], acc[mi * NI + ni]);
+    after_kstep(ks);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -172,33 +193,61 @@ struct MfmaF16 {
   }
 };
 
-// Two-stage pipelined k-loop over nstages 128-byte stages of A and B: the next
-// stage's loads are in flight while the MFMAs consume the current one. fp16
-// selects the outlier-product MFMAs (uniform across the block).
-template <int BM, int BN, int MI, int NI>
+// Pipelined k-loop over nstages 128-byte stages of A and B through a ring of
+// NST LDS buffers. At step it the block waits for stage it only (the NST - 2
+// younger stages stay in flight), synchronizes (which also frees the buffer of
+// stage it - 1), issues stage it + NST - 1 into that buffer and runs the MFMAs
+// of stage it. fp16 selects the outlier-product MFMAs (uniform across the
+// block).
+template <int BM, int BN, int MI, int NI, int NST>
 __device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const OperandTile<BN> &B,
                              int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
                              i32x16 *acc) {
   constexpr int STAGE = (BM + BN) * SK;
+  constexpr int LPS = OperandTile<BM>::G + OperandTile<BN>::G;  // loads per lane per stage
+  static_assert(NST == 2 || NST == 3, "ring depth");
   if (nstages <= 0) return;
-  A.load(smem, 0);
-  B.load(smem + BM * SK, 0);
-  wait_vm();
-  __syncthreads();
-  for (int64_t it = 0; it < nstages; ++it) {
-    const uint8_t *cur = smem + (it & 1) * STAGE;
-    if (it + 1 < nstages) {
-      uint8_t *nxt = smem + ((it + 1) & 1) * STAGE;
-      A.load(nxt, (int)((it + 1) * SK));
-      B.load(nxt + BM * SK, (int)((it + 1) * SK));
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nstages) {
+      A.load(smem + st * STAGE, st * SK);
+      B.load(smem + st * STAGE + BM * SK, st * SK);
     }
-    if (fp16)
-      stage_mfma<BM, BN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16());
+  for (int64_t it = 0; it < nstages; ++it) {
+    if (NST == 3 && it + 1 < nstages)
+      wait_vm<LPS>();
     else
-      stage_mfma<BM, BN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8());
-    wait_vm();
-    __syncthreads();
+      wait_vm<0>();
+    ring_barrier();
+    // The loads of stage it + NST - 1. With three buffers they are spread over
+    // the four k-steps of this stage's MFMAs (they have a whole further stage
+    // to land), so that no wave stalls on a burst of address work; with two
+    // they must all be in flight from the start of the stage.
+    const int64_t nx = it + NST - 1;
+    const bool more = nx < nstages;
+    uint8_t *buf = smem + (nx % NST) * STAGE;
+    const int kb = (int)(nx * SK);
+    constexpr int GA = OperandTile<BM>::G, GB = OperandTile<BN>::G;
+    if (NST == 2 && more) {
+      A.load(buf, kb);
+      B.load(buf + BM * SK, kb);
+    }
+    auto issue = [&](int ks) {
+      if (NST == 2 || !more) return;
+#pragma unroll
+      for (int j = 0; j < GA; ++j)
+        if (j * 4 / GA == ks) A.load_group(buf, kb, j);
+#pragma unroll
+      for (int j = 0; j < GB; ++j)
+        if (j * 4 / GB == ks) B.load_group(buf + BM * SK, kb, j);
+    };
+    const uint8_t *cur = smem + (it % NST) * STAGE;
+    if (fp16)
+      stage_mfma<BM, BN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
+    else
+      stage_mfma<BM, BN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
   }
+  __syncthreads();  // every wave is done with the ring before it is reused
 }
 
 template <int BM, int BN, bool DBG>
@@ -207,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
   extern __shared__ u32x4 smem_v[];
   uint8_t *smem = (uint8_t *)smem_v;
-  float *sm = (float *)(smem + 2 * T::STAGE);
+  float *sm = (float *)(smem + T::NST * T::STAGE);
   float *ss = sm + BM;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -238,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
       B.init(a.wqc, a.ldq, n0, a.N);
     else
       B.init(a.wq, a.K, n0, a.N);
-    kloop<BM, BN, MI, NI>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg, acc);
+    kloop<BM, BN, MI, NI, T::NST>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg, acc);
   }
 
   // dequantize in place: C * m[i] * s[n] / 127^2
@@ -276,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
     OperandTile<BN> B;
     A.init(a.xo, a.ldo * 2, m0, a.M);
     B.init(a.wot, a.ldo * 2, n0, a.N);
-    kloop<BM, BN, MI, NI>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg, acc);
+    kloop<BM, BN, MI, NI, T::NST>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg, acc);
   }
 
   // store Y (fp16, round to nearest even); rows past M fall outside the resource
