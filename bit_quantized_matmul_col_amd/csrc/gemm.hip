@@ -5,6 +5,9 @@ namespace llmint8 {
 
 namespace {
 
+// waves along N of a 256x256 tile (4: two waves per SIMD)
+constexpr int kWideWavesN = 4;
+
 // W_O^T [N x ldo] (fp16): row n holds W[idx[p], n] for p < |O|, zeros up to the
 // next multiple of 64. One block per 64 columns of W, 64 outlier rows per step,
 // transposed through LDS.
@@ -58,15 +61,17 @@ double wave_fill(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t cus) {
   return (double)tiles / (double)(waves * cus);
 }
 
-// 256x256 tiles unless their last wave leaves much of the chip idle and
-// 256x128 tiles fill the waves better; a 256x128 tile does half the MFMA work
-// per k stage for the same per-stage overhead, so it is taken as 10% slower.
+// 256x256 tiles (8 waves) unless their last wave leaves most of the chip idle
+// and 256x128 tiles fill the waves much better. A 256x128 tile moves 1.5x the
+// operand bytes per MFMA and runs 4 waves; measured on the 7B, 13B and 70B
+// shapes it is 3-10% slower even where its waves are 90% full against 67%,
+// so it is taken as 30% slower.
 bool narrow_tiles(int64_t M, int64_t N) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  return 0.9 * wave_fill(M, N, 256, 128, cus) > wave_fill(M, N, 256, 256, cus);
+  return 0.7 * wave_fill(M, N, 256, 128, cus) > wave_fill(M, N, 256, 256, cus);
 }
 
 }  // namespace
@@ -79,8 +84,8 @@ hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const in
 }
 
 hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 256, true>(a, ev, stream)
-                : gemm_detail::launch_prefill<256, 256, false>(a, ev, stream);
+  return a.cdbg ? gemm_detail::launch_prefill<256, 256, kWideWavesN, true>(a, ev, stream)
+                : gemm_detail::launch_prefill<256, 256, kWideWavesN, false>(a, ev, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {

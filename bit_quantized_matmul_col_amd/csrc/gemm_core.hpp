@@ -8,8 +8,9 @@
 // the dequantized int8 result ("LLM.int8() pitfalls" page, section 3.3;
 // "LLM.int8()" walkthrough, section 2.3), accumulated in fp32.
 //
-// Design (one 256-thread block per BM x BN output tile, 4 waves of
-// BM/2 x BN/2, 32x32 MFMA blocks):
+// Design (one block per BM x BN output tile, 2 x NWN waves of BM/2 x BN/NWN,
+// 32x32 MFMA blocks; 256x256 tiles run 8 waves, two per SIMD, so that one
+// wave's MFMAs cover the other's waits):
 //  * Operands stream through LDS in stages of 128 bytes of k per row (128 int8
 //    or 64 fp16), in a ring of three stages (256x128 tiles) or two (256x256,
 //    whose three would not fit in LDS), filled by buffer_load_dwordx4 ... lds: lane
@@ -77,12 +78,12 @@ __device__ inline void ring_barrier() { asm volatile("s_barrier" ::: "memory"); 
 // Byte offset of logical 16-byte chunk c of row r inside a stage.
 __device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ ((r >> 1) & 7)); }
 
-// One operand tile: ROWS rows from row0 of a row-major matrix. Wave w loads the
-// 8-row groups w, w + 4, ...; lane l of a group fetches the logical chunk that
-// belongs at physical slot l % 8 of row l / 8.
-template <int ROWS>
+// One operand tile: ROWS rows from row0 of a row-major matrix, loaded by NW
+// waves. Wave w loads the 8-row groups w, w + NW, ...; lane l of a group
+// fetches the logical chunk that belongs at physical slot l % 8 of row l / 8.
+template <int ROWS, int NW>
 struct OperandTile {
-  static constexpr int G = ROWS / 32;  // 8-row groups per wave
+  static constexpr int G = ROWS / (8 * NW);  // 8-row groups per wave
   const uint8_t *base;  // first row of the tile
   int bytes;            // bytes from base to the end of the matrix rows in the tile
   int voff[G];
@@ -95,7 +96,7 @@ struct OperandTile {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int r = (wv + 4 * j) * 8 + (lane >> 3);
+      const int r = (wv + NW * j) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       voff[j] = r * (int)ld_bytes + 16 * c;
     }
@@ -110,14 +111,17 @@ struct OperandTile {
   __device__ void load_group(uint8_t *stage, int kbyte, int j) const {
     const int wv = threadIdx.x >> 6;
     const rsrc_t rs = make_rsrc(base, bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + 4 * j) * 8 * SK), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + NW * j) * 8 * SK), 16,
                                               voff[j], kbyte, 0, 0);
   }
 };
 
-template <int BM, int BN>
+// BM x BN block tile computed by 2 x NWN waves of WM x WN (NWN = 2: one wave
+// per SIMD; NWN = 4: two).
+template <int BM, int BN, int NWN>
 struct TileCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int NW = 2 * NWN, THREADS = 64 * NW;
+  static constexpr int WM = BM / 2, WN = BN / NWN;
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int STAGE = (BM + BN) * SK;
   // stages in the LDS ring: three when they fit in the 160 KB of a CU
@@ -148,10 +152,9 @@ __device__ inline V lds_frag(const uint8_t *p) {
   return *(const V *)p;
 }
 
-template <int BM, int BN, int MI, int NI, typename V, typename MFMA, typename HOOK>
+template <int BM, int WM, int WN, int MI, int NI, typename V, typename MFMA, typename HOOK>
 __device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, int lg,
                                   i32x16 *acc, MFMA mfma, HOOK after_kstep) {
-  constexpr int WM = BM / 2, WN = BN / 2;
   V av[2][MI], bv[2][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) av[0][mi] = lds_frag<V>(cur + swz(wm * WM + mi * 32 + li, lg));
@@ -199,12 +202,13 @@ struct MfmaF16 {
 // stage it - 1), issues stage it + NST - 1 into that buffer and runs the MFMAs
 // of stage it. fp16 selects the outlier-product MFMAs (uniform across the
 // block).
-template <int BM, int BN, int MI, int NI, int NST>
-__device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const OperandTile<BN> &B,
+template <int BM, int BN, int WM, int WN, int MI, int NI, int NST, int NW>
+__device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW> &A,
+                             const OperandTile<BN, NW> &B,
                              int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
                              i32x16 *acc) {
   constexpr int STAGE = (BM + BN) * SK;
-  constexpr int LPS = OperandTile<BM>::G + OperandTile<BN>::G;  // loads per lane per stage
+  constexpr int LPS = OperandTile<BM, NW>::G + OperandTile<BN, NW>::G;  // loads per lane per stage
   static_assert(NST == 2 || NST == 3, "ring depth");
   if (nstages <= 0) return;
 #pragma unroll
@@ -227,7 +231,7 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const Oper
     const bool more = nx < nstages;
     uint8_t *buf = smem + (nx % NST) * STAGE;
     const int kb = (int)(nx * SK);
-    constexpr int GA = OperandTile<BM>::G, GB = OperandTile<BN>::G;
+    constexpr int GA = OperandTile<BM, NW>::G, GB = OperandTile<BN, NW>::G;
     if (NST == 2 && more) {
       A.load(buf, kb);
       B.load(buf + BM * SK, kb);
@@ -243,16 +247,17 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM> &A, const Oper
     };
     const uint8_t *cur = smem + (it % NST) * STAGE;
     if (fp16)
-      stage_mfma<BM, BN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
+      stage_mfma<BM, WM, WN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
     else
-      stage_mfma<BM, BN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
+      stage_mfma<BM, WM, WN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 }
 
-template <int BM, int BN, bool DBG>
-__global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
-  using T = TileCfg<BM, BN>;
+template <int BM, int BN, int NWN, bool DBG>
+__global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
+  using T = TileCfg<BM, BN, NWN>;
+  constexpr int NW = T::NW, TH = T::THREADS;
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
   extern __shared__ u32x4 smem_v[];
   uint8_t *smem = (uint8_t *)smem_v;
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
   float *ss = sm + BM;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / NWN, wn = wv % NWN;
   const int li = lane & 31, lg = lane >> 5;
   int64_t tm, tn;
   tile_of_block((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
@@ -270,8 +275,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
   const bool compact = use_compaction(count, a.K, a.M);
   const int64_t Kl = compact ? a.K - count : a.K;
 
-  for (int i = t; i < BM; i += 256) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
-  for (int i = t; i < BN; i += 256) ss[i] = (n0 + i < a.N) ? a.s[n0 + i] * (1.0f / 16129.0f) : 0.f;
+  for (int i = t; i < BM; i += TH) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
+  for (int i = t; i < BN; i += TH) ss[i] = (n0 + i < a.N) ? a.s[n0 + i] * (1.0f / 16129.0f) : 0.f;
 
   i32x16 acc[MI * NI];
 #pragma unroll
@@ -280,14 +285,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
     for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = (i32x16){};
 
   {
-    OperandTile<BM> A;
-    OperandTile<BN> B;
+    OperandTile<BM, NW> A;
+    OperandTile<BN, NW> B;
     A.init(a.xq, a.ldq, m0, a.M);
     if (compact)
       B.init(a.wqc, a.ldq, n0, a.N);
     else
       B.init(a.wq, a.K, n0, a.N);
-    kloop<BM, BN, MI, NI, T::NST>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg, acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg,
+                                              acc);
   }
 
   // dequantize in place: C * m[i] * s[n] / 127^2
@@ -321,11 +327,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
 
   // fp16 outlier product X_O . W_O over the gathered outlier columns
   if (count > 0 && a.w) {
-    OperandTile<BM> A;
-    OperandTile<BN> B;
+    OperandTile<BM, NW> A;
+    OperandTile<BN, NW> B;
     A.init(a.xo, a.ldo * 2, m0, a.M);
     B.init(a.wot, a.ldo * 2, n0, a.N);
-    kloop<BM, BN, MI, NI, T::NST>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg, acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg,
+                                              acc);
   }
 
   // store Y (fp16, round to nearest even); rows past M fall outside the resource
@@ -348,15 +355,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_prefill(GemmArgs a) {
     }
 }
 
-template <int BM, int BN, bool DBG>
+template <int BM, int BN, int NWN, bool DBG>
 hipError_t launch_prefill(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  using T = TileCfg<BM, BN>;
-  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, DBG>,
+  using T = TileCfg<BM, BN, NWN>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, NWN, DBG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, DBG>), dim3((unsigned)tiles), dim3(256), T::LDS,
-                        stream, (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
+  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, NWN, DBG>), dim3((unsigned)tiles),
+                        dim3(T::THREADS), T::LDS, stream, (hipEvent_t)ev.begin,
+                        (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();
 }
 
