@@ -5,8 +5,10 @@ namespace llmint8 {
 
 namespace {
 
-// waves along N of a 256x256 tile (4: two waves per SIMD)
+// waves along N of a 256x256 tile (4: two waves per SIMD) and k bytes per
+// stage (128; 64-byte stages with a four-deep ring measured 7-9% slower)
 constexpr int kWideWavesN = 4;
+constexpr int kWideStageK = 128;
 
 // W_O^T [N x ldo] (fp16): row n holds W[idx[p], n] for p < |O|, zeros up to the
 // next multiple of 64. One block per 64 columns of W, 64 outlier rows per step,
@@ -84,8 +86,8 @@ hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const in
 }
 
 hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 256, kWideWavesN, true>(a, ev, stream)
-                : gemm_detail::launch_prefill<256, 256, kWideWavesN, false>(a, ev, stream);
+  return a.cdbg ? gemm_detail::launch_prefill<256, 256, kWideWavesN, kWideStageK, true>(a, ev, stream)
+                : gemm_detail::launch_prefill<256, 256, kWideWavesN, kWideStageK, false>(a, ev, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {

@@ -46,8 +46,6 @@
 namespace llmint8 {
 namespace gemm_detail {
 
-
-constexpr int SK = 128;     // bytes of k per stage and row
 constexpr int kXcds = 8;    // XCDs of the MI355X
 constexpr int kGroupM = 8;  // tile rows per ordering group
 
@@ -75,15 +73,29 @@ __device__ inline void wait_vm() {
 // reads of the previous stage have been consumed by its MFMAs.
 __device__ inline void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Byte offset of logical 16-byte chunk c of row r inside a stage.
-__device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ ((r >> 1) & 7)); }
+// Chunk permutation of row r in a stage of SK bytes per row (SK / 16 chunks of
+// 16 bytes). The 16 rows that lanes 0..15 read for one MFMA operand then fall
+// in 16 different 16-byte bank groups of the 256-byte bank row: with 128-byte
+// rows, rows 2q and 2q + 1 sit in opposite halves and q picks the chunk; with
+// 64-byte rows, r % 4 picks the quarter and (r / 4) % 4 the chunk.
+template <int SK>
+__device__ inline int swz_key(int r) {
+  static_assert(SK == 128 || SK == 64, "stage row size");
+  return SK == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
 
-// One operand tile: ROWS rows from row0 of a row-major matrix, loaded by NW
-// waves. Wave w loads the 8-row groups w, w + NW, ...; lane l of a group
-// fetches the logical chunk that belongs at physical slot l % 8 of row l / 8.
-template <int ROWS, int NW>
+// Byte offset of logical 16-byte chunk c of row r inside a stage.
+template <int SK>
+__device__ inline int swz(int r, int c) { return r * SK + 16 * (c ^ swz_key<SK>(r)); }
+
+// One operand tile: ROWS rows from row0 of a row-major matrix, SK bytes of k
+// per stage, loaded by NW waves. One wave instruction moves 1 KB = RPI rows;
+// wave w loads the row groups w, w + NW, ...; lane l of a group fetches the
+// logical chunk that belongs at physical slot l % (SK / 16) of row l / (SK / 16).
+template <int ROWS, int NW, int SK>
 struct OperandTile {
-  static constexpr int G = ROWS / (8 * NW);  // 8-row groups per wave
+  static constexpr int RPI = 1024 / SK;            // rows per wave instruction
+  static constexpr int G = ROWS / (RPI * NW);      // row groups per wave
   const uint8_t *base;  // first row of the tile
   int bytes;            // bytes from base to the end of the matrix rows in the tile
   int voff[G];
@@ -96,8 +108,8 @@ struct OperandTile {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int r = (wv + NW * j) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int r = (wv + NW * j) * RPI + lane / (SK / 16);
+      const int c = (lane % (SK / 16)) ^ swz_key<SK>(r);
       voff[j] = r * (int)ld_bytes + 16 * c;
     }
   }
@@ -107,25 +119,27 @@ struct OperandTile {
     for (int j = 0; j < G; ++j) load_group(stage, kbyte, j);
   }
 
-  // The j-th of the wave's G 8-row groups of one stage.
+  // The j-th of the wave's G row groups of one stage.
   __device__ void load_group(uint8_t *stage, int kbyte, int j) const {
     const int wv = threadIdx.x >> 6;
     const rsrc_t rs = make_rsrc(base, bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + NW * j) * 8 * SK), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(stage + (wv + NW * j) * RPI * SK), 16,
                                               voff[j], kbyte, 0, 0);
   }
 };
 
 // BM x BN block tile computed by 2 x NWN waves of WM x WN (NWN = 2: one wave
-// per SIMD; NWN = 4: two).
-template <int BM, int BN, int NWN>
+// per SIMD; NWN = 4: two), staged SK bytes of k at a time.
+template <int BM, int BN, int NWN, int SK>
 struct TileCfg {
   static constexpr int NW = 2 * NWN, THREADS = 64 * NW;
   static constexpr int WM = BM / 2, WN = BN / NWN;
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int STAGE = (BM + BN) * SK;
-  // stages in the LDS ring: three when they fit in the 160 KB of a CU
-  static constexpr int NST = 3 * STAGE + (BM + BN) * 4 <= 160 * 1024 ? 3 : 2;
+  // stages in the LDS ring: as many as fit in the 160 KB of a CU, up to 4
+  static constexpr int FIT = (160 * 1024 - (BM + BN) * 4) / STAGE;
+  static constexpr int NST = FIT > 4 ? 4 : FIT;
+  static_assert(NST >= 2, "two stages must fit");
   static constexpr int LDS = NST * STAGE + (BM + BN) * 4;
 };
 
@@ -152,26 +166,28 @@ __device__ inline V lds_frag(const uint8_t *p) {
   return *(const V *)p;
 }
 
-template <int BM, int WM, int WN, int MI, int NI, typename V, typename MFMA, typename HOOK>
+template <int BM, int WM, int WN, int MI, int NI, int SK, typename V, typename MFMA,
+          typename HOOK>
 __device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, int lg,
                                   i32x16 *acc, MFMA mfma, HOOK after_kstep) {
+  constexpr int KSTEPS = SK / 32;
   V av[2][MI], bv[2][NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) av[0][mi] = lds_frag<V>(cur + swz(wm * WM + mi * 32 + li, lg));
+  for (int mi = 0; mi < MI; ++mi) av[0][mi] = lds_frag<V>(cur + swz<SK>(wm * WM + mi * 32 + li, lg));
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
-    bv[0][ni] = lds_frag<V>(cur + BM * SK + swz(wn * WN + ni * 32 + li, lg));
+    bv[0][ni] = lds_frag<V>(cur + BM * SK + swz<SK>(wn * WN + ni * 32 + li, lg));
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < KSTEPS; ++ks) {
     const int b = ks & 1;
-    if (ks + 1 < 4) {
+    if (ks + 1 < KSTEPS) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        av[b ^ 1][mi] = lds_frag<V>(cur + swz(wm * WM + mi * 32 + li, 2 * (ks + 1) + lg));
+        av[b ^ 1][mi] = lds_frag<V>(cur + swz<SK>(wm * WM + mi * 32 + li, 2 * (ks + 1) + lg));
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         bv[b ^ 1][ni] =
-            lds_frag<V>(cur + BM * SK + swz(wn * WN + ni * 32 + li, 2 * (ks + 1) + lg));
+            lds_frag<V>(cur + BM * SK + swz<SK>(wn * WN + ni * 32 + li, 2 * (ks + 1) + lg));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -202,14 +218,15 @@ struct MfmaF16 {
 // stage it - 1), issues stage it + NST - 1 into that buffer and runs the MFMAs
 // of stage it. fp16 selects the outlier-product MFMAs (uniform across the
 // block).
-template <int BM, int BN, int WM, int WN, int MI, int NI, int NST, int NW>
-__device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW> &A,
-                             const OperandTile<BN, NW> &B,
+template <int BM, int BN, int WM, int WN, int MI, int NI, int NST, int NW, int SK>
+__device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
+                             const OperandTile<BN, NW, SK> &B,
                              int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
                              i32x16 *acc) {
   constexpr int STAGE = (BM + BN) * SK;
-  constexpr int LPS = OperandTile<BM, NW>::G + OperandTile<BN, NW>::G;  // loads per lane per stage
-  static_assert(NST == 2 || NST == 3, "ring depth");
+  constexpr int LPS = OperandTile<BM, NW, SK>::G + OperandTile<BN, NW, SK>::G;  // per lane per stage
+  constexpr int KSTEPS = SK / 32;
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
   if (nstages <= 0) return;
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
@@ -218,20 +235,24 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW> &A,
       B.load(smem + st * STAGE + BM * SK, st * SK);
     }
   for (int64_t it = 0; it < nstages; ++it) {
-    if (NST == 3 && it + 1 < nstages)
+    // younger stages already issued may stay in flight
+    const int64_t ahead = (nstages - 1 - it < NST - 2) ? nstages - 1 - it : NST - 2;
+    if (NST >= 4 && ahead >= 2)
+      wait_vm<2 * LPS>();
+    else if (NST >= 3 && ahead >= 1)
       wait_vm<LPS>();
     else
       wait_vm<0>();
     ring_barrier();
-    // The loads of stage it + NST - 1. With three buffers they are spread over
-    // the four k-steps of this stage's MFMAs (they have a whole further stage
-    // to land), so that no wave stalls on a burst of address work; with two
-    // they must all be in flight from the start of the stage.
+    // The loads of stage it + NST - 1. With three or more buffers they are
+    // spread over the k-steps of this stage's MFMAs (they have at least one
+    // further stage to land), so that no wave stalls on a burst of address
+    // work; with two they must all be in flight from the start of the stage.
     const int64_t nx = it + NST - 1;
     const bool more = nx < nstages;
     uint8_t *buf = smem + (nx % NST) * STAGE;
     const int kb = (int)(nx * SK);
-    constexpr int GA = OperandTile<BM, NW>::G, GB = OperandTile<BN, NW>::G;
+    constexpr int GA = OperandTile<BM, NW, SK>::G, GB = OperandTile<BN, NW, SK>::G;
     if (NST == 2 && more) {
       A.load(buf, kb);
       B.load(buf + BM * SK, kb);
@@ -240,23 +261,23 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW> &A,
       if (NST == 2 || !more) return;
 #pragma unroll
       for (int j = 0; j < GA; ++j)
-        if (j * 4 / GA == ks) A.load_group(buf, kb, j);
+        if (j * KSTEPS / GA == ks) A.load_group(buf, kb, j);
 #pragma unroll
       for (int j = 0; j < GB; ++j)
-        if (j * 4 / GB == ks) B.load_group(buf + BM * SK, kb, j);
+        if (j * KSTEPS / GB == ks) B.load_group(buf + BM * SK, kb, j);
     };
     const uint8_t *cur = smem + (it % NST) * STAGE;
     if (fp16)
-      stage_mfma<BM, WM, WN, MI, NI, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
+      stage_mfma<BM, WM, WN, MI, NI, SK, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
     else
-      stage_mfma<BM, WM, WN, MI, NI, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
+      stage_mfma<BM, WM, WN, MI, NI, SK, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 }
 
-template <int BM, int BN, int NWN, bool DBG>
+template <int BM, int BN, int NWN, int SK, bool DBG>
 __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
-  using T = TileCfg<BM, BN, NWN>;
+  using T = TileCfg<BM, BN, NWN, SK>;
   constexpr int NW = T::NW, TH = T::THREADS;
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
   extern __shared__ u32x4 smem_v[];
@@ -285,15 +306,15 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
     for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = (i32x16){};
 
   {
-    OperandTile<BM, NW> A;
-    OperandTile<BN, NW> B;
+    OperandTile<BM, NW, SK> A;
+    OperandTile<BN, NW, SK> B;
     A.init(a.xq, a.ldq, m0, a.M);
     if (compact)
       B.init(a.wqc, a.ldq, n0, a.N);
     else
       B.init(a.wq, a.K, n0, a.N);
-    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li, lg,
-                                              acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li,
+                                                  lg, acc);
   }
 
   // dequantize in place: C * m[i] * s[n] / 127^2
@@ -327,12 +348,12 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
 
   // fp16 outlier product X_O . W_O over the gathered outlier columns
   if (count > 0 && a.w) {
-    OperandTile<BM, NW> A;
-    OperandTile<BN, NW> B;
+    OperandTile<BM, NW, SK> A;
+    OperandTile<BN, NW, SK> B;
     A.init(a.xo, a.ldo * 2, m0, a.M);
     B.init(a.wot, a.ldo * 2, n0, a.N);
-    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW>(smem, A, B, (count + 63) / 64, true, wm, wn, li, lg,
-                                              acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK>(smem, A, B, (2 * count + SK - 1) / SK, true, wm,
+                                                  wn, li, lg, acc);
   }
 
   // store Y (fp16, round to nearest even); rows past M fall outside the resource
@@ -355,14 +376,14 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
     }
 }
 
-template <int BM, int BN, int NWN, bool DBG>
+template <int BM, int BN, int NWN, int SK, bool DBG>
 hipError_t launch_prefill(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  using T = TileCfg<BM, BN, NWN>;
-  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, NWN, DBG>,
+  using T = TileCfg<BM, BN, NWN, SK>;
+  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, NWN, SK, DBG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, NWN, DBG>), dim3((unsigned)tiles),
+  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, NWN, SK, DBG>), dim3((unsigned)tiles),
                         dim3(T::THREADS), T::LDS, stream, (hipEvent_t)ev.begin,
                         (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();

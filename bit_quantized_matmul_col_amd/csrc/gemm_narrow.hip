@@ -4,8 +4,8 @@
 namespace llmint8 {
 
 hipError_t launch_gemm_narrow(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 128, 2, true>(a, ev, stream)
-                : gemm_detail::launch_prefill<256, 128, 2, false>(a, ev, stream);
+  return a.cdbg ? gemm_detail::launch_prefill<256, 128, 2, 128, true>(a, ev, stream)
+                : gemm_detail::launch_prefill<256, 128, 2, 128, false>(a, ev, stream);
 }
 
 }  // namespace llmint8
