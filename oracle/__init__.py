@@ -10,6 +10,10 @@ from .oracle import (  # noqa: F401
     quantize_rowwise,
     gemm_i8,
     merge,
+    merge_int8w,
+    add_bias,
+    quantize_tensorwise,
+    linear_tensorwise,
     linear,
     linear_rows,
 )

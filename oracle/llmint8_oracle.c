@@ -22,7 +22,14 @@
  *        section 3.2 (round, then clamp, then cast; compute in float32) and
  *        section 3.3 (symmetric: zero point 0, clamp to [-127, 127]).
  *   [P1] "8-Bit LLM Quantization with Lightning Fabric" (aicoding) section 2.2
- *        (int8 x int8 -> int32 matmul, then rescale by scale_x * scale_w).
+ *        (int8 x int8 -> int32 matmul, then rescale by scale_x * scale_w and
+ *        add the bias), section 3.12 (per-layer quantization error as the
+ *        mean absolute difference from the 16-bit output).
+ *   [P2] also section 2.4 (int8 weights take half the memory of fp16 ones)
+ *        and section 6 (the int8 weights are kept and reused; the fp16 ones
+ *        need not be).
+ *   [P5] also section 2 (the traditional 8-bit quantization uses one scale for
+ *        the whole matrix).
  *
  * Readings taken where the pages are silent or disagree:
  *   - outlier test is |x| >= threshold (inclusive); a column is an outlier when
@@ -213,4 +220,81 @@ int32_t ora_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
         return -1;
     ora_merge(C, m, s, X, ldx, W, ldw, idx, count, M, N, Y);
     return count;
+}
+
+/* Int8-only weight residency ([P2] sections 2.4 and 6: only Wq and s are
+ * kept). The 16-bit outlier product then takes the outlier rows of W from the
+ * dequantized codes, W_O[k, n] = Wq[n, k] * s[n] / 127, instead of the fp16
+ * rows. Otherwise as ora_merge: fp64, outlier terms in ascending k. */
+void ora_merge_int8w(const int32_t *C, const float *m, const float *s,
+                     const uint16_t *X, int64_t ldx, const int8_t *Wq, int64_t K,
+                     const int32_t *idx, int32_t count, int64_t M, int64_t N, double *Y)
+{
+    double *yo = malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t n = 0; n < N; ++n)
+            yo[n] = 0.0;
+        for (int32_t p = 0; p < count; ++p) {
+            int64_t k = idx[p];
+            double x = (double)ora_half(X[i * ldx + k]);
+            for (int64_t n = 0; n < N; ++n)
+                yo[n] += x * ((double)Wq[n * K + k] * (double)s[n] / 127.0);
+        }
+        for (int64_t n = 0; n < N; ++n)
+            Y[i * N + n] = (double)C[i * N + n] * (double)m[i] * (double)s[n] / 16129.0 + yo[n];
+    }
+    free(yo);
+}
+
+/* The traditional 8-bit comparison ([P5] section 2: one scale for the whole
+ * matrix; section 1: scale = 127 / max|x|): one absmax over all of W, the same
+ * quantizer. Wq is [N x K] as in ora_quantize_colwise. Returns the absmax. */
+float ora_quantize_tensorwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq)
+{
+    float sw = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            float a = fabsf(ora_half(W[k * ldw + n]));
+            if (a > sw)
+                sw = a;
+        }
+    float inv = sw > 0.0f ? 127.0f / sw : 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Wq[n * K + k] = sw > 0.0f ? ora_quant(ora_half(W[k * ldw + n]), inv) : 0;
+    return sw;
+}
+
+/* The traditional 8-bit linear layer: one absmax over all of X, the int8
+ * matmul, and Y = C * sx * sw / 127^2 (fp64). No outlier decomposition. Xq is
+ * [M x K]; returns sx. */
+float ora_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                            const int8_t *Wq, float sw, int64_t N, int8_t *Xq, int32_t *C,
+                            double *Y)
+{
+    float sx = 0.0f;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(ora_half(X[i * ldx + k]));
+            if (a > sx)
+                sx = a;
+        }
+    float inv = sx > 0.0f ? 127.0f / sx : 0.0f;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            Xq[i * K + k] = sx > 0.0f ? ora_quant(ora_half(X[i * ldx + k]), inv) : 0;
+    ora_gemm_i8(Xq, Wq, M, N, K, C);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t n = 0; n < N; ++n)
+            Y[i * N + n] = (double)C[i * N + n] * (double)sx * (double)sw / 16129.0;
+    return sx;
+}
+
+/* The bias of the layer, added after the rescale ([P1] section 2.2):
+ * Y[i, n] += b[n] with b an fp16 vector of N entries. */
+void ora_add_bias(double *Y, int64_t M, int64_t N, const uint16_t *bias)
+{
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t n = 0; n < N; ++n)
+            Y[i * N + n] += (double)ora_half(bias[n]);
 }

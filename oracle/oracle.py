@@ -38,6 +38,14 @@ def _load():
         lib.ora_gemm_i8.restype = C.c_int
         lib.ora_merge.argtypes = [p, p, p, p, i64, p, i64, p, C.c_int32, i64, i64, p]
         lib.ora_merge.restype = None
+        lib.ora_merge_int8w.argtypes = [p, p, p, p, i64, p, i64, p, C.c_int32, i64, i64, p]
+        lib.ora_merge_int8w.restype = None
+        lib.ora_quantize_tensorwise.argtypes = [p, i64, i64, i64, p]
+        lib.ora_quantize_tensorwise.restype = C.c_float
+        lib.ora_linear_tensorwise.argtypes = [p, i64, i64, i64, p, C.c_float, i64, p, p, p]
+        lib.ora_linear_tensorwise.restype = C.c_float
+        lib.ora_add_bias.argtypes = [p, i64, i64, p]
+        lib.ora_add_bias.restype = None
         _lib = lib
     return _lib
 
@@ -122,18 +130,83 @@ def merge(Cm: np.ndarray, m: np.ndarray, s: np.ndarray, X: np.ndarray, W: np.nda
     return Y
 
 
-def linear(X: np.ndarray, W: np.ndarray, threshold: float, Wq=None, s=None) -> dict:
-    """The whole layer. Returns every intermediate the GPU path also exposes."""
+def merge_int8w(Cm: np.ndarray, m: np.ndarray, s: np.ndarray, X: np.ndarray, Wq: np.ndarray,
+                idx: np.ndarray) -> np.ndarray:
+    """Dequantize C and add the outlier product with W_O = Wq . s / 127 -> Y float64."""
+    X = _bits(X)
+    Cm = np.ascontiguousarray(Cm, dtype=np.int32)
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    Wq = np.ascontiguousarray(Wq, dtype=np.int8)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    M, N = Cm.shape
+    Y = np.empty((M, N), np.float64)
+    _load().ora_merge_int8w(_ptr(Cm), _ptr(m), _ptr(s), _ptr(X), X.shape[1], _ptr(Wq),
+                            Wq.shape[1], _ptr(idx), int(idx.size), M, N, _ptr(Y))
+    return Y
+
+
+def add_bias(Y: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """Y float64 [M, N] + fp16 bias [N] (a new array)."""
+    Y = np.array(Y, dtype=np.float64, order="C")
+    b = _bits(bias)
+    _load().ora_add_bias(_ptr(Y), Y.shape[0], Y.shape[1], _ptr(b))
+    return Y
+
+
+def quantize_tensorwise(W: np.ndarray):
+    """W fp16 [K, N] -> (Wq int8 [N, K], absmax float32 over all of W)."""
+    W = _bits(W)
+    K, N = W.shape
+    Wq = np.empty((N, K), np.int8)
+    sw = _load().ora_quantize_tensorwise(_ptr(W), K, N, N, _ptr(Wq))
+    return Wq, np.float32(sw)
+
+
+def linear_tensorwise(X: np.ndarray, Wq: np.ndarray, sw, bias=None) -> dict:
+    """The traditional per-tensor int8 layer (no outlier decomposition)."""
+    X = _bits(X)
+    Wq = np.ascontiguousarray(Wq, dtype=np.int8)
+    M, K = X.shape
+    N = Wq.shape[0]
+    Xq = np.empty((M, K), np.int8)
+    Cm = np.empty((M, N), np.int32)
+    Y = np.empty((M, N), np.float64)
+    sx = _load().ora_linear_tensorwise(_ptr(X), M, K, K, _ptr(Wq), float(sw), N, _ptr(Xq),
+                                       _ptr(Cm), _ptr(Y))
+    if bias is not None:
+        Y = add_bias(Y, bias)
+    return dict(Xq=Xq, sx=np.float32(sx), C=Cm, Y=Y)
+
+
+def _merge_mode(Cm, m, s, X, W, Wq, idx, outlier_weights):
+    if outlier_weights == "fp16":
+        return merge(Cm, m, s, X, W, idx)
+    if outlier_weights == "int8":
+        return merge_int8w(Cm, m, s, X, Wq, idx)
+    raise ValueError("outlier_weights is 'fp16' or 'int8'")
+
+
+def linear(X: np.ndarray, W: np.ndarray, threshold: float, Wq=None, s=None, *,
+           outlier_weights: str = "fp16", bias=None) -> dict:
+    """The whole layer. Returns every intermediate the GPU path also exposes.
+
+    outlier_weights "fp16" takes the outlier rows of W as given; "int8" takes
+    them from the dequantized codes Wq * s / 127 (W is then only needed to
+    quantize, if Wq and s are not passed). bias, if given, is added last."""
     if Wq is None or s is None:
         Wq, s = quantize_colwise(W)
     idx = find_outliers(X, threshold)
     Xq, m = quantize_rowwise(X, idx)
     Cm = gemm_i8(Xq, Wq)
-    Y = merge(Cm, m, s, X, W, idx)
+    Y = _merge_mode(Cm, m, s, X, W, Wq, idx, outlier_weights)
+    if bias is not None:
+        Y = add_bias(Y, bias)
     return dict(idx=idx, Xq=Xq, m=m, Wq=Wq, s=s, C=Cm, Y=Y)
 
 
-def linear_rows(X: np.ndarray, W: np.ndarray, threshold: float, rows, Wq=None, s=None) -> dict:
+def linear_rows(X: np.ndarray, W: np.ndarray, threshold: float, rows, Wq=None, s=None, *,
+                outlier_weights: str = "fp16", bias=None) -> dict:
     """The layer's results for selected rows of X only.
 
     The outlier set is a property of the whole X, so it is found on all rows;
@@ -146,5 +219,7 @@ def linear_rows(X: np.ndarray, W: np.ndarray, threshold: float, rows, Wq=None, s
     Xs = np.ascontiguousarray(_bits(X)[rows])
     Xq, m = quantize_rowwise(Xs, idx)
     Cm = gemm_i8(Xq, Wq)
-    Y = merge(Cm, m, s, Xs, W, idx)
+    Y = _merge_mode(Cm, m, s, Xs, W, Wq, idx, outlier_weights)
+    if bias is not None:
+        Y = add_bias(Y, bias)
     return dict(rows=rows, idx=idx, Xq=Xq, m=m, Wq=Wq, s=s, C=Cm, Y=Y)

@@ -283,3 +283,107 @@ def test_outlier_isolation_beats_per_tensor_int8():
     e_mixed = np.linalg.norm(y - exact)
     e_tensor = np.linalg.norm(per_tensor - exact)
     assert e_mixed * 5 < e_tensor
+
+
+# --- int8-only weight residency (walkthrough sections 2.4 and 6) --------------------
+
+def exact_code_weight(K, N, seed):
+    """fp16 W whose columns are integer codes times a power of two, with one code
+    of magnitude 127 per column: quantize_colwise recovers the codes exactly and
+    Wq * s / 127 reproduces W exactly."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-127, 128, size=(K, N))
+    q[rng.integers(0, K, size=N), np.arange(N)] = 127 * rng.choice([-1, 1], size=N)
+    e = rng.integers(-12, -4, size=N).astype(np.float64)
+    return (q * np.exp2(e)).astype(np.float16), q, e
+
+
+def test_int8_weights_equal_fp16_weights_when_codes_are_exact():
+    X, _, _ = workloads.random_case(9, 96, 8, seed=3, n_out=4)
+    W, q, e = exact_code_weight(96, 20, seed=4)
+    a = oracle.linear(X, W, 6.0)
+    assert np.array_equal(a["Wq"].T.astype(np.int64), q)
+    assert np.array_equal(a["s"].astype(np.float64), 127 * np.exp2(e))
+    b = oracle.linear(X, W, 6.0, outlier_weights="int8")
+    assert a["idx"].size >= 4
+    assert np.array_equal(a["Y"], b["Y"])
+
+
+def test_int8_weights_all_outlier_is_matmul_with_dequantized_codes():
+    # threshold 0: every column is an outlier, so Y = X . (Wq^T * s / 127) exactly
+    X, W, _ = workloads.random_case(7, 64, 24, seed=5, n_out=2)
+    r = oracle.linear(X, W, 0.0, outlier_weights="int8")
+    assert r["idx"].size == 64 and not r["C"].any()
+    deq = r["Wq"].T.astype(np.float64) * r["s"].astype(np.float64) / 127.0
+    np.testing.assert_allclose(r["Y"], X.astype(np.float64) @ deq, rtol=1e-12, atol=1e-12)
+
+
+def test_int8_weights_without_outliers_change_nothing():
+    X, W, _ = workloads.random_case(11, 80, 16, seed=6, n_out=3)
+    a = oracle.linear(X, W, math.inf)
+    b = oracle.linear(X, W, math.inf, outlier_weights="int8")
+    assert a["idx"].size == 0 and np.array_equal(a["Y"], b["Y"])
+
+
+def test_int8_weights_brute_force():
+    X, W, _ = workloads.random_case(3, 32, 5, seed=7, n_out=2)
+    r = oracle.linear(X, W, 5.0, outlier_weights="int8")
+    xf = X.astype(np.float64)
+    Wq, s = r["Wq"], r["s"].astype(np.float64)
+    for i in range(3):
+        for n in range(5):
+            acc = sum(float(r["Xq"][i, k]) * float(Wq[n, k]) for k in range(32))
+            y = acc * float(r["m"][i]) * s[n] / 16129.0
+            for k in r["idx"]:
+                y += xf[i, k] * (float(Wq[n, k]) * s[n] / 127.0)
+            assert abs(y - r["Y"][i, n]) <= 1e-12 * max(1.0, abs(y))
+
+
+# --- the traditional per-tensor int8 layer (codearts page sections 1 and 2) -----------
+
+def test_per_tensor_worked_example_codearts_section2():
+    # the page's example is one scale for the whole (1 x 4) tensor
+    g = load("p5_worked_example.txt")
+    X = f16([floats(g["x"])])
+    W = np.eye(4, dtype=np.float16)
+    Wq, sw = oracle.quantize_tensorwise(W)
+    r = oracle.linear_tensorwise(X, Wq, sw)
+    assert r["Xq"][0].tolist() == ints(g["q"])
+    assert round(127.0 / float(r["sx"]), 2) == float(g["scale_printed"][0])
+
+
+def test_per_tensor_exact_integers_reduce_to_integer_matmul():
+    rng = np.random.default_rng(8)
+    X = rng.integers(-100, 101, size=(6, 40)).astype(np.float16)
+    W = rng.integers(-100, 101, size=(40, 12)).astype(np.float16)
+    # both absmax 127, reached only in the last row and column: scale 1, codes = values
+    X[5, 39], W[39, 11] = 127, -127
+    Wq, sw = oracle.quantize_tensorwise(W)
+    r = oracle.linear_tensorwise(X, Wq, sw)
+    assert float(sw) == 127.0 and float(r["sx"]) == 127.0
+    exact = X.astype(np.int64) @ W.astype(np.int64)
+    assert np.array_equal(r["C"].astype(np.int64), exact)
+    assert np.array_equal(r["Y"], exact.astype(np.float64))
+
+
+def test_per_tensor_weights_equal_per_column_when_columns_share_the_absmax():
+    X, W, _ = workloads.random_case(1, 48, 10, seed=9)
+    W = W.astype(np.float32)
+    W[5, :] = 0.75  # every column reaches the same absmax 0.75 (larger than the rest)
+    W = W.astype(np.float16)
+    Wq_t, sw = oracle.quantize_tensorwise(W)
+    Wq_c, s = oracle.quantize_colwise(W)
+    assert np.all(s == sw) and np.array_equal(Wq_t, Wq_c)
+
+
+def test_bias_is_added_after_the_rescale():
+    X, W, _ = workloads.random_case(5, 64, 12, seed=10, n_out=2)
+    b = (np.arange(12) * 0.125 - 0.5).astype(np.float16)
+    for mode in ("fp16", "int8"):
+        a = oracle.linear(X, W, 6.0, outlier_weights=mode)
+        c = oracle.linear(X, W, 6.0, outlier_weights=mode, bias=b)
+        assert np.array_equal(c["Y"], a["Y"] + b.astype(np.float64)[None, :])
+    Wq, sw = oracle.quantize_tensorwise(W)
+    a = oracle.linear_tensorwise(X, Wq, sw)
+    c = oracle.linear_tensorwise(X, Wq, sw, bias=b)
+    assert np.array_equal(c["Y"], a["Y"] + b.astype(np.float64)[None, :])
