@@ -29,10 +29,16 @@ LLMINT8_MAX_K = 133144
 _lib = None
 
 
+LLMINT8_OUTLIER_W_FP16 = 0
+LLMINT8_OUTLIER_W_INT8 = 1
+
+
 class LinearOpts(C.Structure):
     """Mirror of llmint8_linear_opts."""
     _fields_ = [("struct_size", C.c_size_t), ("gemm_begin_event", C.c_void_p),
-                ("gemm_end_event", C.c_void_p)]
+                ("gemm_end_event", C.c_void_p), ("outlier_weights", C.c_int),
+                ("bias", C.c_void_p), ("y_col_absmax", C.c_void_p),
+                ("x_col_absmax", C.c_void_p)]
 
     def __init__(self, **kw):
         super().__init__(struct_size=C.sizeof(LinearOpts), **kw)
@@ -162,9 +168,17 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
                    W: torch.Tensor | None, threshold: float = 6.0, *, Y=None, workspace=None,
                    outlier_count: torch.Tensor | None = None,
                    C_debug: torch.Tensor | None = None,
-                   opts: LinearOpts | None = None) -> torch.Tensor:
+                   opts: LinearOpts | None = None, outlier_weights: str = "fp16",
+                   bias: torch.Tensor | None = None,
+                   y_col_absmax: torch.Tensor | None = None,
+                   x_col_absmax: torch.Tensor | None = None) -> torch.Tensor:
     """The whole LLM.int8() layer: fp16 X [M, K] with Wq [N, K], col_absmax [N] and the
-    fp16 weight W [K, N] (rows in the outlier set feed the 16-bit product) -> fp16 Y [M, N]."""
+    fp16 weight W [K, N] (rows in the outlier set feed the 16-bit product) -> fp16 Y [M, N].
+
+    outlier_weights "int8" takes the outlier rows from the codes Wq * col_absmax / 127
+    instead (W may then be None); bias [N] fp16 is added to Y; y_col_absmax [N] fp32
+    receives max_i |Y[i, n]|; x_col_absmax [K] fp32, if given, is taken as X's column
+    absmax and decides the outlier columns without a scan of X."""
     _need(X, "X", torch.float16, 2)
     _need(Wq, "Wq", torch.int8, 2)
     _need(col_absmax, "col_absmax", torch.float32, 1)
@@ -172,21 +186,41 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
     N = Wq.shape[0]
     if Wq.shape[1] != K or not Wq.is_contiguous():
         raise ValueError("Wq must be contiguous [N, K]")
+    if outlier_weights not in ("fp16", "int8"):
+        raise ValueError("outlier_weights is 'fp16' or 'int8'")
     if W is not None:
         _need(W, "W", torch.float16, 2)
         if tuple(W.shape) != (K, N):
             raise ValueError("W must be [K, N]")
-    elif not (math.isinf(threshold) and threshold > 0):
-        raise ValueError("W may be omitted only with threshold=+inf")
+    elif outlier_weights == "fp16" and not (math.isinf(threshold) and threshold > 0):
+        raise ValueError("W may be omitted only with threshold=+inf or int8 outlier weights")
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, "Y", torch.float16, 2)
     for name, t in (("outlier_count", outlier_count), ("C_debug", C_debug)):
         if t is not None:
             _need(t, name, torch.int32)
+    for name, t, dt, n in (("bias", bias, torch.float16, N),
+                           ("y_col_absmax", y_col_absmax, torch.float32, N),
+                           ("x_col_absmax", x_col_absmax, torch.float32, K)):
+        if t is not None:
+            _need(t, name, dt, 1)
+            if t.numel() != n or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous vector of {n}")
     if workspace is None:
         workspace = torch.empty((llmint8_workspace_size(M, K, N),), dtype=torch.uint8,
                                 device=X.device)
+    extra = (outlier_weights != "fp16" or bias is not None or y_col_absmax is not None
+             or x_col_absmax is not None)
+    if extra:
+        o = LinearOpts(gemm_begin_event=opts.gemm_begin_event if opts else None,
+                       gemm_end_event=opts.gemm_end_event if opts else None,
+                       outlier_weights=(LLMINT8_OUTLIER_W_INT8 if outlier_weights == "int8"
+                                        else LLMINT8_OUTLIER_W_FP16),
+                       bias=bias.data_ptr() if bias is not None else None,
+                       y_col_absmax=y_col_absmax.data_ptr() if y_col_absmax is not None else None,
+                       x_col_absmax=x_col_absmax.data_ptr() if x_col_absmax is not None else None)
+        opts = o
     args = (_ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
             _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
             _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X))

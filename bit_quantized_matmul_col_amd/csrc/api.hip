@@ -159,8 +159,9 @@ LLMINT8_EXPORT int llmint8_find_outliers(const uint16_t *X, int64_t M, int64_t K
   if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
   uint8_t *ws = (uint8_t *)workspace;
-  DetectOut d{(uint32_t *)(ws + L.pmask), (uint32_t *)(ws + L.omask), (int32_t *)(ws + L.wprefix),
-              idx, (int32_t *)(ws + L.nidx), count, nullptr};
+  DetectOut d{nullptr, threshold, nullptr, 0, (uint32_t *)(ws + L.pmask),
+              (uint32_t *)(ws + L.omask), (int32_t *)(ws + L.wprefix), idx,
+              (int32_t *)(ws + L.nidx), count, nullptr};
   return hip_status(launch_detect(X, M, K, ldx, threshold, detect_plan(M, K), d,
                                   (hipStream_t)stream));
 }
@@ -190,11 +191,18 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
                                      void *workspace, size_t workspace_bytes, void *stream,
                                      const llmint8_linear_opts *opts) {
   if (opts && opts->struct_size != sizeof(llmint8_linear_opts)) return LLMINT8_ERR_INVALID_ARG;
+  const llmint8_linear_opts o = opts ? *opts : llmint8_linear_opts{};
+  if (o.outlier_weights != LLMINT8_OUTLIER_W_FP16 && o.outlier_weights != LLMINT8_OUTLIER_W_INT8)
+    return LLMINT8_ERR_INVALID_ARG;
+  const bool int8w = o.outlier_weights == LLMINT8_OUTLIER_W_INT8;
+  if ((o.bias && !aligned16(o.bias)) || (o.y_col_absmax && !aligned16(o.y_col_absmax)) ||
+      (o.x_col_absmax && !aligned16(o.x_col_absmax)))
+    return LLMINT8_ERR_UNSUPPORTED;
   int st = check_matrix(X, M, K, ldx);
   if (st) return st;
   if ((st = check_matrix(Y, M, N, ldy))) return st;
   if (!Wq || !col_absmax || std::isnan(threshold)) return LLMINT8_ERR_INVALID_ARG;
-  if (!W && !(std::isinf(threshold) && threshold > 0)) return LLMINT8_ERR_INVALID_ARG;
+  if (!W && !int8w && !(std::isinf(threshold) && threshold > 0)) return LLMINT8_ERR_INVALID_ARG;
   if (W && (st = check_matrix(W, K, N, ldw))) return st;
   if ((st = check_k(K))) return st;
   if (N % 8 != 0 || !aligned16(Wq) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
@@ -208,12 +216,15 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  const GemmEvents ev{opts ? opts->gemm_begin_event : nullptr,
-                      opts ? opts->gemm_end_event : nullptr};
+  const GemmEvents ev{o.gemm_begin_event, o.gemm_end_event};
+  // with int8 outlier weights the fp16 weight is not read at all
+  const uint16_t *Wf = int8w ? nullptr : W;
+  const EpilogueOpts ep{int8w ? 1 : 0, o.bias, o.y_col_absmax};
 
   if (fused_decode_fits(M, K, ldx)) {
-    const FusedArgs f{X, Wq, col_absmax, W, Y, C_debug, outlier_count_out, ldx, ldw, ldy,
-                      (int)M, (int)K, (int)N, (int)((N + 15) / 16), fp16_threshold_bits(threshold)};
+    const FusedArgs f{X, Wq, col_absmax, Wf, Y, C_debug, outlier_count_out, ldx, ldw, ldy,
+                      (int)M, (int)K, (int)N, (int)((N + 15) / 16), fp16_threshold_bits(threshold),
+                      threshold, o.x_col_absmax, ep};
     return hip_status(launch_decode_fused(f, ev, s));
   }
   if (M <= kDecodeMaxM) {
@@ -221,10 +232,11 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
     const int64_t kw = (K + 31) / 32;
     uint32_t *omask = (uint32_t *)(ws + L.omask);
     float *pmax = (float *)(ws + L.pmask);
-    DecodeDetectArgs det{X, (int)M, K, ldx, kw, threshold, omask, pmax};
-    DecodeGemmArgs g{X, Wq, col_absmax, omask, pmax, W, (int32_t *)(ws + L.part),
+    DecodeDetectArgs det{X, (int)M, K, ldx, kw, threshold, omask, pmax, o.x_col_absmax,
+                         o.y_col_absmax, N};
+    DecodeGemmArgs g{X, Wq, col_absmax, omask, pmax, Wf, (int32_t *)(ws + L.part),
                      (float *)(ws + L.m), outlier_count_out, Y, C_debug,
-                     M, N, K, kw, dp.kc, ldx, ldw, ldy, dp.det_blocks, dp.kb};
+                     M, N, K, kw, dp.kc, ldx, ldw, ldy, dp.det_blocks, dp.kb, ep};
     return hip_status(launch_decode(det, g, dp, ev, s));
   }
 
@@ -238,18 +250,21 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   uint16_t *xo = (uint16_t *)(ws + L.xo);
   int8_t *wqc = (int8_t *)(ws + L.wqc);
 
-  DetectOut d{(uint32_t *)(ws + L.pmask), omask, wprefix, idx, (int32_t *)(ws + L.nidx), count,
-              outlier_count_out};
+  DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
+              wprefix, idx, (int32_t *)(ws + L.nidx), count, outlier_count_out};
   const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
   uint16_t *wot = (uint16_t *)(ws + L.wot);
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
   if (e == hipSuccess)
     e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, ldq, m, xo, ldo, s);
   if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, ldq, s);
-  if (e == hipSuccess && W) e = launch_gather_wot(W, ldw, N, idx, count, wot, ldo, s);
+  if (e == hipSuccess && (Wf || int8w))
+    e = launch_gather_wot(Wf, ldw, Wq, K, N, idx, count, wot, ldo, s);
   if (e == hipSuccess) {
-    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, W, count, Y, C_debug, M, N, K, ldq, ldo, ldw,
-               ldy};
+    // the GEMM's outlier product runs when it has weight rows (gathered above)
+    const uint16_t *wo_src = (Wf || int8w) ? wot : nullptr;
+    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, wo_src ? (const uint16_t *)wot : nullptr,
+               count, Y, C_debug, M, N, K, ldq, ldo, ldw, ldy, ep};
     e = launch_gemm(g, ev, s);
   }
   return hip_status(e);

@@ -45,6 +45,15 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   const int64_t col0 = (int64_t)blockIdx.x * kDetCols + c * 8;
   const bool colok = col0 < a.K;
   const uint16_t *base = a.X + (colok ? col0 : 0);
+  if (a.ycmax)  // the epilogue's column maxima start from zero
+    for (int64_t n = (int64_t)blockIdx.x * kDetCols + t; n < a.N; n += (int64_t)gridDim.x * kDetCols)
+      a.ycmax[n] = 0.f;
+  // a caller-supplied column absmax decides the outlier columns
+  float xc = 0.f;
+  if (a.xcmax) {
+    const int64_t col = (int64_t)blockIdx.x * kDetCols + t;
+    xc = a.xcmax[col < a.K ? col : 0];
+  }
 
   u32x4 v[8];
 #pragma unroll
@@ -67,7 +76,7 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
 #pragma unroll
     for (int p = 0; p < kDetRows; ++p) mx = __builtin_fmaxf(mx, scol[p][t]);
     const int64_t col = (int64_t)blockIdx.x * kDetCols + t;
-    const bool flag = col < a.K && mx >= a.threshold;
+    const bool flag = col < a.K && (a.xcmax ? xc : mx) >= a.threshold;
     const uint64_t bal = __ballot(flag);
     if ((t & 63) == 0) {
       sflag[(t >> 5)] = (uint32_t)bal;
@@ -295,11 +304,15 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     mrow[i] = a.m[rowc];
   }
   const float scol = a.s[colc];
+  const float bcol = a.ep.bias ? h2f(a.ep.bias[colc]) : 0.f;
+  // the outlier product runs with fp16 weight rows or with the int8 codes
+  const bool i8w = a.ep.int8w != 0;
+  const bool outl = a.w || i8w;
   const __amdgpu_buffer_rsrc_t mrs =
       __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
-  uint32_t mw = a.w ? __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0) : 0u;
+  uint32_t mw = outl ? __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0) : 0u;
 
-  float y[4];
+  float y[4], yo[4] = {0.f, 0.f, 0.f, 0.f};
   const float sd = scol * (1.0f / 16129.0f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -311,9 +324,10 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     y[i] = (float)cacc * (mrow[i] * sd);
   }
 
-  // fp16 outlier terms, outlier columns in ascending order
+  // fp16 outlier terms, outlier columns in ascending order (yo: with int8
+  // weight codes they are scaled by s / 127 at the end)
   int total_all = 0;
-  if (a.w) {
+  if (outl) {
     for (int64_t w0 = 0; w0 < a.kw; w0 += kListWords) {
       if (w0 > 0) {
         __syncthreads();  // the previous window's list is consumed
@@ -352,8 +366,19 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
           const int p = t >> 3, ch = t & 7;
           const int64_t cc = n0 + 8 * ch;
           const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
-          *(u32x4 *)(swo + p * kTileN + 8 * ch) =
-              *(const u32x4 *)(a.w + kk * a.ldw + (cc < a.N ? cc : a.N - 8));
+          u32x4 v;
+          if (i8w) {  // codes Wq[n, kk] of the 8 columns, as fp16 (exact)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t c0 = cc + 2 * e, c1 = c0 + 1;
+              const int q0 = a.wq[(c0 < a.N ? c0 : a.N - 1) * a.K + kk];
+              const int q1 = a.wq[(c1 < a.N ? c1 : a.N - 1) * a.K + kk];
+              v[e] = (uint32_t)f2h((float)q0) | ((uint32_t)f2h((float)q1) << 16);
+            }
+          } else {
+            v = *(const u32x4 *)(a.w + kk * a.ldw + (cc < a.N ? cc : a.N - 8));
+          }
+          *(u32x4 *)(swo + p * kTileN + 8 * ch) = v;
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {  // X entries: 16 rows x 32 outliers
@@ -367,7 +392,7 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
         for (int p = 0; p < np; ++p) {
           const float wval = h2f(swo[p * kTileN + lane]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] += sxo[wv + 4 * i][p] * wval;
+          for (int i = 0; i < 4; ++i) yo[i] += sxo[wv + 4 * i][p] * wval;
         }
         __syncthreads();
       }
@@ -384,11 +409,23 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     if (t == 0) *a.count_out = scount[0] + scount[1] + scount[2] + scount[3];
   }
 
-  if (colok) {
+  const float oscale = i8w ? scol * (1.0f / 127.0f) : 1.0f;
+  float cmax = 0.f;  // |Y| of this column over the block's rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rbase + wv + 4 * i;
-      if (row < a.M) a.y[(int64_t)row * a.ldy + col] = f2h(y[i]);
+  for (int i = 0; i < 4; ++i) {
+    const int row = rbase + wv + 4 * i;
+    const float v = y[i] + yo[i] * oscale + bcol;
+    if (colok && row < a.M) a.y[(int64_t)row * a.ldy + col] = f2h(v);
+    cmax = row < a.M ? __builtin_fmaxf(cmax, stored_abs(v)) : cmax;
+  }
+  if (a.ep.ycmax) {
+    __shared__ float scm[4][kTileN];
+    scm[wv][lane] = cmax;
+    __syncthreads();
+    if (t < kTileN && n0 + t < a.N) {
+      const float mx = __builtin_fmaxf(__builtin_fmaxf(scm[0][t], scm[1][t]),
+                                       __builtin_fmaxf(scm[2][t], scm[3][t]));
+      ycmax_update(a.ep.ycmax, n0 + t, mx);
     }
   }
 }

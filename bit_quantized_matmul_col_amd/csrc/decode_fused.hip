@@ -75,7 +75,7 @@ __device__ inline uint32_t pmax16(uint32_t a, uint32_t b) {
 // Layout of the dynamic LDS (byte offsets); P = K + 16 is the Xq row pitch
 // (16 rows that one MFMA operand reads fall in distinct bank groups).
 struct FusedLds {
-  int xq, red, list, inv, m, bits, rmax, xo0, misc, total;
+  int xq, red, list, inv, m, bits, rmax, xo0, ycm, misc, total;
 };
 
 __host__ __device__ constexpr FusedLds fused_lds(int K, int MB) {
@@ -101,6 +101,8 @@ __host__ __device__ constexpr FusedLds fused_lds(int K, int MB) {
   o += kWaves * 32 * 4;
   L.xo0 = o;  // X entries of the first outlier batch [16][64] fp32
   o += 16 * MB * kBatch * 4;
+  L.ycm = o;  // per-wave column maxima of |Y| [4][16]
+  o += 4 * 16 * 4;
   L.misc = o;
   o += 64;
   L.total = o;
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   static_assert(MB == 1, "one output per thread");
   struct TileRegs {
     u32x4 b[KS];
-    float sc;
+    float sc, bias;
     u32x4 wo;
   };
   auto load_b = [&](TileRegs &tr, int tile) {
@@ -178,19 +180,38 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     for (int j = 0; j < KS; ++j) tr.b[j] = *(const u32x4 *)(row + 64 * j);
     const int no = tile * kTileCols + (t & 15);
     tr.sc = a.s[no < a.N ? no : a.N - 1];
+    tr.bias = a.ep.bias ? h2f(a.ep.bias[no < a.N ? no : a.N - 1]) : 0.f;
   };
   // W rows of outlier columns p0 .. p0 + 63 for the tile: thread t < 128 loads
   // row p0 + t / 2, columns 8 (t % 2) .. + 8 of the tile
+  // (with int8 outlier weights: the codes Wq[n, k] of those columns as fp16)
   auto load_wo = [&](int tile, int p0, int np) {
     const int p = t >> 1, half = t & 1;
     const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
     const int nc = tile * kTileCols + 8 * half;
+    if (a.ep.int8w) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c0 = nc + 2 * e, c1 = c0 + 1;
+        const int q0 = a.wq[(int64_t)(c0 < a.N ? c0 : a.N - 1) * K + kk];
+        const int q1 = a.wq[(int64_t)(c1 < a.N ? c1 : a.N - 1) * K + kk];
+        v[e] = (uint32_t)f2h((float)q0) | ((uint32_t)f2h((float)q1) << 16);
+      }
+      return v;
+    }
     return *(const u32x4 *)(a.w + kk * a.ldw + (nc < a.N ? nc : a.N - 8));
   };
   // 2. X: chunk c of rows h + R j (rows past M read as zero: harmless for every
   //    max, and their codes are replaced by zeros). X is issued before Wq: loads
   //    complete in issue order, and steps 3-5 wait only for X.
   const int c = t % C, h = t / C;
+  // a caller-supplied column absmax of X decides the outlier columns
+  f32x4 xc0 = {0.f, 0.f, 0.f, 0.f}, xc1 = xc0;
+  if (a.xcmax && h == 0) {
+    xc0 = *(const f32x4 *)(a.xcmax + 8 * c);
+    xc1 = *(const f32x4 *)(a.xcmax + 8 * c + 4);
+  }
   u32x4 xv[MR];
   {
     // one buffer resource over rows 0 .. M-1: rows past M read as zero and
@@ -229,10 +250,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   }
   if (h == 0) {
     uint32_t bits = 0;
+    if (a.xcmax) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bits |= ((cm[e] & 0xffffu) >= a.tcut ? 1u : 0u) << (2 * e);
-      bits |= ((cm[e] >> 16) >= a.tcut ? 1u : 0u) << (2 * e + 1);
+      for (int e = 0; e < 4; ++e) {
+        bits |= (xc0[e] >= a.threshold ? 1u : 0u) << e;
+        bits |= (xc1[e] >= a.threshold ? 1u : 0u) << (4 + e);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bits |= ((cm[e] & 0xffffu) >= a.tcut ? 1u : 0u) << (2 * e);
+        bits |= ((cm[e] >> 16) >= a.tcut ? 1u : 0u) << (2 * e + 1);
+      }
     }
     sbits[c] = (uint8_t)bits;
   }
@@ -310,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   // first batch of the fp16 outlier product: its X entries (tile independent)
   // and the W rows of the first tile, in flight while the codes are computed
   const int total = *stotal;
-  const bool outl = total > 0 && a.w;
+  const bool outl = total > 0 && (a.w || a.ep.int8w);
   const int np0 = total < kBatch ? total : kBatch;
   float xo0[2] = {0.f, 0.f};
   if (outl) {
@@ -367,12 +396,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     __syncthreads();
     // outputs: index q = t + 512 u (u < OPT) is row q / 16, column q % 16 of the tile
     constexpr int OPT = (MB * 256 + kThreads - 1) / kThreads;
-    float y[OPT];
+    float y[OPT], yo[OPT];
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int q = t + kThreads * u;
       const int orow = q >> 4, n = tile * kTileCols + (q & 15);
       y[u] = 0.f;
+      yo[u] = 0.f;
       if (q < MB * 256) {
         int cacc = 0;
 #pragma unroll
@@ -405,16 +435,34 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
           const int q = t + kThreads * u;
           if (q < MB * 256)
             for (int p = 0; p < np; ++p)
-              y[u] += xs[(q >> 4) * kBatch + p] * h2f(swo[p * 16 + (q & 15)]);
+              yo[u] += xs[(q >> 4) * kBatch + p] * h2f(swo[p * 16 + (q & 15)]);
         }
         __syncthreads();
       }
     }
+    // with int8 outlier weights the outlier terms carry the codes: times s / 127
+    const float oscale = a.ep.int8w ? tr.sc * (1.0f / 127.0f) : 1.0f;
+    float cmax = 0.f;
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int q = t + kThreads * u;
       const int orow = q >> 4, n = tile * kTileCols + (q & 15);
-      if (q < MB * 256 && orow < a.M && n < a.N) a.y[(int64_t)orow * a.ldy + n] = f2h(y[u]);
+      const float v = y[u] + yo[u] * oscale + tr.bias;
+      if (q < MB * 256 && orow < a.M && n < a.N) a.y[(int64_t)orow * a.ldy + n] = f2h(v);
+      cmax = (q < MB * 256 && orow < a.M) ? __builtin_fmaxf(cmax, stored_abs(v)) : cmax;
+    }
+    if (a.ep.ycmax) {
+      // the block holds every row of its 16 columns: rows 4 w + l / 16 of
+      // column l % 16 in lane l of wave w < 4
+      cmax = __builtin_fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = __builtin_fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      float *sycm = (float *)(lds + L.ycm);  // [4][16]
+      if (wv < 4 && lane < 16) sycm[wv * 16 + lane] = cmax;
+      __syncthreads();
+      const int n = tile * kTileCols + t;
+      if (t < 16 && n < a.N)
+        a.ep.ycmax[n] = __builtin_fmaxf(__builtin_fmaxf(sycm[t], sycm[16 + t]),
+                                        __builtin_fmaxf(sycm[32 + t], sycm[48 + t]));
     }
   };
 

@@ -11,7 +11,9 @@
 // test as "some entry >= t") and stored as 16 mask words per row chunk.
 // Pass 2 (k_detect_finish): one block ORs the row-chunk masks into LDS (all
 // partial-mask loads in flight at once), scans the per-word popcounts and writes
-// the ascending outlier and kept lists, the per-word prefix and the count.
+// the ascending outlier and kept lists, the per-word prefix and the count. When
+// the caller supplies the column absmax of X, pass 1 is skipped and pass 2
+// compares it with the threshold instead.
 #include "internal.hpp"
 
 namespace llmint8 {
@@ -74,25 +76,43 @@ __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restri
                                                         DetectOut out) {
   extern __shared__ uint32_t smask[];  // [kw]
   const int t = threadIdx.x;
-  for (int64_t w = t; w < kw; w += 1024) smask[w] = 0u;
-  __syncthreads();
-  // OR the row-chunk masks: every thread issues a batch of independent loads,
-  // then merges the non-zero words (rare) into LDS.
-  constexpr int kBatch = 8;
-  const int64_t total_words = (int64_t)row_chunks * kw;
-  for (int64_t base = 0; base < total_words; base += 1024 * kBatch) {
-    uint32_t v[kBatch];
+  if (out.ycmax)  // the epilogue's column maxima start from zero
+    for (int64_t n = t; n < out.N; n += 1024) out.ycmax[n] = 0.f;
+  if (out.xcmax) {
+    // outlier bits straight from the caller's column absmax of X
+    for (int64_t w = t; w < kw; w += 1024) {
+      uint32_t bits = 0u;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t k = 32 * w + 4 * j;
+        if (k >= K) break;
+        const f32x4 v = *(const f32x4 *)(out.xcmax + k);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t q = base + t + 1024 * u;
-      const uint32_t x = pmask[q < total_words ? q : 0];
-      v[u] = q < total_words ? x : 0u;
+        for (int e = 0; e < 4; ++e) bits |= (v[e] >= out.threshold ? 1u : 0u) << (4 * j + e);
+      }
+      smask[w] = bits;
     }
+    __syncthreads();
+  } else {
+    for (int64_t w = t; w < kw; w += 1024) smask[w] = 0u;
+    __syncthreads();
+    // OR the row-chunk masks: every thread issues a batch of independent loads,
+    // then merges the non-zero words (rare) into LDS.
+    constexpr int kBatch = 8;
+    const int64_t total_words = (int64_t)row_chunks * kw;
+    for (int64_t base = 0; base < total_words; base += 1024 * kBatch) {
+      uint32_t v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (v[u]) atomicOr(&smask[(base + t + 1024 * u) % kw], v[u]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t q = base + t + 1024 * u;
+        const uint32_t x = pmask[q < total_words ? q : 0];
+        v[u] = q < total_words ? x : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (v[u]) atomicOr(&smask[(base + t + 1024 * u) % kw], v[u]);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const int64_t per = (kw + 1023) / 1024;
   const int64_t w0 = (int64_t)t * per;
@@ -161,10 +181,13 @@ DetectPlan detect_plan(int64_t M, int64_t K) {
 
 hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
                          const DetectPlan &plan, const DetectOut &out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_detect_partial, dim3(plan.col_tiles, plan.row_chunks), dim3(256), 0, stream,
-                     X, M, K, ldx, threshold, plan.rows_per_chunk, plan.kw, out.pmask);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // a caller-supplied column absmax replaces the scan of X
+  if (!out.xcmax) {
+    hipLaunchKernelGGL(k_detect_partial, dim3(plan.col_tiles, plan.row_chunks), dim3(256), 0,
+                       stream, X, M, K, ldx, threshold, plan.rows_per_chunk, plan.kw, out.pmask);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_detect_finish, dim3(1), dim3(1024), (size_t)plan.kw * 4, stream,
                      (const uint32_t *)out.pmask,
                      plan.row_chunks, K, plan.kw, out);

@@ -56,6 +56,26 @@ __global__ __launch_bounds__(256) void k_gather_wot(const uint16_t *__restrict__
   }
 }
 
+// The int8 outlier-weight form of W_O^T [N x ldo]: row n holds the codes
+// Wq[n, idx[p]] as fp16 (exact) for p < |O|, zeros up to the next multiple of
+// 64. One block per 64 rows of Wq; a row's codes are gathered by 4 threads.
+__global__ __launch_bounds__(256) void k_gather_wot_codes(const int8_t *__restrict__ Wq, int64_t K,
+                                                          int64_t N,
+                                                          const int32_t *__restrict__ idx,
+                                                          const int32_t *__restrict__ count_ptr,
+                                                          uint16_t *__restrict__ wot, int64_t ldo) {
+  const int count = *count_ptr;
+  const int t = threadIdx.x;
+  const int64_t n = (int64_t)blockIdx.x * 64 + (t >> 2);
+  if (n >= N) return;
+  const int pad = (count + 63) / 64 * 64;
+  const int8_t *row = Wq + n * K;
+  for (int p = t & 3; p < pad; p += 4) {
+    const int q = p < count ? row[idx[p]] : 0;
+    wot[n * ldo + p] = f2h((float)q);
+  }
+}
+
 // Share of the CU slots that the tiles fill over all waves (one block per CU).
 double wave_fill(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t cus) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
@@ -78,10 +98,15 @@ bool narrow_tiles(int64_t M, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const int32_t *idx,
-                             const int32_t *count, uint16_t *wot, int64_t ldo, hipStream_t stream) {
-  hipLaunchKernelGGL(k_gather_wot, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream, W, ldw,
-                     N, idx, count, wot, ldo);
+hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, const int8_t *Wq, int64_t K,
+                             int64_t N, const int32_t *idx, const int32_t *count, uint16_t *wot,
+                             int64_t ldo, hipStream_t stream) {
+  if (W)
+    hipLaunchKernelGGL(k_gather_wot, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream, W, ldw,
+                       N, idx, count, wot, ldo);
+  else
+    hipLaunchKernelGGL(k_gather_wot_codes, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, stream,
+                       Wq, K, N, idx, count, wot, ldo);
   return hipGetLastError();
 }
 

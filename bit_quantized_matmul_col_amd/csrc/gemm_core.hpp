@@ -137,10 +137,11 @@ struct TileCfg {
   static constexpr int MI = WM / 32, NI = WN / 32;
   static constexpr int STAGE = (BM + BN) * SK;
   // stages in the LDS ring: as many as fit in the 160 KB of a CU, up to 4
-  static constexpr int FIT = (160 * 1024 - (BM + BN) * 4) / STAGE;
+  static constexpr int SCALES = (BM + 2 * BN) * 4;  // row scales, two column scales
+  static constexpr int FIT = (160 * 1024 - SCALES) / STAGE;
   static constexpr int NST = FIT > 4 ? 4 : FIT;
   static_assert(NST >= 2, "two stages must fit");
-  static constexpr int LDS = NST * STAGE + (BM + BN) * 4;
+  static constexpr int LDS = NST * STAGE + SCALES;
 };
 
 // Tile coordinates of this block after the XCD-aware renumbering.
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   extern __shared__ u32x4 smem_v[];
   uint8_t *smem = (uint8_t *)smem_v;
   float *sm = (float *)(smem + T::NST * T::STAGE);
-  float *ss = sm + BM;
+  float *ss = sm + BM;  // column factor of the int8 dequantization
+  float *sf = ss + BN;  // column factor applied at the end (int8 outlier weights)
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv / NWN, wn = wv % NWN;
@@ -296,8 +298,16 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   const bool compact = use_compaction(count, a.K, a.M);
   const int64_t Kl = compact ? a.K - count : a.K;
 
+  // Y = C m s / 127^2 + X_O W_O. With int8 outlier weights W_O = q s / 127, so
+  // Y = s / 127 * (C m / 127 + X_O q): the int8 part is scaled by m / 127
+  // before the 16-bit MFMAs add X_O q, and s / 127 is applied last.
+  const bool i8w = a.ep.int8w != 0;
   for (int i = t; i < BM; i += TH) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
-  for (int i = t; i < BN; i += TH) ss[i] = (n0 + i < a.N) ? a.s[n0 + i] * (1.0f / 16129.0f) : 0.f;
+  for (int i = t; i < BN; i += TH) {
+    const float sn = (n0 + i < a.N) ? a.s[n0 + i] : 0.f;
+    ss[i] = i8w ? 1.0f / 127.0f : sn * (1.0f / 16129.0f);
+    sf[i] = i8w ? sn * (1.0f / 127.0f) : 1.0f;
+  }
 
   i32x16 acc[MI * NI];
 #pragma unroll
@@ -361,19 +371,31 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   rows = rows < BM ? rows : BM;
   const rsrc_t ry = make_rsrc(a.y + m0 * a.ldy, rows * a.ldy * 2);
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int ni = 0; ni < NI; ++ni) {
+    const int cl = wn * WN + ni * 32 + li;
+    const bool colok = n0 + cl < a.N;
+    const float fin = sf[cl];
+    const float b = (a.ep.bias && colok) ? h2f(a.ep.bias[n0 + cl]) : 0.f;
+    float cmax = 0.f;  // |Y| of this column over the wave's rows
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int cl = wn * WN + ni * 32 + li;
-      if (n0 + cl >= a.N) continue;
+    for (int mi = 0; mi < MI; ++mi) {
       const f32x16 f = __builtin_bit_cast(f32x16, acc[mi * NI + ni]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        __builtin_amdgcn_raw_buffer_store_b16(f2h(f[r]), ry,
-                                              (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
+        const float y = f[r] * fin + b;
+        if (colok)
+          __builtin_amdgcn_raw_buffer_store_b16(f2h(y), ry,
+                                                (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
+        cmax = (m0 + rl < a.M) ? __builtin_fmaxf(cmax, stored_abs(y)) : cmax;
       }
     }
+    if (a.ep.ycmax) {
+      // lanes l and l + 32 hold the same column
+      cmax = __builtin_fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      if (lg == 0 && colok) ycmax_update(a.ep.ycmax, n0 + cl, cmax);
+    }
+  }
 }
 
 template <int BM, int BN, int NWN, int SK, bool DBG>

@@ -6,6 +6,23 @@
 
 namespace llmint8 {
 
+// What the layer's epilogue adds beyond Y = dequant(C) + X_O . W_O.
+struct EpilogueOpts {
+  int int8w;             // W_O from the int8 codes, Wq[n, k] * s[n] / 127
+  const uint16_t *bias;  // optional [N] fp16, added to every row
+  float *ycmax;          // optional [N]: max over rows of |Y[i, n]| as stored
+};
+
+// Column maxima of |Y| combined across blocks with an integer max on the float
+// bits (non-negative floats order like their patterns): the result does not
+// depend on the order.
+__device__ inline void ycmax_update(float *ycmax, int64_t n, float v) {
+  atomicMax((unsigned int *)(ycmax + n), __builtin_bit_cast(unsigned int, v));
+}
+
+// |Y| as stored: the fp16 rounding of v, as a float.
+__device__ inline float stored_abs(float v) { return __builtin_fabsf(h2f(f2h(v))); }
+
 // Outlier detection is split over row chunks: each (column tile, row chunk)
 // block writes one partial column bitmask; a single block ORs them.
 struct DetectPlan {
@@ -17,6 +34,10 @@ struct DetectPlan {
 DetectPlan detect_plan(int64_t M, int64_t K);
 
 struct DetectOut {
+  const float *xcmax;  // optional [K]: column absmax of X supplied by the caller
+  float threshold;
+  float *ycmax;        // optional [N], zeroed here for the epilogue's maxima
+  int64_t N;
   uint32_t *pmask;   // [row_chunks x kw] partial masks (scratch)
   uint32_t *omask;   // [kw] outlier bitmask, bit k%32 of word k/32
   int32_t *wprefix;  // [kw] outliers in words before w
@@ -56,9 +77,11 @@ hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
                              int8_t *Wqc, int64_t ldq, hipStream_t stream);
 
 // W_O^T [N x ldo] fp16: row n holds W[idx[p], n] for p < |O|, then zeros up to
-// the next multiple of 64.
-hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, int64_t N, const int32_t *idx,
-                             const int32_t *count, uint16_t *wot, int64_t ldo, hipStream_t stream);
+// the next multiple of 64. With W null it holds the int8 codes Wq[n, idx[p]]
+// instead (exact in fp16; the epilogue applies s[n] / 127).
+hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, const int8_t *Wq, int64_t K,
+                             int64_t N, const int32_t *idx, const int32_t *count, uint16_t *wot,
+                             int64_t ldo, hipStream_t stream);
 
 struct GemmArgs {
   const int8_t *xq;      // [M x ldq] int8 (compacted rows when compaction is on)
@@ -68,11 +91,12 @@ struct GemmArgs {
   const float *s;        // [N]
   const uint16_t *xo;    // [M x ldo] fp16 gathered outlier columns
   const uint16_t *wot;   // [N x ldo] fp16 outlier rows of W, transposed
-  const uint16_t *w;     // [K x ldw] fp16 original weight (null: no outlier product)
+  const uint16_t *w;     // non-null when the outlier product runs (rows gathered in wot)
   const int32_t *count;  // [1]
   uint16_t *y;           // [M x ldy] fp16
   int32_t *cdbg;         // optional [M x N] int32
   int64_t M, N, K, ldq, ldo, ldw, ldy;
+  EpilogueOpts ep;
 };
 
 // Caller-supplied events (may be null) that the GEMM kernel's own dispatch
@@ -97,6 +121,9 @@ struct DecodeDetectArgs {
   float threshold;
   uint32_t *omask;    // [kw] outlier bitmask
   float *pmax;        // [det_blocks x M] row absmax over each block's kept columns
+  const float *xcmax; // optional [K]: column absmax of X supplied by the caller
+  float *ycmax;       // optional [N], zeroed here for the epilogue's maxima
+  int64_t N;
 };
 
 struct DecodeGemmArgs {
@@ -114,6 +141,7 @@ struct DecodeGemmArgs {
   int64_t M, N, K, kw, kc, ldx, ldw, ldy;
   int det_blocks;
   int kb;             // K splits (partial sums per output)
+  EpilogueOpts ep;
 };
 
 struct DecodePlan {
@@ -141,6 +169,9 @@ struct FusedArgs {
   int M, K, N;
   int tiles;           // 16-column output tiles
   uint32_t tcut;       // smallest fp16 magnitude pattern whose value reaches the threshold
+  float threshold;
+  const float *xcmax;  // optional [K]: column absmax of X supplied by the caller
+  EpilogueOpts ep;
 };
 bool fused_decode_fits(int64_t M, int64_t K, int64_t ldx);
 hipError_t launch_decode_fused(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream);

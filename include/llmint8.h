@@ -122,20 +122,42 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                    uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Where the 16-bit outlier product takes its weight rows from. */
+#define LLMINT8_OUTLIER_W_FP16 0 /* rows k in O of the fp16 weight W */
+#define LLMINT8_OUTLIER_W_INT8 1 /* the dequantized codes Wq[n, k] * col_absmax[n] / 127 */
+
 /*
  * Options of llmint8_linear_ex. Zero-initialize, set struct_size =
- * sizeof(llmint8_linear_opts), then fill the fields you use; NULL fields are
- * off. The struct is read during the call only.
+ * sizeof(llmint8_linear_opts), then fill the fields you use; zero and NULL
+ * fields are off. The struct is read during the call only; pointers in it are
+ * device pointers, 16-byte aligned.
  *   gemm_begin_event, gemm_end_event  optional hipEvent_t handles (created by
  *       the caller) that the GEMM kernel's own dispatch on `stream` stamps when
  *       the kernel starts and when it completes (no separate stream commands),
  *       so a caller can time the dominant kernel of the layer with
  *       hipEventElapsedTime.
+ *   outlier_weights  LLMINT8_OUTLIER_W_FP16 (default) or LLMINT8_OUTLIER_W_INT8:
+ *       keep only the int8 weight (walkthrough page, sections 2.4 and 6: the
+ *       int8 weights replace the fp16 ones); W may then be NULL at any
+ *       threshold. Any other value is LLMINT8_ERR_INVALID_ARG.
+ *   bias         optional [N] fp16, added to every row of Y after the rescale
+ *       (Lightning Fabric page, section 2.2).
+ *   y_col_absmax optional [N] fp32 output: max over the M rows of |Y[i, n]| as
+ *       stored (fp16). The next layer can pass it as its x_col_absmax, which
+ *       spares its outlier scan a pass over its X.
+ *   x_col_absmax optional [K] fp32 input: max over the M rows of |X[i, k]|. The
+ *       outlier columns are then taken as those with x_col_absmax[k] >=
+ *       threshold, without a scan of X; the caller vouches that it is X's
+ *       column absmax (the result follows the values given).
  */
 typedef struct llmint8_linear_opts {
   size_t struct_size;
   void *gemm_begin_event;
   void *gemm_end_event;
+  int outlier_weights;
+  const uint16_t *bias;
+  float *y_col_absmax;
+  const float *x_col_absmax;
 } llmint8_linear_opts;
 
 /* llmint8_linear with options; opts == NULL is exactly llmint8_linear. A

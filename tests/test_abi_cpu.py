@@ -51,6 +51,10 @@ L.llmint8_quantize_colwise.argtypes = [p, i64, i64, i64, p, p, p]
 L.llmint8_find_outliers.argtypes = [p, i64, i64, i64, f32, p, p, p, sz, p]
 L.llmint8_quantize_rowwise.argtypes = [p, i64, i64, i64, p, p, p, p, p]
 L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p, sz, p]
+L.llmint8_linear_ex.argtypes = L.llmint8_linear.argtypes + [p]
+class Opts(C.Structure):
+    _fields_ = [("struct_size", sz), ("b", p), ("e", p), ("outlier_weights", C.c_int),
+                ("bias", p), ("y_col_absmax", p), ("x_col_absmax", p)]
 L.llmint8_workspace_size.argtypes = [i64, i64, i64]
 L.llmint8_workspace_size.restype = sz
 L.llmint8_find_outliers_workspace_size.argtypes = [i64, i64]
@@ -68,6 +72,10 @@ def rowq(name, X=A, M=4, K=64, ldx=64, idx=N0, cnt=N0, Xq=B, m=A):
 def linear(name, X=A, M=4, K=64, ldx=64, Wq=B, s=A, W=A, ldw=32, N=32, t=6.0, Y=B, ldy=32,
            cnt=N0, cdbg=N0, ws=A, wsb=0):
     res[name] = L.llmint8_linear(X, M, K, ldx, Wq, s, W, ldw, N, t, Y, ldy, cnt, cdbg, ws, wsb, None)
+def linear_ex(name, size=C.sizeof(Opts), ow=0, bias=N0, ycm=N0, xcm=N0, W=A, t=6.0, wsb=0):
+    o = Opts(size, None, None, ow, bias, ycm, xcm)
+    res[name] = L.llmint8_linear_ex(A, 4, 64, 64, B, A, W, 32, 32, t, B, 32, None, None, A, wsb,
+                                    None, C.byref(o))
 colwise("colwise_null_W", W=N0)
 colwise("colwise_K0", K=0)
 colwise("colwise_ld_short", ldw=16)
@@ -95,6 +103,13 @@ linear("linear_misaligned_cdbg", cdbg=MIS, wsb=1 << 40)
 linear("linear_workspace_small", wsb=100)
 linear("linear_K_not_mult16", K=40, ldx=48)
 linear("linear_N0", N=0)
+linear_ex("ex_struct_size_old", size=24)
+linear_ex("ex_bad_outlier_weights", ow=2)
+linear_ex("ex_misaligned_bias", bias=MIS)
+linear_ex("ex_misaligned_y_col_absmax", ycm=MIS)
+linear_ex("ex_misaligned_x_col_absmax", xcm=MIS)
+linear_ex("ex_int8_weights_null_W_small_ws", ow=1, W=N0)
+linear_ex("ex_fp16_weights_null_W", ow=0, W=N0)
 res["ws_size_ok"] = L.llmint8_workspace_size(32, 4096, 4096)
 res["ws_size_prefill"] = L.llmint8_workspace_size(2048, 4096, 11008)
 res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
@@ -114,6 +129,11 @@ EXPECTED = {
     "linear_null_Y": 1, "linear_ldy_short": 1, "linear_nan_threshold": 1,
     "linear_misaligned_cdbg": 2, "linear_workspace_small": 4, "linear_K_not_mult16": 2,
     "linear_N0": 1,
+    "ex_struct_size_old": 1, "ex_bad_outlier_weights": 1, "ex_misaligned_bias": 2,
+    "ex_misaligned_y_col_absmax": 2, "ex_misaligned_x_col_absmax": 2,
+    # int8 outlier weights need no fp16 W at any threshold: the call reaches the
+    # workspace check
+    "ex_int8_weights_null_W_small_ws": 4, "ex_fp16_weights_null_W": 1,
 }
 
 

@@ -289,3 +289,89 @@ def test_workload_70b(dev, w70, threshold, call):
     run_all(torch, lm, X, W, threshold, rows=sample_rows(wl.M, 6), check_colwise=(call == 0),
             ref_w=ref_w)
     torch.cuda.empty_cache()
+
+
+# --- layer options: int8 outlier weights, bias, column absmax out and in ---------------
+
+# one shape per path: single kernel (M <= 16, K 4096), three-kernel small M,
+# large M, large M with K-compaction (threshold 3.0 flags ~a third of K)
+OPTION_CASES = [(5, 4096, 520, 6.0), (48, 2048, 1032, 2.5), (300, 1024, 264, 6.0),
+                (700, 1008, 200, 3.0)]
+
+
+@pytest.mark.parametrize("M,K,N,threshold", OPTION_CASES)
+@pytest.mark.parametrize("tau_override", [None, 0.0, math.inf])
+def test_int8_outlier_weights(dev, M, K, N, threshold, tau_override):
+    torch, lm = dev
+    tau = threshold if tau_override is None else tau_override
+    say(f"case int8 outlier weights M={M} K={K} N={N} threshold={tau}")
+    X, W, _ = workloads.random_case(M, K, N, seed=M + 7 * K + N, n_out=3)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    Y = lm.llmint8_linear(Xd, Wq, s, None, tau, outlier_weights="int8", C_debug=C,
+                          outlier_count=cnt)
+    Yp = lm.llmint8_linear(Xd, Wq, s, None, tau, outlier_weights="int8")
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yp.view(torch.int16))
+    ref = oracle.linear(X, W, tau, outlier_weights="int8")
+    assert int(cnt.item()) == ref["idx"].size
+    assert np.array_equal(C.cpu().numpy(), ref["C"]), "C differs"
+    assert_y_close(Y.cpu().numpy(), ref["Y"], "Y")
+
+
+@pytest.mark.parametrize("M,K,N,threshold", OPTION_CASES)
+@pytest.mark.parametrize("mode", ["fp16", "int8"])
+def test_bias_and_output_column_absmax(dev, M, K, N, threshold, mode):
+    torch, lm = dev
+    say(f"case bias and Y column absmax M={M} K={K} N={N} mode={mode}")
+    X, W, _ = workloads.random_case(M, K, N, seed=M + K + 3 * N, n_out=3)
+    b = (np.random.default_rng(N).standard_normal(N) * 0.5).astype(np.float16)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    ycm = torch.full((N,), 1e30, dtype=torch.float32, device="cuda")  # must be overwritten
+    Y = lm.llmint8_linear(Xd, Wq, s, Wd, threshold, outlier_weights=mode,
+                          bias=to_gpu(torch, b), y_col_absmax=ycm)
+    torch.cuda.synchronize()
+    ref = oracle.linear(X, W, threshold, outlier_weights=mode, bias=b)
+    y = Y.cpu().numpy()
+    assert_y_close(y, ref["Y"], "Y")
+    # the maxima are those of the stored fp16 Y, exactly
+    assert np.array_equal(ycm.cpu().numpy(), np.abs(y.astype(np.float32)).max(axis=0))
+
+
+@pytest.mark.parametrize("M,K,N,threshold", OPTION_CASES)
+def test_supplied_input_column_absmax(dev, M, K, N, threshold):
+    torch, lm = dev
+    say(f"case supplied X column absmax M={M} K={K} N={N}")
+    X, W, _ = workloads.random_case(M, K, N, seed=2 * M + K + N, n_out=3)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    xcm = to_gpu(torch, np.abs(X.astype(np.float32)).max(axis=0))
+    c0 = torch.empty(1, dtype=torch.int32, device="cuda")
+    c1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    Y0 = lm.llmint8_linear(Xd, Wq, s, Wd, threshold, outlier_count=c0)
+    Y1 = lm.llmint8_linear(Xd, Wq, s, Wd, threshold, outlier_count=c1, x_col_absmax=xcm)
+    torch.cuda.synchronize()
+    assert int(c0.item()) == int(c1.item()) == oracle.find_outliers(X, threshold).size
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+
+
+def test_column_absmax_chains_two_layers(dev):
+    # layer 1 emits its Y's column absmax; layer 2 takes it instead of scanning
+    torch, lm = dev
+    say("case two chained layers through the column absmax")
+    X, W1, _ = workloads.random_case(200, 512, 1024, seed=31, n_out=3, w_sigma=0.2)
+    _, W2, _ = workloads.random_case(1, 1024, 256, seed=32)
+    Xd = to_gpu(torch, X)
+    W1d, W2d = to_gpu(torch, W1), to_gpu(torch, W2)
+    Wq1, s1 = lm.llmint8_quantize_colwise(W1d)
+    Wq2, s2 = lm.llmint8_quantize_colwise(W2d)
+    ycm = torch.empty(1024, dtype=torch.float32, device="cuda")
+    H = lm.llmint8_linear(Xd, Wq1, s1, W1d, 6.0, y_col_absmax=ycm)
+    Z0 = lm.llmint8_linear(H, Wq2, s2, W2d, 6.0)
+    Z1 = lm.llmint8_linear(H, Wq2, s2, W2d, 6.0, x_col_absmax=ycm)
+    torch.cuda.synchronize()
+    assert torch.equal(Z0.view(torch.int16), Z1.view(torch.int16))
+    assert oracle.find_outliers(H.cpu().numpy(), 6.0).size > 0
