@@ -70,10 +70,18 @@ def lib() -> C.CDLL:
         L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p,
                                      sz, p]
         L.llmint8_linear_ex.argtypes = L.llmint8_linear.argtypes + [p]
+        L.llmint8_quantize_tensorwise_workspace_size.argtypes = [i64, i64]
+        L.llmint8_quantize_tensorwise_workspace_size.restype = sz
+        L.llmint8_quantize_tensorwise.argtypes = [p, i64, i64, i64, p, p, p, sz, p]
+        L.llmint8_linear_tensorwise_workspace_size.argtypes = [i64, i64, i64]
+        L.llmint8_linear_tensorwise_workspace_size.restype = sz
+        L.llmint8_linear_tensorwise.argtypes = [p, i64, i64, i64, p, p, i64, p, p, i64, p, p, p,
+                                                sz, p]
         L.llmint8_status_string.argtypes = [C.c_int]
         L.llmint8_status_string.restype = C.c_char_p
         for name in ("llmint8_quantize_colwise", "llmint8_find_outliers",
-                     "llmint8_quantize_rowwise", "llmint8_linear", "llmint8_linear_ex"):
+                     "llmint8_quantize_rowwise", "llmint8_linear", "llmint8_linear_ex",
+                     "llmint8_quantize_tensorwise", "llmint8_linear_tensorwise"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -228,4 +236,59 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
         _check(lib().llmint8_linear(*args))
     else:
         _check(lib().llmint8_linear_ex(*args, C.byref(opts)))
+    return Y
+
+
+def llmint8_quantize_tensorwise_workspace_size(K: int, N: int) -> int:
+    return int(lib().llmint8_quantize_tensorwise_workspace_size(K, N))
+
+
+def llmint8_quantize_tensorwise(W: torch.Tensor, workspace=None):
+    """fp16 W [K, N] -> (Wq int8 [N, K], w_absmax fp32 [1]): one scale for all of W."""
+    _need(W, "W", torch.float16, 2)
+    K, N = W.shape
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    sw = torch.empty((1,), dtype=torch.float32, device=W.device)
+    if workspace is None:
+        workspace = torch.empty((max(llmint8_quantize_tensorwise_workspace_size(K, N), 1),),
+                                dtype=torch.uint8, device=W.device)
+    _check(lib().llmint8_quantize_tensorwise(_ptr(W), K, N, _ld(W, "W"), _ptr(Wq), _ptr(sw),
+                                             _ptr(workspace), workspace.numel(), _stream(W)))
+    return Wq, sw
+
+
+def llmint8_linear_tensorwise_workspace_size(M: int, K: int, N: int) -> int:
+    return int(lib().llmint8_linear_tensorwise_workspace_size(M, K, N))
+
+
+def llmint8_linear_tensorwise(X: torch.Tensor, Wq: torch.Tensor, w_absmax: torch.Tensor, *,
+                              bias: torch.Tensor | None = None, Y=None, workspace=None,
+                              x_absmax: torch.Tensor | None = None,
+                              C_debug: torch.Tensor | None = None) -> torch.Tensor:
+    """The traditional per-tensor int8 layer: fp16 X [M, K], Wq [N, K] and w_absmax [1]
+    from llmint8_quantize_tensorwise -> fp16 Y [M, N] (no outlier decomposition)."""
+    _need(X, "X", torch.float16, 2)
+    _need(Wq, "Wq", torch.int8, 2)
+    _need(w_absmax, "w_absmax", torch.float32, 1)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or not Wq.is_contiguous():
+        raise ValueError("Wq must be contiguous [N, K]")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+        if bias.numel() != N or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous vector of {N}")
+    for name, t in (("x_absmax", x_absmax), ("C_debug", C_debug)):
+        if t is not None:
+            _need(t, name, torch.float32 if name == "x_absmax" else torch.int32)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if workspace is None:
+        workspace = torch.empty((llmint8_linear_tensorwise_workspace_size(M, K, N),),
+                                dtype=torch.uint8, device=X.device)
+    _check(lib().llmint8_linear_tensorwise(
+        _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(w_absmax), N, _ptr(bias), _ptr(Y),
+        _ld(Y, "Y"), _ptr(x_absmax), _ptr(C_debug), _ptr(workspace), workspace.numel(),
+        _stream(X)))
     return Y

@@ -270,6 +270,85 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   return hip_status(e);
 }
 
+LLMINT8_EXPORT size_t llmint8_quantize_tensorwise_workspace_size(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
+  return up((size_t)N * 4);
+}
+
+LLMINT8_EXPORT int llmint8_quantize_tensorwise(const uint16_t *W, int64_t K, int64_t N,
+                                               int64_t ldw, int8_t *Wq, float *w_absmax,
+                                               void *workspace, size_t workspace_bytes,
+                                               void *stream) {
+  int st = check_matrix(W, K, N, ldw);
+  if (st) return st;
+  if (!Wq || !w_absmax) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq) || !aligned16(w_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < up((size_t)N * 4)) return LLMINT8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_tensorwise(W, K, N, ldw, Wq, w_absmax, (float *)workspace,
+                                               (hipStream_t)stream));
+}
+
+namespace {
+
+// Workspace of llmint8_linear_tensorwise: partial maxima, broadcast scales,
+// a zero outlier count, the padded int8 copy of X.
+struct TensorwiseOffsets {
+  size_t partial, m, s, count, xq, total;
+};
+
+TensorwiseOffsets tensorwise_offsets(int64_t M, int64_t K, int64_t N) {
+  TensorwiseOffsets L{};
+  size_t o = 0;
+  L.partial = o;
+  o += up((size_t)kTensorAbsBlocks * 4);
+  L.m = o;
+  o += up((size_t)M * 4);
+  L.s = o;
+  o += up((size_t)N * 4);
+  L.count = o;
+  o += up(64);
+  L.xq = o;
+  o += up((size_t)M * (size_t)pitch_q(K));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+LLMINT8_EXPORT size_t llmint8_linear_tensorwise_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
+  return tensorwise_offsets(M, K, N).total;
+}
+
+LLMINT8_EXPORT int llmint8_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K,
+                                             int64_t ldx, const int8_t *Wq,
+                                             const float *w_absmax, int64_t N,
+                                             const uint16_t *bias, uint16_t *Y, int64_t ldy,
+                                             float *x_absmax, int32_t *C_debug, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if ((st = check_matrix(Y, M, N, ldy))) return st;
+  if (!Wq || !w_absmax) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq) || !aligned16(w_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if ((bias && !aligned16(bias)) || (x_absmax && !aligned16(x_absmax)) ||
+      (C_debug && !aligned16(C_debug)))
+    return LLMINT8_ERR_UNSUPPORTED;
+  if (ldy >= kMaxTileLd || N >= kMaxTileLd) return LLMINT8_ERR_UNSUPPORTED;
+  const TensorwiseOffsets o = tensorwise_offsets(M, K, N);
+  if (!workspace || workspace_bytes < o.total) return LLMINT8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
+  uint8_t *ws = (uint8_t *)workspace;
+  const TensorwiseLayout L{(float *)(ws + o.partial), (float *)(ws + o.m), (float *)(ws + o.s),
+                           (int32_t *)(ws + o.count), (int8_t *)(ws + o.xq), pitch_q(K)};
+  return hip_status(launch_linear_tensorwise(X, M, K, ldx, Wq, w_absmax, N, Y, ldy, bias,
+                                             x_absmax, C_debug, L, GemmEvents{nullptr, nullptr},
+                                             (hipStream_t)stream));
+}
+
 LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                                   const int8_t *Wq, const float *col_absmax, const uint16_t *W,
                                   int64_t ldw, int64_t N, float threshold, uint16_t *Y,

@@ -66,9 +66,14 @@ hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_
                                  const int32_t *count, int8_t *Xq, int64_t ldq, float *m,
                                  uint16_t *xo, int64_t ldo, hipStream_t stream);
 
-// Column absmax + quantize + transpose of W [K x N] into Wq [N x K].
+// Column absmax + quantize + transpose of W [K x N] into Wq [N x K]; the two
+// halves also run alone (s: column maxima out, then the scales the codes use).
 hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
                           float *s, hipStream_t stream);
+hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, float *s,
+                                 hipStream_t stream);
+hipError_t launch_colwise_quant(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                const float *s, int8_t *Wq, hipStream_t stream);
 
 // Compacted copy Wqc [N x K] (first K - |O| bytes of each row) of Wq without
 // the outlier columns; a no-op unless the outlier share calls for it.
@@ -175,5 +180,27 @@ struct FusedArgs {
 };
 bool fused_decode_fits(int64_t M, int64_t K, int64_t ldx);
 hipError_t launch_decode_fused(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream);
+
+// The per-tensor int8 layer (one absmax for all of X, one for all of W).
+// scratch holds N floats.
+hipError_t launch_quantize_tensorwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                      int8_t *Wq, float *w_absmax, float *scratch,
+                                      hipStream_t stream);
+
+constexpr int kTensorAbsBlocks = 512;  // blocks of the partial max|X| pass
+
+struct TensorwiseLayout {
+  float *partial;  // [kTensorAbsBlocks]
+  float *m;        // [M], every entry max|X|
+  float *s;        // [N], every entry max|W|
+  int32_t *count;  // [1], zero: no outlier product
+  int8_t *xq;      // [M x ldq], zero past column K
+  int64_t ldq;
+};
+hipError_t launch_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                    const int8_t *Wq, const float *w_absmax, int64_t N,
+                                    uint16_t *Y, int64_t ldy, const uint16_t *bias,
+                                    float *x_absmax, int32_t *cdbg, const TensorwiseLayout &L,
+                                    const GemmEvents &ev, hipStream_t stream);
 
 }  // namespace llmint8

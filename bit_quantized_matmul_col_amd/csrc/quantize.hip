@@ -321,8 +321,8 @@ hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
-                          float *s, hipStream_t stream) {
+hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, float *s,
+                                 hipStream_t stream) {
   unsigned *sbits = (unsigned *)s;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, sbits, N,
                      0u);
@@ -335,11 +335,21 @@ hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, 
   const int row_chunks = (int)((K + rows_per_chunk - 1) / rows_per_chunk);
   hipLaunchKernelGGL(k_colabsmax, dim3(col_tiles, row_chunks), dim3(256), 0, stream, W, K, N, ldw,
                      rows_per_chunk, sbits);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_colquant, dim3((unsigned)((K + 127) / 128), (unsigned)((N + 63) / 64)),
-                     dim3(256), 0, stream, W, K, N, ldw, (const float *)s, Wq);
   return hipGetLastError();
+}
+
+hipError_t launch_colwise_quant(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                const float *s, int8_t *Wq, hipStream_t stream) {
+  hipLaunchKernelGGL(k_colquant, dim3((unsigned)((K + 127) / 128), (unsigned)((N + 63) / 64)),
+                     dim3(256), 0, stream, W, K, N, ldw, s, Wq);
+  return hipGetLastError();
+}
+
+hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
+                          float *s, hipStream_t stream) {
+  const hipError_t e = launch_colwise_absmax(W, K, N, ldw, s, stream);
+  if (e != hipSuccess) return e;
+  return launch_colwise_quant(W, K, N, ldw, s, Wq, stream);
 }
 
 hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,

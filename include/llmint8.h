@@ -169,6 +169,43 @@ int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                       void *workspace, size_t workspace_bytes, void *stream,
                       const llmint8_linear_opts *opts);
 
+/*
+ * The traditional 8-bit layer that LLM.int8() is measured against ("LLM.int8()
+ * pitfalls" page, section 2: one scale for the whole matrix; section 1: scale =
+ * 127 / max|x|). No outlier decomposition: an outlier sets the scale of every
+ * entry. Same conventions and shape rules as the calls above.
+ *
+ * llmint8_quantize_tensorwise: W [K x N] fp16 (ldw >= N) ->
+ *   Wq       [N x K] int8 output, Wq[n, k] = clamp(rint(W[k, n] * fl32(127 / sw)), -127, 127);
+ *   w_absmax [1] fp32 output (device): sw = max over all of W of |W[k, n]|.
+ *   workspace at least llmint8_quantize_tensorwise_workspace_size(K, N) bytes.
+ * Bit-exact with that definition; sw = 0 gives all-zero codes.
+ */
+size_t llmint8_quantize_tensorwise_workspace_size(int64_t K, int64_t N);
+int llmint8_quantize_tensorwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                int8_t *Wq, float *w_absmax, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * llmint8_linear_tensorwise: Y = fp16( C * sx * sw / 127^2 [+ bias] ) with
+ *   sx = max over all of X of |X[i, k]|, Xq = clamp(rint(X * fl32(127 / sx)), -127, 127),
+ *   C = Xq . Wq^T (int32, exact).
+ *   X          [M x K] fp16, leading dimension ldx >= K.
+ *   Wq, w_absmax  from llmint8_quantize_tensorwise.
+ *   bias       optional [N] fp16, added after the rescale (Lightning Fabric
+ *              page, section 2.2).
+ *   Y          [M x N] fp16 output, leading dimension ldy >= N.
+ *   x_absmax   optional [1] fp32 output (device): sx.
+ *   C_debug    optional [M x N] int32 output (leading dimension N): C.
+ *   workspace  at least llmint8_linear_tensorwise_workspace_size(M, K, N) bytes.
+ */
+size_t llmint8_linear_tensorwise_workspace_size(int64_t M, int64_t K, int64_t N);
+int llmint8_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                              const int8_t *Wq, const float *w_absmax, int64_t N,
+                              const uint16_t *bias, uint16_t *Y, int64_t ldy, float *x_absmax,
+                              int32_t *C_debug, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *llmint8_status_string(int status);
 

@@ -57,6 +57,12 @@ class Opts(C.Structure):
                 ("bias", p), ("y_col_absmax", p), ("x_col_absmax", p)]
 L.llmint8_workspace_size.argtypes = [i64, i64, i64]
 L.llmint8_workspace_size.restype = sz
+L.llmint8_quantize_tensorwise.argtypes = [p, i64, i64, i64, p, p, p, sz, p]
+L.llmint8_quantize_tensorwise_workspace_size.argtypes = [i64, i64]
+L.llmint8_quantize_tensorwise_workspace_size.restype = sz
+L.llmint8_linear_tensorwise.argtypes = [p, i64, i64, i64, p, p, i64, p, p, i64, p, p, p, sz, p]
+L.llmint8_linear_tensorwise_workspace_size.argtypes = [i64, i64, i64]
+L.llmint8_linear_tensorwise_workspace_size.restype = sz
 L.llmint8_find_outliers_workspace_size.argtypes = [i64, i64]
 L.llmint8_find_outliers_workspace_size.restype = sz
 A, B, MIS = 0x100000, 0x200000, 0x300008   # 16-byte aligned fakes and a misaligned one
@@ -76,6 +82,12 @@ def linear_ex(name, size=C.sizeof(Opts), ow=0, bias=N0, ycm=N0, xcm=N0, W=A, t=6
     o = Opts(size, None, None, ow, bias, ycm, xcm)
     res[name] = L.llmint8_linear_ex(A, 4, 64, 64, B, A, W, 32, 32, t, B, 32, None, None, A, wsb,
                                     None, C.byref(o))
+def qtw(name, W=A, K=64, N=32, ldw=32, Wq=B, sw=A, ws=A, wsb=1 << 20):
+    res[name] = L.llmint8_quantize_tensorwise(W, K, N, ldw, Wq, sw, ws, wsb, None)
+def ltw(name, X=A, M=4, K=64, ldx=64, Wq=B, sw=A, N=32, bias=N0, Y=B, ldy=32, xa=N0, cdbg=N0,
+        ws=A, wsb=0):
+    res[name] = L.llmint8_linear_tensorwise(X, M, K, ldx, Wq, sw, N, bias, Y, ldy, xa, cdbg, ws,
+                                            wsb, None)
 colwise("colwise_null_W", W=N0)
 colwise("colwise_K0", K=0)
 colwise("colwise_ld_short", ldw=16)
@@ -110,7 +122,24 @@ linear_ex("ex_misaligned_y_col_absmax", ycm=MIS)
 linear_ex("ex_misaligned_x_col_absmax", xcm=MIS)
 linear_ex("ex_int8_weights_null_W_small_ws", ow=1, W=N0)
 linear_ex("ex_fp16_weights_null_W", ow=0, W=N0)
+qtw("qtw_null_sw", sw=N0)
+qtw("qtw_misaligned_Wq", Wq=MIS)
+qtw("qtw_K_not_mult16", K=40)
+qtw("qtw_workspace_small", wsb=16)
+qtw("qtw_no_workspace", ws=N0)
+qtw("qtw_K_too_big", K=133152)
+ltw("ltw_null_Wq", Wq=N0)
+ltw("ltw_null_X", X=N0)
+ltw("ltw_ldy_short", ldy=16)
+ltw("ltw_misaligned_bias", bias=MIS)
+ltw("ltw_misaligned_x_absmax", xa=MIS)
+ltw("ltw_N_not_mult8", N=36, ldy=40)
+ltw("ltw_workspace_small", wsb=64)
 res["ws_size_ok"] = L.llmint8_workspace_size(32, 4096, 4096)
+res["qtw_ws"] = L.llmint8_quantize_tensorwise_workspace_size(4096, 11008)
+res["qtw_ws_bad"] = L.llmint8_quantize_tensorwise_workspace_size(4096, 0)
+res["ltw_ws"] = L.llmint8_linear_tensorwise_workspace_size(2048, 4096, 11008)
+res["ltw_ws_bad"] = L.llmint8_linear_tensorwise_workspace_size(2048, 133160, 64)
 res["ws_size_prefill"] = L.llmint8_workspace_size(2048, 4096, 11008)
 res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
 res["find_ws_ok"] = L.llmint8_find_outliers_workspace_size(8192, 8192)
@@ -134,6 +163,10 @@ EXPECTED = {
     # int8 outlier weights need no fp16 W at any threshold: the call reaches the
     # workspace check
     "ex_int8_weights_null_W_small_ws": 4, "ex_fp16_weights_null_W": 1,
+    "qtw_null_sw": 1, "qtw_misaligned_Wq": 2, "qtw_K_not_mult16": 2, "qtw_workspace_small": 4,
+    "qtw_no_workspace": 4, "qtw_K_too_big": 3,
+    "ltw_null_Wq": 1, "ltw_null_X": 1, "ltw_ldy_short": 1, "ltw_misaligned_bias": 2,
+    "ltw_misaligned_x_absmax": 2, "ltw_N_not_mult8": 2, "ltw_workspace_small": 4,
 }
 
 
@@ -152,6 +185,9 @@ def test_invalid_arguments_are_rejected_before_any_hip_call():
     assert res["ws_size_prefill"] >= 2048 * 4096 * 3 + 11008 * 4096
     assert res["ws_size_bad"] == 0
     assert res["find_ws_ok"] > 0 and res["find_ws_bad"] == 0
+    # per-tensor layer: the column maxima for W; the int8 copy of X and the scales
+    assert res["qtw_ws"] >= 11008 * 4 and res["qtw_ws_bad"] == 0
+    assert res["ltw_ws"] >= 2048 * 4096 + 2048 * 4 + 11008 * 4 and res["ltw_ws_bad"] == 0
 
 
 def test_status_strings():

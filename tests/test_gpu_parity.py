@@ -375,3 +375,89 @@ def test_column_absmax_chains_two_layers(dev):
     torch.cuda.synchronize()
     assert torch.equal(Z0.view(torch.int16), Z1.view(torch.int16))
     assert oracle.find_outliers(H.cpu().numpy(), 6.0).size > 0
+
+
+# --- the traditional per-tensor int8 layer -----------------------------------------------
+
+TENSOR_CASES = [(1, 16, 8), (5, 4096, 520), (48, 2048, 1032), (257, 784, 520), (300, 1024, 264),
+                (700, 1008, 200)]
+
+
+def check_tensorwise(torch, lm, X, W, bias=None, rows=None):
+    M, K = X.shape
+    N = W.shape[1]
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, sw = lm.llmint8_quantize_tensorwise(Wd)
+    Wq_r, sw_r = oracle.quantize_tensorwise(W)
+    torch.cuda.synchronize()
+    assert np.array_equal(Wq.cpu().numpy(), Wq_r), "per-tensor Wq differs"
+    assert sw.cpu().numpy().view(np.uint32)[0] == np.float32(sw_r).view(np.uint32), "sw differs"
+    C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    sx = torch.empty(1, dtype=torch.float32, device="cuda")
+    bd = to_gpu(torch, bias) if bias is not None else None
+    Y = lm.llmint8_linear_tensorwise(Xd, Wq, sw, bias=bd, x_absmax=sx, C_debug=C)
+    Yp = lm.llmint8_linear_tensorwise(Xd, Wq, sw, bias=bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yp.view(torch.int16)), "debug/production Y differ"
+    if rows is None:
+        ref = oracle.linear_tensorwise(X, Wq_r, sw_r, bias=bias)
+        assert np.array_equal(C.cpu().numpy(), ref["C"]), "per-tensor C differs"
+        y = Y.cpu().numpy()
+    else:
+        # rows are independent once sx is known; the subset keeps the row that
+        # holds max|X|, so its absmax is that of the whole X
+        amax_row = int(np.abs(X.astype(np.float32)).max(axis=1).argmax())
+        rows = sorted(set(rows) | {amax_row})
+        ref = oracle.linear_tensorwise(np.ascontiguousarray(X[rows]), Wq_r, sw_r, bias=bias)
+        rt = torch.tensor(rows, device="cuda")
+        assert np.array_equal(C.index_select(0, rt).cpu().numpy(), ref["C"]), "C rows differ"
+        y = Y.index_select(0, rt).cpu().numpy()
+    assert sx.cpu().numpy().view(np.uint32)[0] == ref["sx"].view(np.uint32), "sx differs"
+    assert_y_close(y, ref["Y"], "per-tensor Y")
+    return Y
+
+
+@pytest.mark.parametrize("M,K,N", TENSOR_CASES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_tensorwise_layer(dev, M, K, N, with_bias):
+    torch, lm = dev
+    say(f"case per-tensor M={M} K={K} N={N} bias={with_bias}")
+    X, W, _ = workloads.random_case(M, K, N, seed=5 * M + K + N, n_out=2)
+    b = (np.random.default_rng(M).standard_normal(N) * 0.5).astype(np.float16) if with_bias else None
+    check_tensorwise(torch, lm, X, W, bias=b)
+
+
+def test_tensorwise_zero_inputs(dev):
+    # a zero matrix has absmax 0: its codes are all zero and so is C
+    torch, lm = dev
+    say("case per-tensor zero X and zero W")
+    X, W, _ = workloads.random_case(40, 256, 64, seed=9)
+    check_tensorwise(torch, lm, np.zeros_like(X), W)
+    check_tensorwise(torch, lm, X, np.zeros_like(W))
+
+
+def test_tensorwise_workload_sampled(dev):
+    torch, lm = dev
+    wl = workloads.WORKLOADS["prefill"]
+    say("case per-tensor on the prefill workload (sampled rows)")
+    X, W = workloads.make_x(wl), workloads.make_w(wl)
+    check_tensorwise(torch, lm, X, W, rows=sample_rows(wl.M))
+    torch.cuda.empty_cache()
+
+
+def test_tensorwise_loses_more_than_mixed_decomposition(dev):
+    # with outlier columns in X one scale squeezes every other entry into a few
+    # codes; the mixed decomposition keeps them (the per-tensor error is larger)
+    torch, lm = dev
+    say("case per-tensor vs mixed decomposition error")
+    X, W, _ = workloads.random_case(128, 1024, 256, seed=77, n_out=4, out_lo=20.0, out_hi=60.0)
+    exact = X.astype(np.float64) @ W.astype(np.float64)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    Ym = lm.llmint8_linear(Xd, Wq, s, Wd, 6.0)
+    Wqt, sw = lm.llmint8_quantize_tensorwise(Wd)
+    Yt = lm.llmint8_linear_tensorwise(Xd, Wqt, sw)
+    torch.cuda.synchronize()
+    err_m = np.abs(Ym.cpu().numpy().astype(np.float64) - exact).mean()
+    err_t = np.abs(Yt.cpu().numpy().astype(np.float64) - exact).mean()
+    assert err_t > 5 * err_m, (err_t, err_m)
