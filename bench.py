@@ -41,8 +41,8 @@ DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources that define the GEMM kernels (small-M and large-M)
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc", f)
-                  for f in ("common.hpp", "internal.hpp", "decode.hip", "gemm_core.hpp",
-                            "gemm.hip", "gemm_narrow.hip")]
+                  for f in ("common.hpp", "internal.hpp", "decode.hip", "decode_fused.hip",
+                            "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")]
 
 
 def kernel_source_digest() -> str:
@@ -79,14 +79,16 @@ def uses_compaction(M, K, n_out):
             and M * n_out * 16 > 5000 * (2 * K - n_out))
 
 
-def step_work(M, K, N, n_out, compacted):
+def step_work(M, K, N, n_out, compacted, int8w=False):
     """Algorithmic bytes and work of one layer call, and the algorithmic bytes of
     its GEMM kernel. The small-M GEMM kernel quantizes fp16 X itself and writes
     int32 sums, so its minimum traffic is Wq + X + C; the large-M kernel reads
     Xq, Wq (or their compacted copies), the scales and the outlier operands and
-    writes Y."""
+    writes Y. With int8 outlier weights the outlier rows come out of Wq, which
+    the call reads anyway, so the fp16 rows drop out of the call's bytes."""
     k_int8 = K - n_out
-    call_bytes = 2 * M * K + K * N + 4 * N + 2 * n_out * N + 2 * M * N
+    w_o = 0 if int8w else 2 * n_out * N
+    call_bytes = 2 * M * K + K * N + 4 * N + w_o + 2 * M * N
     if M <= DECODE_MAX_M:
         gemm_bytes = N * K + 2 * M * K + 4 * M * N
     else:
@@ -96,6 +98,39 @@ def step_work(M, K, N, n_out, compacted):
     int8_ops = 2 * M * N * k_int8
     fp16_flops = 2 * M * N * n_out
     return call_bytes, gemm_bytes, int8_ops, fp16_flops
+
+
+def accuracy(torch, lm, X_host, W_host, Xd, Wd, Wq, s, threshold, n_rows=16):
+    """Output error of each variant of the layer against the exact product X.W
+    (fp64) on sampled rows: mean absolute error (the per-layer error measure of
+    the Lightning Fabric page, section 3.12), its ratio to the mean |X.W|, and
+    the largest absolute error."""
+    import numpy as np
+
+    M = X_host.shape[0]
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(
+        M, size=min(n_rows, M), replace=False)]))
+    exact = X_host[rows].astype(np.float64) @ W_host.astype(np.float64)
+    scale = float(np.abs(exact).mean())
+    rt = torch.from_numpy(rows).to(Xd.device)
+    Wqt, sw = lm.llmint8_quantize_tensorwise(Wd)
+    variants = {
+        "llm_int8": lambda: lm.llmint8_linear(Xd, Wq, s, Wd, threshold),
+        "llm_int8_int8_weights": lambda: lm.llmint8_linear(Xd, Wq, s, None, threshold,
+                                                           outlier_weights="int8"),
+        "vector_wise_no_outliers": lambda: lm.llmint8_linear(Xd, Wq, s, None, math.inf),
+        "per_tensor": lambda: lm.llmint8_linear_tensorwise(Xd, Wqt, sw),
+    }
+    out = {"rows": int(rows.size), "reference": "fp64 X.W on the same rows",
+           "mean_abs_X_W": round(scale, 6)}
+    for name, run in variants.items():
+        y = run().index_select(0, rt).cpu().numpy().astype(np.float64)
+        err = np.abs(y - exact)
+        out[name] = {"mean_abs_err": float(f"{err.mean():.6g}"),
+                     "rel_mean_abs_err": float(f"{err.mean() / scale:.6g}"),
+                     "max_abs_err": float(f"{err.max():.6g}")}
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out):
@@ -140,6 +175,10 @@ def main():
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the output-error comparison of the layer's variants")
+    ap.add_argument("--outlier-weights", default="fp16", choices=("fp16", "int8"),
+                    help="fp16: outlier rows of the fp16 weight; int8: from Wq (no fp16 W kept)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
     args = ap.parse_args()
@@ -187,7 +226,9 @@ def main():
     colwise_ms = e0.elapsed_time(e1) / reps
     colwise_bytes = 3 * wl.K * wl.N + 4 * wl.N
 
-    sets = [(Wq0, s0, W0)] + [(Wq0.clone(), s0.clone(), W0.clone()) for _ in range(n_sets - 1)]
+    int8w = args.outlier_weights == "int8"
+    sets = [(Wq0, s0, None if int8w else W0)] + [
+        (Wq0.clone(), s0.clone(), None if int8w else W0.clone()) for _ in range(n_sets - 1)]
     Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
     ws = torch.empty((lm.llmint8_workspace_size(wl.M, wl.K, wl.N),), dtype=torch.uint8,
                      device=dev)
@@ -196,7 +237,7 @@ def main():
     def step(i, opts=None):
         Wq, s, W = sets[i % n_sets]
         lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
-                          outlier_count=cnt, opts=opts)
+                          outlier_count=cnt, opts=opts, outlier_weights=args.outlier_weights)
 
     for i in range(warmup):
         step(i)
@@ -268,7 +309,8 @@ def main():
 
     n_out = int(cnt.item())
     compacted = uses_compaction(wl.M, wl.K, n_out)
-    call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted)
+    call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted,
+                                                             int8w)
     if hbm_bound:
         value, unit = call_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -289,6 +331,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.description, "M": wl.M, "K": wl.K, "N": wl.N,
                    "threshold": threshold, "outlier_columns": n_out,
+                   "outlier_weights": args.outlier_weights,
                    "k_compacted": compacted, "weight_sets_cycled": n_sets,
                    "activation_pool": x_pool, "parallelism": "single GPU"},
         "roofline": roof,
@@ -305,6 +348,9 @@ def main():
         "quantize_colwise": {"ms": round(colwise_ms, 5), "algorithmic_bytes": colwise_bytes,
                              "GB_per_s": round(colwise_bytes / (colwise_ms * 1e-3) / 1e9, 2)},
     }
+    if not args.no_accuracy:
+        del graph
+        out["accuracy"] = accuracy(torch, lm, X_host[0], W_host, Xs[0], W0, Wq0, s0, threshold)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X_host[0], W_host, threshold, args.cpu_seconds,
                                            hbm_bound, n_out)

@@ -6,7 +6,9 @@ only the extern "C" entry points declared in include/llmint8.h are exported.
 from __future__ import annotations
 
 import glob
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -15,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libllmint8.so")
+# per-kernel register use, scratch and occupancy reported by the compiler
+RESOURCES = os.path.join(HERE, "libllmint8.kernels.json")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -22,7 +26,25 @@ FLAGS = [
     "-fvisibility=hidden", "-Wall",
     # packed fp32 instructions stay off for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|[A-Za-z ]+?)(?: \[[^\]]*\])?:\s+(\S+)\s+\[-Rpass")
+
+
+def kernel_resources(stderr: str) -> dict:
+    """{kernel symbol: {field: value}} from the kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val) if val.isdigit() else val
+    return out
 
 
 def sources():
@@ -34,13 +56,16 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "-Rpass-analysis=kernel-resource",
+             "remark:", "| ^", " | ")
+    err = "\n".join(l for l in proc.stderr.splitlines() if not any(n in l for n in noise))
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)
+    with open(RESOURCES, "w") as f:
+        json.dump(kernel_resources(proc.stderr), f, indent=1, sort_keys=True)
     return LIB
 
 

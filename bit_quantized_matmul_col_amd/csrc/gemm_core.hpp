@@ -302,7 +302,10 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   // Y = s / 127 * (C m / 127 + X_O q): the int8 part is scaled by m / 127
   // before the 16-bit MFMAs add X_O q, and s / 127 is applied last.
   const bool i8w = a.ep.int8w != 0;
-  for (int i = t; i < BM; i += TH) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : 0.f;
+  // Rows past M take a NaN row scale. Their values fall outside the Y resource
+  // when stored, and fmax ignores a NaN, so the column maxima skip them with no
+  // per-row test (per-element row masks would stay live across the store loop).
+  for (int i = t; i < BM; i += TH) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : __builtin_nanf("");
   for (int i = t; i < BN; i += TH) {
     const float sn = (n0 + i < a.N) ? a.s[n0 + i] : 0.f;
     ss[i] = i8w ? 1.0f / 127.0f : sn * (1.0f / 16129.0f);
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
         if (colok)
           __builtin_amdgcn_raw_buffer_store_b16(f2h(y), ry,
                                                 (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
-        cmax = (m0 + rl < a.M) ? __builtin_fmaxf(cmax, stored_abs(y)) : cmax;
+        cmax = __builtin_fmaxf(cmax, stored_abs(y));
       }
     }
     if (a.ep.ycmax) {
