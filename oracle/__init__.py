@@ -16,4 +16,11 @@ from .oracle import (  # noqa: F401
     linear_tensorwise,
     linear,
     linear_rows,
+    e4m3_encode,
+    e4m3_value,
+    quantize_colwise_fp8,
+    quantize_rowwise_fp8,
+    gemm_fp8,
+    merge_fp8,
+    linear_fp8,
 )

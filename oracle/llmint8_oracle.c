@@ -30,6 +30,10 @@
  *        need not be).
  *   [P5] also section 2 (the traditional 8-bit quantization uses one scale for
  *        the whole matrix).
+ *   [P4] "Model quantization in practice: INT8 vs FP8" (CSDN) sections 2 and 4
+ *        (FP8 E4M3: 4 exponent bits, 3 mantissa bits, largest value about 448;
+ *        an alternative to INT8 at the same 8-bit size; wide-ranged activations
+ *        need a scale before the cast).
  *
  * Readings taken where the pages are silent or disagree:
  *   - outlier test is |x| >= threshold (inclusive); a column is an outlier when
@@ -42,6 +46,12 @@
  *   - merge is a sum; the 16-bit product and the merge are evaluated in fp64
  *     here (the most exact reading of "fp32-accumulated"; the GPU's fp16 output
  *     is compared against it with a tolerance).
+ *   - FP8 variant: E4M3 as in the OCP 8-bit formats (bias 7, subnormals, no
+ *     infinities, 0x7f and 0xff are NaN, largest finite 448); the same absmax
+ *     scaling with 448 in place of 127: t = x * fl32(448 / absmax) in fp32,
+ *     then the nearest E4M3 value, ties to the even code, magnitudes above 448
+ *     saturating to 448; dequantization divides by 448^2; the fp8 matmul sums
+ *     the exact products in fp64.
  *
  * Build: gcc -O2 -ffp-contract=off -std=c11 -shared -fPIC (no fast-math).
  */
@@ -297,4 +307,151 @@ void ora_add_bias(double *Y, int64_t M, int64_t N, const uint16_t *bias)
     for (int64_t i = 0; i < M; ++i)
         for (int64_t n = 0; n < N; ++n)
             Y[i * N + n] += (double)ora_half(bias[n]);
+}
+
+/* ---- FP8 (E4M3) variant of the decomposition ([P4] sections 2 and 4) ---- */
+
+/* Value of an E4M3 code: sign, 4-bit exponent field e (bias 7), 3-bit mantissa
+ * field f. e = 0 is subnormal (f/8 * 2^-6); otherwise (1 + f/8) * 2^(e-7).
+ * e = 15, f = 7 is NaN (the format has no infinities). */
+double ora_e4m3_value(uint8_t c)
+{
+    unsigned e = (c >> 3) & 0xfu, f = c & 7u;
+    double v;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)f, -9);
+    else
+        v = ldexp((double)(8u + f), (int)e - 10);
+    return (c & 0x80u) ? -v : v;
+}
+
+/* Nearest E4M3 code to a finite fp32 value: the 127 non-negative finite codes
+ * 0x00 .. 0x7e are in increasing order of value, so a binary search brackets
+ * |t| between two neighbours; the nearer one wins and a tie goes to the even
+ * code (even mantissa). |t| above 448 gives 448. The sign is copied (so -0 and
+ * small negative values that round to zero give 0x80). */
+uint8_t ora_e4m3_encode(float t)
+{
+    double a = fabs((double)t);
+    uint8_t sign = signbit(t) ? 0x80u : 0u;
+    if (a >= 448.0)
+        return sign | 0x7eu;
+    unsigned lo = 0, hi = 0x7e; /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        unsigned mid = (lo + hi) / 2;
+        if (ora_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dlo = a - ora_e4m3_value((uint8_t)lo), dhi = ora_e4m3_value((uint8_t)hi) - a;
+    unsigned c = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1u) ? hi : lo);
+    return sign | (uint8_t)c;
+}
+
+void ora_e4m3_encode_array(const float *t, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ora_e4m3_encode(t[i]);
+}
+
+void ora_e4m3_value_array(const uint8_t *c, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ora_e4m3_value(c[i]);
+}
+
+/* The E4M3 code of x under absmax a: x * fl32(448 / a) in fp32, then encoded;
+ * a = 0 gives code 0. */
+static uint8_t ora_quant_fp8(float x, float a)
+{
+    if (!(a > 0.0f))
+        return 0;
+    float inv = 448.0f / a;
+    float t = x * inv;
+    return ora_e4m3_encode(t);
+}
+
+/* Weight side of the FP8 variant: s[n] = max_k |W[k, n]| over all K rows;
+ * Wq8 [N x K] holds the E4M3 codes of W[k, n] under s[n]. */
+void ora_quantize_colwise_fp8(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                              uint8_t *Wq8, float *s)
+{
+    for (int64_t n = 0; n < N; ++n)
+        s[n] = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            float a = fabsf(ora_half(W[k * ldw + n]));
+            if (a > s[n])
+                s[n] = a;
+        }
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Wq8[n * K + k] = ora_quant_fp8(ora_half(W[k * ldw + n]), s[n]);
+}
+
+/* Activation side of the FP8 variant: m[i] = max over non-outlier k of
+ * |X[i, k]|; Xq8 [M x K] holds the E4M3 codes under m[i], 0 on outlier
+ * columns. */
+void ora_quantize_rowwise_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                              const int32_t *idx, int32_t count, uint8_t *Xq8, float *m)
+{
+    unsigned char *is_out = calloc((size_t)(K > 0 ? K : 1), 1);
+    for (int32_t p = 0; p < count; ++p)
+        is_out[idx[p]] = 1;
+    for (int64_t i = 0; i < M; ++i) {
+        float mi = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(ora_half(X[i * ldx + k]));
+            if (!is_out[k] && a > mi)
+                mi = a;
+        }
+        m[i] = mi;
+        for (int64_t k = 0; k < K; ++k)
+            Xq8[i * K + k] = is_out[k] ? 0 : ora_quant_fp8(ora_half(X[i * ldx + k]), mi);
+    }
+    free(is_out);
+}
+
+/* The fp8 matmul: C[i, n] = sum_k value(Xq8[i, k]) * value(Wq8[n, k]) in fp64
+ * (every product is exact), ascending k. */
+void ora_gemm_fp8(const uint8_t *Xq8, const uint8_t *Wq8, int64_t M, int64_t N, int64_t K,
+                  double *C)
+{
+    double *xv = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t k = 0; k < K; ++k)
+            xv[k] = ora_e4m3_value(Xq8[i * K + k]);
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += xv[k] * ora_e4m3_value(Wq8[n * K + k]);
+            C[i * N + n] = acc;
+        }
+    }
+    free(xv);
+}
+
+/* Merge of the FP8 variant: Y[i, n] = C[i, n] * m[i] * s[n] / 448^2 + the
+ * 16-bit outlier product over the fp16 rows of W (as ora_merge), fp64. */
+void ora_merge_fp8(const double *C, const float *m, const float *s,
+                   const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                   const int32_t *idx, int32_t count, int64_t M, int64_t N, double *Y)
+{
+    double *yo = malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t n = 0; n < N; ++n)
+            yo[n] = 0.0;
+        for (int32_t p = 0; p < count; ++p) {
+            int64_t k = idx[p];
+            double x = (double)ora_half(X[i * ldx + k]);
+            for (int64_t n = 0; n < N; ++n)
+                yo[n] += x * (double)ora_half(W[k * ldw + n]);
+        }
+        for (int64_t n = 0; n < N; ++n)
+            Y[i * N + n] = C[i * N + n] * (double)m[i] * (double)s[n] / 200704.0 + yo[n];
+    }
+    free(yo);
 }

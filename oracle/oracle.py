@@ -46,6 +46,18 @@ def _load():
         lib.ora_linear_tensorwise.restype = C.c_float
         lib.ora_add_bias.argtypes = [p, i64, i64, p]
         lib.ora_add_bias.restype = None
+        lib.ora_e4m3_encode_array.argtypes = [p, i64, p]
+        lib.ora_e4m3_encode_array.restype = None
+        lib.ora_e4m3_value_array.argtypes = [p, i64, p]
+        lib.ora_e4m3_value_array.restype = None
+        lib.ora_quantize_colwise_fp8.argtypes = [p, i64, i64, i64, p, p]
+        lib.ora_quantize_colwise_fp8.restype = None
+        lib.ora_quantize_rowwise_fp8.argtypes = [p, i64, i64, i64, p, C.c_int32, p, p]
+        lib.ora_quantize_rowwise_fp8.restype = None
+        lib.ora_gemm_fp8.argtypes = [p, p, i64, i64, i64, p]
+        lib.ora_gemm_fp8.restype = None
+        lib.ora_merge_fp8.argtypes = [p, p, p, p, i64, p, i64, p, C.c_int32, i64, i64, p]
+        lib.ora_merge_fp8.restype = None
         _lib = lib
     return _lib
 
@@ -223,3 +235,86 @@ def linear_rows(X: np.ndarray, W: np.ndarray, threshold: float, rows, Wq=None, s
     if bias is not None:
         Y = add_bias(Y, bias)
     return dict(rows=rows, idx=idx, Xq=Xq, m=m, Wq=Wq, s=s, C=Cm, Y=Y)
+
+
+# ---- FP8 (E4M3) variant --------------------------------------------------------------
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    """fp32 values -> nearest E4M3 codes (uint8), ties to even, |t| > 448 -> 448."""
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(t.shape, np.uint8)
+    _load().ora_e4m3_encode_array(_ptr(t), t.size, _ptr(out))
+    return out
+
+
+def e4m3_value(c: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> their values (float64; NaN for 0x7f / 0xff)."""
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().ora_e4m3_value_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize_colwise_fp8(W: np.ndarray):
+    """W fp16 [K, N] -> (Wq8 uint8 E4M3 codes [N, K], s float32 [N])."""
+    W = _bits(W)
+    K, N = W.shape
+    Wq = np.empty((N, K), np.uint8)
+    s = np.empty(N, np.float32)
+    _load().ora_quantize_colwise_fp8(_ptr(W), K, N, N, _ptr(Wq), _ptr(s))
+    return Wq, s
+
+
+def quantize_rowwise_fp8(X: np.ndarray, idx: np.ndarray | None = None):
+    """X fp16 [M, K], outlier columns -> (Xq8 uint8 E4M3 codes [M, K], m float32 [M])."""
+    X = _bits(X)
+    M, K = X.shape
+    idx = np.ascontiguousarray(np.zeros(0, np.int32) if idx is None else idx, dtype=np.int32)
+    Xq = np.empty((M, K), np.uint8)
+    m = np.empty(M, np.float32)
+    _load().ora_quantize_rowwise_fp8(_ptr(X), M, K, K, _ptr(idx), int(idx.size), _ptr(Xq),
+                                     _ptr(m))
+    return Xq, m
+
+
+def gemm_fp8(Xq8: np.ndarray, Wq8: np.ndarray) -> np.ndarray:
+    """E4M3 codes Xq8 [M, K] and Wq8 [N, K] -> C float64 [M, N] (exact products)."""
+    Xq8 = np.ascontiguousarray(Xq8, dtype=np.uint8)
+    Wq8 = np.ascontiguousarray(Wq8, dtype=np.uint8)
+    M, K = Xq8.shape
+    N, K2 = Wq8.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    Cm = np.empty((M, N), np.float64)
+    _load().ora_gemm_fp8(_ptr(Xq8), _ptr(Wq8), M, N, K, _ptr(Cm))
+    return Cm
+
+
+def merge_fp8(Cm, m, s, X, W, idx) -> np.ndarray:
+    """Y = C m s / 448^2 + the fp16 outlier product -> float64 [M, N]."""
+    X = _bits(X)
+    W = _bits(W)
+    Cm = np.ascontiguousarray(Cm, dtype=np.float64)
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    M, N = Cm.shape
+    Y = np.empty((M, N), np.float64)
+    _load().ora_merge_fp8(_ptr(Cm), _ptr(m), _ptr(s), _ptr(X), X.shape[1], _ptr(W), W.shape[1],
+                          _ptr(idx), int(idx.size), M, N, _ptr(Y))
+    return Y
+
+
+def linear_fp8(X: np.ndarray, W: np.ndarray, threshold: float, Wq8=None, s=None,
+               rows=None) -> dict:
+    """The FP8 variant of the layer: the same outlier split, E4M3 codes with
+    absmax scaling to 448 for the rest. With `rows`, results for those rows of X
+    only (the outlier set is still found on all of X)."""
+    if Wq8 is None or s is None:
+        Wq8, s = quantize_colwise_fp8(W)
+    idx = find_outliers(X, threshold)
+    Xs = _bits(X) if rows is None else np.ascontiguousarray(_bits(X)[np.asarray(rows)])
+    Xq8, m = quantize_rowwise_fp8(Xs, idx)
+    Cm = gemm_fp8(Xq8, Wq8)
+    Y = merge_fp8(Cm, m, s, Xs, W, idx)
+    return dict(idx=idx, Xq=Xq8, m=m, Wq=Wq8, s=s, C=Cm, Y=Y)

@@ -387,3 +387,156 @@ def test_bias_is_added_after_the_rescale():
     a = oracle.linear_tensorwise(X, Wq, sw)
     c = oracle.linear_tensorwise(X, Wq, sw, bias=b)
     assert np.array_equal(c["Y"], a["Y"] + b.astype(np.float64)[None, :])
+
+
+# --- FP8 (E4M3) variant ------------------------------------------------------------
+# The INT8/FP8 page (CSDN, sections 2 and 4): E4M3 has 4 exponent bits and 3
+# mantissa bits, its largest value is about 448, and wide-ranged activations
+# need a scale before the cast.
+
+def test_e4m3_format_facts():
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_value(codes)
+    assert v[0x7E] == 448.0 and np.nanmax(v) == 448.0  # largest finite value
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2  # no infinities
+    assert v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6 and v[0x38] == 1.0
+    assert v[0x00] == 0.0 and math.copysign(1.0, v[0x80]) == -1.0
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)  # codes 0x00..0x7e ascend with their value
+    assert np.array_equal(v[0x80:0xFF], -pos)  # the sign bit negates
+    # 3 mantissa bits: 8 values per binade above the subnormals
+    assert np.sum((pos >= 1.0) & (pos < 2.0)) == 8
+
+
+def _torch_e4m3(t):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(t, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encoding_matches_torch_cast():
+    # in range the encoder must agree bit for bit with PyTorch's own cast to
+    # float8_e4m3fn (round to nearest, ties to even), including every exact
+    # midpoint between neighbouring codes
+    rng = np.random.default_rng(3)
+    mag = np.exp2(rng.uniform(-13.0, np.log2(448.0), 200000)).astype(np.float32)
+    t = mag * rng.choice(np.float32([-1.0, 1.0]), mag.size)
+    pos = oracle.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[1:] + pos[:-1]) / 2)  # exact in fp32
+    t = np.concatenate([t, mids, -mids, pos.astype(np.float32), np.float32([0.0, -0.0])])
+    assert np.array_equal(oracle.e4m3_encode(t), _torch_e4m3(t))
+
+
+def test_e4m3_saturates_above_448():
+    t = np.float32([448.0, 449.0, 463.9, 464.0, 480.0, 1e6, -500.0])
+    assert oracle.e4m3_encode(t).tolist() == [0x7E] * 6 + [0xFE]
+
+
+def test_fp8_quantizer_brute_force():
+    pos = oracle.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    rng = np.random.default_rng(12)
+    for trial in range(30):
+        K = int(rng.integers(1, 20))
+        x = (rng.standard_normal(K) * rng.choice([0.001, 1.0, 30.0])).astype(np.float16)
+        Xq, m = oracle.quantize_rowwise_fp8(x[None, :], None)
+        amax = np.float32(np.abs(x.astype(np.float32)).max())
+        assert m[0] == amax
+        if amax == 0:
+            assert not Xq.any()
+            continue
+        inv = np.float32(448.0) / amax
+        for k in range(K):
+            t = float(np.float32(x[k]) * inv)
+            d = np.abs(pos - abs(t))
+            best = np.flatnonzero(d == d.min())
+            code = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+            assert Xq[0, k] == (code | (0x80 if np.signbit(np.float32(t)) else 0))
+
+
+def _exact_fp8_case(rng, M, K, N):
+    """X, W whose every non-outlier entry is an E4M3 value times a power of two
+    set by its row (X) or column (W) absmax of 448 * 2^-r, so both quantizations
+    are exact."""
+    vals = oracle.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    vals = vals[vals >= 2.0 ** -6]  # normal values (exact in fp16 after the shift)
+
+    def draw(rows, cols, axis):
+        a = rng.choice(vals, size=(rows, cols)) * rng.choice([-1.0, 1.0], size=(rows, cols))
+        if axis == 1:
+            a[np.arange(rows), rng.integers(cols, size=rows)] = 448.0
+            return a * np.exp2(-rng.integers(0, 6, size=(rows, 1)))
+        a[rng.integers(rows, size=cols), np.arange(cols)] = -448.0
+        return a * np.exp2(-rng.integers(4, 10, size=(1, cols)))
+
+    Xd, Wd = draw(M, K, 1), draw(K, N, 0)
+    X, W = Xd.astype(np.float16), Wd.astype(np.float16)
+    assert np.array_equal(X.astype(np.float64), Xd) and np.array_equal(W.astype(np.float64), Wd)
+    return X, W
+
+
+def test_fp8_exact_codes_reduce_to_matmul():
+    rng = np.random.default_rng(21)
+    X, W = _exact_fp8_case(rng, 9, 40, 12)
+    ref = oracle.linear_fp8(X, W, math.inf)
+    exact = X.astype(np.float64) @ W.astype(np.float64)
+    assert np.allclose(ref["Y"], exact, rtol=1e-12, atol=1e-12)
+    # and the codes decode to the scaled inputs exactly
+    deq = oracle.e4m3_value(ref["Xq"]) * ref["m"][:, None] / 448.0
+    assert np.array_equal(deq, X.astype(np.float64))
+
+
+def test_fp8_all_outlier_columns_reduce_to_fp16_matmul():
+    X, W, _ = workloads.random_case(11, 64, 24, seed=8, n_out=2)
+    ref = oracle.linear_fp8(X, W, 0.0)
+    assert ref["idx"].size == 64 and not ref["Xq"].any() and not ref["m"].any()
+    assert np.allclose(ref["Y"], X.astype(np.float64) @ W.astype(np.float64), rtol=1e-12,
+                       atol=1e-12)
+
+
+def test_fp8_reconstruction_error_bound():
+    # |t - e4m3(t)| <= max(|t| 2^-4, 2^-10) for t = x * 448 / m (half a step of
+    # 3 mantissa bits; subnormal steps are 2^-9), back in x units times m / 448,
+    # plus the fp32 roundings inside x * fl(448 / m)
+    X, _, _ = workloads.random_case(64, 512, 8, seed=15, n_out=5)
+    idx = oracle.find_outliers(X, 6.0)
+    Xq, m = oracle.quantize_rowwise_fp8(X, idx)
+    keep = np.ones(X.shape[1], bool)
+    keep[idx] = False
+    xf = X.astype(np.float64)
+    md = m.astype(np.float64)[:, None]
+    err = np.abs(xf - oracle.e4m3_value(Xq) * md / 448.0)[:, keep]
+    bound = (np.maximum(np.abs(xf) * 2.0 ** -4, md / 448.0 * 2.0 ** -10) * (1 + 2.0 ** -20)
+             + np.abs(xf) * 2.0 ** -22)[:, keep]
+    assert np.all(err <= bound)
+    assert np.all(Xq[:, idx] == 0)
+
+
+def test_fp8_layer_brute_force_against_torch_encoding():
+    # an independent implementation of the FP8 layer: numpy arithmetic with
+    # PyTorch's float8_e4m3fn cast as the encoder
+    import torch
+    X, W, _ = workloads.random_case(13, 48, 20, seed=31, n_out=3)
+    thr = 6.0
+    xf, wf = X.astype(np.float32), W.astype(np.float32)
+    out = np.flatnonzero((np.abs(xf) >= thr).any(axis=0))
+    keep = np.setdiff1d(np.arange(48), out)
+    m = np.abs(xf[:, keep]).max(axis=1)
+    s = np.abs(wf).max(axis=0)
+    xs = (xf * (np.float32(448.0) / m)[:, None]).astype(np.float32)
+    xs[:, out] = 0.0
+    ws = (wf * (np.float32(448.0) / s)[None, :]).astype(np.float32)
+    xc, wc = _torch_e4m3(xs), _torch_e4m3(ws.T)
+
+    def dec(c):
+        return torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    Cm = dec(xc) @ dec(wc).T
+    Y = Cm * m[:, None].astype(np.float64) * s[None, :].astype(np.float64) / 448.0 ** 2 \
+        + X[:, out].astype(np.float64) @ W[out].astype(np.float64)
+    ref = oracle.linear_fp8(X, W, thr)
+    assert ref["idx"].tolist() == out.tolist()
+    assert np.array_equal(ref["Xq"], xc) and np.array_equal(ref["Wq"], wc)
+    assert np.array_equal(ref["m"], m) and np.array_equal(ref["s"], s)
+    assert np.allclose(ref["C"], Cm, rtol=1e-13, atol=1e-9)
+    assert np.allclose(ref["Y"], Y, rtol=1e-12, atol=1e-12)
