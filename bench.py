@@ -53,10 +53,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, variant: str = "int8"):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
     or None when it is missing or was taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"gemm_{workload}_hbm_counters.txt")
+    tag = workload if variant == "int8" else f"{variant}_{workload}"
+    path = os.path.join(PROFILES, f"gemm_{tag}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -73,13 +74,15 @@ def read_traffic(workload: str):
         return None
 
 
-def uses_compaction(M, K, n_out):
-    """The library's rule for running the int8 GEMM on the K - |O| kept columns."""
-    return (M > DECODE_MAX_M and n_out > 0 and K <= 32768
+def uses_compaction(M, K, n_out, any_m=False):
+    """The library's rule for running the 8-bit GEMM on the K - |O| kept columns
+    (the small-M int8 path never compacts; the FP8 layer runs the large-M
+    kernels at every M)."""
+    return ((any_m or M > DECODE_MAX_M) and n_out > 0 and K <= 32768
             and M * n_out * 16 > 5000 * (2 * K - n_out))
 
 
-def step_work(M, K, N, n_out, compacted, int8w=False):
+def step_work(M, K, N, n_out, compacted, int8w=False, large_m=False):
     """Algorithmic bytes and work of one layer call, and the algorithmic bytes of
     its GEMM kernel. The small-M GEMM kernel quantizes fp16 X itself and writes
     int32 sums, so its minimum traffic is Wq + X + C; the large-M kernel reads
@@ -89,7 +92,7 @@ def step_work(M, K, N, n_out, compacted, int8w=False):
     k_int8 = K - n_out
     w_o = 0 if int8w else 2 * n_out * N
     call_bytes = 2 * M * K + K * N + 4 * N + w_o + 2 * M * N
-    if M <= DECODE_MAX_M:
+    if M <= DECODE_MAX_M and not large_m:
         gemm_bytes = N * K + 2 * M * K + 4 * M * N
     else:
         k_loop = k_int8 if compacted else K
@@ -100,7 +103,7 @@ def step_work(M, K, N, n_out, compacted, int8w=False):
     return call_bytes, gemm_bytes, int8_ops, fp16_flops
 
 
-def accuracy(torch, lm, X_host, W_host, Xd, Wd, Wq, s, threshold, n_rows=16):
+def accuracy(torch, lm, X_host, W_host, Xd, Wd, threshold, n_rows=16):
     """Output error of each variant of the layer against the exact product X.W
     (fp64) on sampled rows: mean absolute error (the per-layer error measure of
     the Lightning Fabric page, section 3.12), its ratio to the mean |X.W|, and
@@ -113,13 +116,16 @@ def accuracy(torch, lm, X_host, W_host, Xd, Wd, Wq, s, threshold, n_rows=16):
     exact = X_host[rows].astype(np.float64) @ W_host.astype(np.float64)
     scale = float(np.abs(exact).mean())
     rt = torch.from_numpy(rows).to(Xd.device)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
     Wqt, sw = lm.llmint8_quantize_tensorwise(Wd)
+    Wq8, s8 = lm.llmint8_quantize_colwise_fp8(Wd)
     variants = {
         "llm_int8": lambda: lm.llmint8_linear(Xd, Wq, s, Wd, threshold),
         "llm_int8_int8_weights": lambda: lm.llmint8_linear(Xd, Wq, s, None, threshold,
                                                            outlier_weights="int8"),
         "vector_wise_no_outliers": lambda: lm.llmint8_linear(Xd, Wq, s, None, math.inf),
         "per_tensor": lambda: lm.llmint8_linear_tensorwise(Xd, Wqt, sw),
+        "fp8_e4m3_decomposition": lambda: lm.llmint8_linear_fp8(Xd, Wq8, s8, Wd, threshold),
     }
     out = {"rows": int(rows.size), "reference": "fp64 X.W on the same rows",
            "mean_abs_X_W": round(scale, 6)}
@@ -133,13 +139,22 @@ def accuracy(torch, lm, X_host, W_host, Xd, Wd, Wq, s, threshold, n_rows=16):
     return out
 
 
-def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out):
+def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8=False):
     """The oracle as it stands, single-threaded, on a bounded sample. Its weight
     quantization (load time, like the GPU's) is done first and not timed."""
     import numpy as np
     import oracle
 
-    Wq, s = oracle.quantize_colwise(W)
+    if fp8:
+        Wq8, s8 = oracle.quantize_colwise_fp8(W)
+
+        def layer(rows):
+            return oracle.linear_fp8(X, W, threshold, Wq8=Wq8, s=s8, rows=rows)
+    else:
+        Wq, s = oracle.quantize_colwise(W)
+
+        def layer(rows):
+            return oracle.linear_rows(X, W, threshold, rows, Wq=Wq, s=s)
     rows = wl.M
     if not hbm_bound:
         rows = 4
@@ -147,12 +162,12 @@ def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out):
     reps, elapsed = 0, 0.0
     while reps == 0 or (elapsed < budget_s and reps < 50):
         t0 = time.perf_counter()
-        oracle.linear_rows(X, W, threshold, sample_rows, Wq=Wq, s=s)
+        layer(sample_rows)
         elapsed += time.perf_counter() - t0
         reps += 1
     per = elapsed / reps
     if hbm_bound:
-        call_bytes = step_work(wl.M, wl.K, wl.N, n_out, False)[0]
+        call_bytes = step_work(wl.M, wl.K, wl.N, n_out, False, large_m=fp8)[0]
         value, unit = call_bytes / per / 1e9, "GB/s"
         sample = f"{reps} whole layer calls on the {wl.M}x{wl.K}x{wl.N} workload"
     else:
@@ -177,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true",
                     help="skip the output-error comparison of the layer's variants")
+    ap.add_argument("--variant", default="int8", choices=("int8", "fp8"),
+                    help="int8: the LLM.int8() layer; fp8: its E4M3 variant")
     ap.add_argument("--outlier-weights", default="fp16", choices=("fp16", "int8"),
                     help="fp16: outlier rows of the fp16 weight; int8: from Wq (no fp16 W kept)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -213,14 +230,18 @@ def main():
         [workloads.make_x(wl)]
     Xs = [torch.from_numpy(X_host[c % len(X_host)]).to(dev) for c in range(x_pool)]
 
+    fp8 = args.variant == "fp8"
+    if fp8 and args.outlier_weights != "fp16":
+        sys.exit("the FP8 layer takes its outlier rows from the fp16 weight")
+    quantize = lm.llmint8_quantize_colwise_fp8 if fp8 else lm.llmint8_quantize_colwise
     # load-time weight quantization, timed on its own
-    Wq0, s0 = lm.llmint8_quantize_colwise(W0)
+    Wq0, s0 = quantize(W0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
     e0.record()
     for _ in range(reps):
-        lm.llmint8_quantize_colwise(W0)
+        quantize(W0)
     e1.record()
     torch.cuda.synchronize()
     colwise_ms = e0.elapsed_time(e1) / reps
@@ -230,14 +251,18 @@ def main():
     sets = [(Wq0, s0, None if int8w else W0)] + [
         (Wq0.clone(), s0.clone(), None if int8w else W0.clone()) for _ in range(n_sets - 1)]
     Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
-    ws = torch.empty((lm.llmint8_workspace_size(wl.M, wl.K, wl.N),), dtype=torch.uint8,
-                     device=dev)
+    ws_size = (lm.llmint8_linear_fp8_workspace_size if fp8 else lm.llmint8_workspace_size)
+    ws = torch.empty((ws_size(wl.M, wl.K, wl.N),), dtype=torch.uint8, device=dev)
     cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
 
     def step(i, opts=None):
         Wq, s, W = sets[i % n_sets]
-        lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
-                          outlier_count=cnt, opts=opts, outlier_weights=args.outlier_weights)
+        if fp8:
+            lm.llmint8_linear_fp8(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
+                                  outlier_count=cnt, opts=opts)
+        else:
+            lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
+                              outlier_count=cnt, opts=opts, outlier_weights=args.outlier_weights)
 
     for i in range(warmup):
         step(i)
@@ -308,9 +333,9 @@ def main():
         torch.cuda.synchronize()
 
     n_out = int(cnt.item())
-    compacted = uses_compaction(wl.M, wl.K, n_out)
+    compacted = uses_compaction(wl.M, wl.K, n_out, any_m=fp8)
     call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted,
-                                                             int8w)
+                                                             int8w, large_m=fp8)
     if hbm_bound:
         value, unit = call_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -322,15 +347,17 @@ def main():
         achieved = (int8_ops + 2 * fp16_flops) / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof["traffic"] = read_traffic(args.workload)
+    roof["traffic"] = read_traffic(args.workload, args.variant)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3" if fp8 else "i8",
         "data": "synthetic",
         "config": {"workload": wl.description, "M": wl.M, "K": wl.K, "N": wl.N,
                    "threshold": threshold, "outlier_columns": n_out,
+                   "variant": "fp8 (E4M3) decomposition" if fp8 else "LLM.int8()",
                    "outlier_weights": args.outlier_weights,
                    "k_compacted": compacted, "weight_sets_cycled": n_sets,
                    "activation_pool": x_pool, "parallelism": "single GPU"},
@@ -350,10 +377,10 @@ def main():
     }
     if not args.no_accuracy:
         del graph
-        out["accuracy"] = accuracy(torch, lm, X_host[0], W_host, Xs[0], W0, Wq0, s0, threshold)
+        out["accuracy"] = accuracy(torch, lm, X_host[0], W_host, Xs[0], W0, threshold)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, X_host[0], W_host, threshold, args.cpu_seconds,
-                                           hbm_bound, n_out)
+                                           hbm_bound, n_out, fp8)
     print(json.dumps(out), flush=True)
 
 

@@ -77,11 +77,18 @@ def lib() -> C.CDLL:
         L.llmint8_linear_tensorwise_workspace_size.restype = sz
         L.llmint8_linear_tensorwise.argtypes = [p, i64, i64, i64, p, p, i64, p, p, i64, p, p, p,
                                                 sz, p]
+        L.llmint8_quantize_colwise_fp8.argtypes = [p, i64, i64, i64, p, p, p]
+        L.llmint8_quantize_rowwise_fp8.argtypes = [p, i64, i64, i64, p, p, p, p, p]
+        L.llmint8_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
+        L.llmint8_linear_fp8_workspace_size.restype = sz
+        L.llmint8_linear_fp8.argtypes = L.llmint8_linear_ex.argtypes
         L.llmint8_status_string.argtypes = [C.c_int]
         L.llmint8_status_string.restype = C.c_char_p
         for name in ("llmint8_quantize_colwise", "llmint8_find_outliers",
                      "llmint8_quantize_rowwise", "llmint8_linear", "llmint8_linear_ex",
-                     "llmint8_quantize_tensorwise", "llmint8_linear_tensorwise"):
+                     "llmint8_quantize_tensorwise", "llmint8_linear_tensorwise",
+                     "llmint8_quantize_colwise_fp8", "llmint8_quantize_rowwise_fp8",
+                     "llmint8_linear_fp8"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -116,9 +123,10 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
 
 
 def _ld(t: torch.Tensor, name: str) -> int:
-    if t.stride(1) != 1:
+    if t.stride(1) != 1 and t.shape[1] > 1:
         raise ValueError(f"{name} must have unit stride along its last dimension")
-    return t.stride(0)
+    # a single row has no meaningful row stride (numpy and torch may report 0)
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def llmint8_quantize_colwise(W: torch.Tensor):
@@ -291,4 +299,92 @@ def llmint8_linear_tensorwise(X: torch.Tensor, Wq: torch.Tensor, w_absmax: torch
         _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(w_absmax), N, _ptr(bias), _ptr(Y),
         _ld(Y, "Y"), _ptr(x_absmax), _ptr(C_debug), _ptr(workspace), workspace.numel(),
         _stream(X)))
+    return Y
+
+
+# ---- FP8 (E4M3) variant --------------------------------------------------------------
+
+def llmint8_quantize_colwise_fp8(W: torch.Tensor):
+    """fp16 W [K, N] -> (Wq8 uint8 E4M3 codes [N, K], col_absmax fp32 [N])."""
+    _need(W, "W", torch.float16, 2)
+    K, N = W.shape
+    Wq = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    s = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib().llmint8_quantize_colwise_fp8(_ptr(W), K, N, _ld(W, "W"), _ptr(Wq), _ptr(s),
+                                              _stream(W)))
+    return Wq, s
+
+
+def llmint8_quantize_rowwise_fp8(X: torch.Tensor, idx: torch.Tensor | None = None,
+                                 count: torch.Tensor | None = None):
+    """fp16 X [M, K] (+ outlier idx/count) -> (Xq8 uint8 E4M3 codes [M, K], row_absmax [M])."""
+    _need(X, "X", torch.float16, 2)
+    if (idx is None) != (count is None):
+        raise ValueError("idx and count go together")
+    if idx is not None:
+        _need(idx, "idx", torch.int32, 1)
+        _need(count, "count", torch.int32, 1)
+    M, K = X.shape
+    Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    m = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().llmint8_quantize_rowwise_fp8(_ptr(X), M, K, _ld(X, "X"), _ptr(idx), _ptr(count),
+                                              _ptr(Xq), _ptr(m), _stream(X)))
+    return Xq, m
+
+
+def llmint8_linear_fp8_workspace_size(M: int, K: int, N: int) -> int:
+    return int(lib().llmint8_linear_fp8_workspace_size(M, K, N))
+
+
+def llmint8_linear_fp8(X: torch.Tensor, Wq8: torch.Tensor, col_absmax: torch.Tensor,
+                       W: torch.Tensor | None, threshold: float = 6.0, *, Y=None, workspace=None,
+                       outlier_count: torch.Tensor | None = None,
+                       C_debug: torch.Tensor | None = None, opts: LinearOpts | None = None,
+                       bias: torch.Tensor | None = None,
+                       y_col_absmax: torch.Tensor | None = None,
+                       x_col_absmax: torch.Tensor | None = None) -> torch.Tensor:
+    """The FP8 (E4M3) variant of the layer: fp16 X [M, K] with Wq8 [N, K] and col_absmax
+    from llmint8_quantize_colwise_fp8 and the fp16 weight W [K, N] -> fp16 Y [M, N].
+    C_debug, if given, is an fp32 [M, N] tensor receiving the 8-bit product."""
+    _need(X, "X", torch.float16, 2)
+    _need(Wq8, "Wq8", torch.uint8, 2)
+    _need(col_absmax, "col_absmax", torch.float32, 1)
+    M, K = X.shape
+    N = Wq8.shape[0]
+    if Wq8.shape[1] != K or not Wq8.is_contiguous():
+        raise ValueError("Wq8 must be contiguous [N, K]")
+    if W is not None:
+        _need(W, "W", torch.float16, 2)
+        if tuple(W.shape) != (K, N):
+            raise ValueError("W must be [K, N]")
+    elif not (math.isinf(threshold) and threshold > 0):
+        raise ValueError("W may be omitted only with threshold=+inf")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if outlier_count is not None:
+        _need(outlier_count, "outlier_count", torch.int32)
+    if C_debug is not None:
+        _need(C_debug, "C_debug", torch.float32)
+    for name, t, dt, n in (("bias", bias, torch.float16, N),
+                           ("y_col_absmax", y_col_absmax, torch.float32, N),
+                           ("x_col_absmax", x_col_absmax, torch.float32, K)):
+        if t is not None:
+            _need(t, name, dt, 1)
+            if t.numel() != n or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous vector of {n}")
+    if workspace is None:
+        workspace = torch.empty((llmint8_linear_fp8_workspace_size(M, K, N),), dtype=torch.uint8,
+                                device=X.device)
+    o = LinearOpts(gemm_begin_event=opts.gemm_begin_event if opts else None,
+                   gemm_end_event=opts.gemm_end_event if opts else None,
+                   outlier_weights=LLMINT8_OUTLIER_W_FP16,
+                   bias=bias.data_ptr() if bias is not None else None,
+                   y_col_absmax=y_col_absmax.data_ptr() if y_col_absmax is not None else None,
+                   x_col_absmax=x_col_absmax.data_ptr() if x_col_absmax is not None else None)
+    _check(lib().llmint8_linear_fp8(
+        _ptr(X), M, K, _ld(X, "X"), _ptr(Wq8), _ptr(col_absmax), _ptr(W),
+        _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
+        _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X),
+        C.byref(o)))
     return Y

@@ -45,8 +45,8 @@ Layout make_decode_layout(int64_t M, int64_t K, int64_t N) {
   return L;
 }
 
-Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer) {
-  if (layer && M <= kDecodeMaxM) return make_decode_layout(M, K, N);
+Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefill = false) {
+  if (layer && M <= kDecodeMaxM && !any_m_prefill) return make_decode_layout(M, K, N);
   const DetectPlan p = detect_plan(M, K);
   Layout L{};
   size_t o = 0;
@@ -118,6 +118,49 @@ uint32_t fp16_threshold_bits(float threshold) {
   return lo;
 }
 
+// The large-M layer sequence: detection, row quantization with the outlier
+// gather, K-compaction when it pays, the W_O^T gather and the GEMM with the
+// fused epilogue. fp8 selects E4M3 codes for Xq and Wq.
+hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, const int8_t *Wq,
+                         const float *col_absmax, const uint16_t *Wf, int64_t ldw, int64_t N,
+                         float threshold, uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
+                         int32_t *C_debug, uint8_t *ws, const Layout &L,
+                         const llmint8_linear_opts &o, const GemmEvents &ev,
+                         const EpilogueOpts &ep, bool fp8, hipStream_t s) {
+  const DetectPlan plan = detect_plan(M, K);
+  uint32_t *omask = (uint32_t *)(ws + L.omask);
+  int32_t *wprefix = (int32_t *)(ws + L.wprefix);
+  int32_t *idx = (int32_t *)(ws + L.idx);
+  int32_t *count = (int32_t *)(ws + L.count);
+  int8_t *xq = (int8_t *)(ws + L.xq);
+  float *m = (float *)(ws + L.m);
+  uint16_t *xo = (uint16_t *)(ws + L.xo);
+  int8_t *wqc = (int8_t *)(ws + L.wqc);
+  const bool int8w = ep.int8w != 0;
+
+  DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
+              wprefix, idx, (int32_t *)(ws + L.nidx), count, outlier_count_out};
+  const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
+  uint16_t *wot = (uint16_t *)(ws + L.wot);
+  hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
+  if (e == hipSuccess)
+    e = fp8 ? launch_rowquant_layer<CodecE4M3>(X, M, K, ldx, omask, wprefix, count,
+                                               (uint8_t *)xq, ldq, m, xo, ldo, s)
+            : launch_rowquant_layer<CodecI8>(X, M, K, ldx, omask, wprefix, count, (uint8_t *)xq,
+                                             ldq, m, xo, ldo, s);
+  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, ldq, s);
+  if (e == hipSuccess && (Wf || int8w))
+    e = launch_gather_wot(Wf, ldw, Wq, K, N, idx, count, wot, ldo, s);
+  if (e == hipSuccess) {
+    // the GEMM's outlier product runs when it has weight rows (gathered above)
+    const uint16_t *wo_src = (Wf || int8w) ? wot : nullptr;
+    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, wo_src ? (const uint16_t *)wot : nullptr,
+               count, Y, C_debug, M, N, K, ldq, ldo, ldw, ldy, ep, fp8 ? 1 : 0};
+    e = launch_gemm(g, ev, s);
+  }
+  return e;
+}
+
 }  // namespace
 
 LLMINT8_EXPORT const char *llmint8_status_string(int status) {
@@ -139,7 +182,8 @@ LLMINT8_EXPORT int llmint8_quantize_colwise(const uint16_t *W, int64_t K, int64_
   if (!Wq || !col_absmax) return LLMINT8_ERR_INVALID_ARG;
   if ((st = check_k(K))) return st;
   if (N % 8 != 0 || !aligned16(Wq) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
-  return hip_status(launch_colwise(W, K, N, ldw, Wq, col_absmax, (hipStream_t)stream));
+  return hip_status(
+      launch_colwise<CodecI8>(W, K, N, ldw, (uint8_t *)Wq, col_absmax, (hipStream_t)stream));
 }
 
 LLMINT8_EXPORT size_t llmint8_find_outliers_workspace_size(int64_t M, int64_t K) {
@@ -176,7 +220,8 @@ LLMINT8_EXPORT int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_
   if (!aligned16(Xq) || !aligned16(row_absmax)) return LLMINT8_ERR_UNSUPPORTED;
   if (idx && (!aligned16(idx) || !aligned16(count))) return LLMINT8_ERR_UNSUPPORTED;
   return hip_status(
-      launch_rowquant_idx(X, M, K, ldx, idx, count, Xq, row_absmax, (hipStream_t)stream));
+      launch_rowquant_idx<CodecI8>(X, M, K, ldx, idx, count, (uint8_t *)Xq, row_absmax,
+                                   (hipStream_t)stream));
 }
 
 LLMINT8_EXPORT size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N) {
@@ -240,34 +285,8 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
     return hip_status(launch_decode(det, g, dp, ev, s));
   }
 
-  const DetectPlan plan = detect_plan(M, K);
-  uint32_t *omask = (uint32_t *)(ws + L.omask);
-  int32_t *wprefix = (int32_t *)(ws + L.wprefix);
-  int32_t *idx = (int32_t *)(ws + L.idx);
-  int32_t *count = (int32_t *)(ws + L.count);
-  int8_t *xq = (int8_t *)(ws + L.xq);
-  float *m = (float *)(ws + L.m);
-  uint16_t *xo = (uint16_t *)(ws + L.xo);
-  int8_t *wqc = (int8_t *)(ws + L.wqc);
-
-  DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
-              wprefix, idx, (int32_t *)(ws + L.nidx), count, outlier_count_out};
-  const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
-  uint16_t *wot = (uint16_t *)(ws + L.wot);
-  hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
-  if (e == hipSuccess)
-    e = launch_rowquant_layer(X, M, K, ldx, omask, wprefix, count, xq, ldq, m, xo, ldo, s);
-  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, ldq, s);
-  if (e == hipSuccess && (Wf || int8w))
-    e = launch_gather_wot(Wf, ldw, Wq, K, N, idx, count, wot, ldo, s);
-  if (e == hipSuccess) {
-    // the GEMM's outlier product runs when it has weight rows (gathered above)
-    const uint16_t *wo_src = (Wf || int8w) ? wot : nullptr;
-    GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, wo_src ? (const uint16_t *)wot : nullptr,
-               count, Y, C_debug, M, N, K, ldq, ldo, ldw, ldy, ep};
-    e = launch_gemm(g, ev, s);
-  }
-  return hip_status(e);
+  return hip_status(prefill_layer(X, M, K, ldx, Wq, col_absmax, Wf, ldw, N, threshold, Y, ldy,
+                                  outlier_count_out, C_debug, ws, L, o, ev, ep, false, s));
 }
 
 LLMINT8_EXPORT size_t llmint8_quantize_tensorwise_workspace_size(int64_t K, int64_t N) {
@@ -356,4 +375,69 @@ LLMINT8_EXPORT int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64
                                   void *workspace, size_t workspace_bytes, void *stream) {
   return llmint8_linear_ex(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
                            outlier_count_out, C_debug, workspace, workspace_bytes, stream, nullptr);
+}
+
+// ---- FP8 (E4M3) variant --------------------------------------------------------------
+
+LLMINT8_EXPORT int llmint8_quantize_colwise_fp8(const uint16_t *W, int64_t K, int64_t N,
+                                                int64_t ldw, uint8_t *Wq8, float *col_absmax,
+                                                void *stream) {
+  int st = check_matrix(W, K, N, ldw);
+  if (st) return st;
+  if (!Wq8 || !col_absmax) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq8) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  return hip_status(launch_colwise<CodecE4M3>(W, K, N, ldw, Wq8, col_absmax, (hipStream_t)stream));
+}
+
+LLMINT8_EXPORT int llmint8_quantize_rowwise_fp8(const uint16_t *X, int64_t M, int64_t K,
+                                                int64_t ldx, const int32_t *idx,
+                                                const int32_t *count, uint8_t *Xq8,
+                                                float *row_absmax, void *stream) {
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if (!Xq8 || !row_absmax || (!idx) != (!count)) return LLMINT8_ERR_INVALID_ARG;
+  if ((st = check_k(K))) return st;
+  if (!aligned16(Xq8) || !aligned16(row_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if (idx && (!aligned16(idx) || !aligned16(count))) return LLMINT8_ERR_UNSUPPORTED;
+  return hip_status(launch_rowquant_idx<CodecE4M3>(X, M, K, ldx, idx, count, Xq8, row_absmax,
+                                                   (hipStream_t)stream));
+}
+
+LLMINT8_EXPORT size_t llmint8_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
+  return make_layout(M, K, N, true, true).total;
+}
+
+LLMINT8_EXPORT int llmint8_linear_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                      const uint8_t *Wq8, const float *col_absmax,
+                                      const uint16_t *W, int64_t ldw, int64_t N, float threshold,
+                                      uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
+                                      float *C_debug, void *workspace, size_t workspace_bytes,
+                                      void *stream, const llmint8_linear_opts *opts) {
+  if (opts && opts->struct_size != sizeof(llmint8_linear_opts)) return LLMINT8_ERR_INVALID_ARG;
+  const llmint8_linear_opts o = opts ? *opts : llmint8_linear_opts{};
+  if (o.outlier_weights != LLMINT8_OUTLIER_W_FP16) return LLMINT8_ERR_INVALID_ARG;
+  if ((o.bias && !aligned16(o.bias)) || (o.y_col_absmax && !aligned16(o.y_col_absmax)) ||
+      (o.x_col_absmax && !aligned16(o.x_col_absmax)))
+    return LLMINT8_ERR_UNSUPPORTED;
+  int st = check_matrix(X, M, K, ldx);
+  if (st) return st;
+  if ((st = check_matrix(Y, M, N, ldy))) return st;
+  if (!Wq8 || !col_absmax || std::isnan(threshold)) return LLMINT8_ERR_INVALID_ARG;
+  if (!W && !(std::isinf(threshold) && threshold > 0)) return LLMINT8_ERR_INVALID_ARG;
+  if (W && (st = check_matrix(W, K, N, ldw))) return st;
+  if ((st = check_k(K))) return st;
+  if (N % 8 != 0 || !aligned16(Wq8) || !aligned16(col_absmax)) return LLMINT8_ERR_UNSUPPORTED;
+  if ((outlier_count_out && !aligned16(outlier_count_out)) || (C_debug && !aligned16(C_debug)))
+    return LLMINT8_ERR_UNSUPPORTED;
+  if (ldy >= kMaxTileLd || N >= kMaxTileLd) return LLMINT8_ERR_UNSUPPORTED;
+  const Layout L = make_layout(M, K, N, true, true);
+  if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
+  const GemmEvents ev{o.gemm_begin_event, o.gemm_end_event};
+  const EpilogueOpts ep{0, o.bias, o.y_col_absmax};
+  return hip_status(prefill_layer(X, M, K, ldx, (const int8_t *)Wq8, col_absmax, W, ldw, N,
+                                  threshold, Y, ldy, outlier_count_out, (int32_t *)C_debug,
+                                  (uint8_t *)workspace, L, o, ev, ep, true, (hipStream_t)stream));
 }

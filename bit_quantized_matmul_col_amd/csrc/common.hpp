@@ -8,6 +8,7 @@
 namespace llmint8 {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -49,6 +50,40 @@ __device__ inline int quant_i8(float x, float inv) {
   r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
   return (int)r;
 }
+
+// The two 8-bit encodings of the layer. Each maps t = x * fl32(qmax / absmax)
+// to a code byte: int8 rounds half to even and clamps to [-127, 127]; E4M3
+// (the FP8 format of the INT8/FP8 page, sections 2 and 4: 4 exponent bits,
+// 3 mantissa bits, largest value 448) takes the nearest value, ties to even,
+// by the hardware conversion. |t| never exceeds qmax by more than the fp32
+// rounding of the scale, which both encodings take to +-qmax.
+struct CodecI8 {
+  static constexpr double kQmax = 127.0;
+  __device__ static uint32_t code(float t) {
+    float r = __builtin_rintf(t);
+    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(int)r & 0xffu;
+  }
+  // codes of t[0..3] packed little-endian
+  __device__ static uint32_t code4(const float *t) {
+    return code(t[0]) | code(t[1]) << 8 | code(t[2]) << 16 | code(t[3]) << 24;
+  }
+};
+
+struct CodecE4M3 {
+  static constexpr double kQmax = 448.0;
+  __device__ static uint32_t code(float t) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xffu;
+  }
+  __device__ static uint32_t code4(const float *t) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], lo, true);
+  }
+};
+
+// fl32(qmax / a) correctly rounded, as inv_scale.
+template <class Codec>
+__device__ inline float inv_scale_of(float a) { return (float)(Codec::kQmax / (double)a); }
 
 // Absolute values of the 8 fp16 in a 16-byte chunk, folded into a running max.
 __device__ inline void absmax8(const u32x4 &v, float *mx) {

@@ -111,8 +111,13 @@ hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, const int8_t *Wq, i
 }
 
 hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 256, kWideWavesN, kWideStageK, true>(a, ev, stream)
-                : gemm_detail::launch_prefill<256, 256, kWideWavesN, kWideStageK, false>(a, ev, stream);
+  using namespace gemm_detail;
+  constexpr int W = kWideWavesN, S = kWideStageK;
+  if (a.fp8)
+    return a.cdbg ? launch_prefill<256, 256, W, S, true, true>(a, ev, stream)
+                  : launch_prefill<256, 256, W, S, false, true>(a, ev, stream);
+  return a.cdbg ? launch_prefill<256, 256, W, S, true, false>(a, ev, stream)
+                : launch_prefill<256, 256, W, S, false, false>(a, ev, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {

@@ -167,35 +167,63 @@ __device__ inline V lds_frag(const uint8_t *p) {
   return *(const V *)p;
 }
 
+// Operand fragment of one lane for one k-step: FragChunks<V> consecutive
+// logical 16-byte chunks from chunk c0 of a row, each read from its swizzled
+// slot.
+template <typename V>
+struct FragChunks {
+  static constexpr int value = 1;
+};
+template <>
+struct FragChunks<i32x8> {
+  static constexpr int value = 2;
+};
+
+template <int SK, typename V>
+__device__ inline void frag(const uint8_t *tile, int row, int c0, V &out) {
+  out = lds_frag<V>(tile + swz<SK>(row, c0));
+}
+
+template <int SK>
+__device__ inline void frag(const uint8_t *tile, int row, int c0, i32x8 &out) {
+  out.lo = lds_frag<i32x4>(tile + swz<SK>(row, c0));
+  out.hi = lds_frag<i32x4>(tile + swz<SK>(row, c0 + 1));
+}
+
+// The MFMAs of one stage of SK bytes of k. A k-step takes 16 * FragChunks<V>
+// bytes of k from each of the two lane groups. The operand fragments of k-step ks + 1
+// are read from LDS (into the second of two fragment buffers) before the MFMAs
+// of k-step ks are issued; scheduling barriers keep the compiler from sinking
+// those reads next to their use, so their latency hides behind the current
+// k-step's MFMAs. after_kstep(ks, KSTEPS) runs after each k-step's MFMAs.
 template <int BM, int WM, int WN, int MI, int NI, int SK, typename V, typename MFMA,
           typename HOOK>
 __device__ inline void stage_mfma(const uint8_t *cur, int wm, int wn, int li, int lg,
                                   i32x16 *acc, MFMA mfma, HOOK after_kstep) {
-  constexpr int KSTEPS = SK / 32;
+  constexpr int CPL = FragChunks<V>::value;  // chunks per lane per k-step
+  constexpr int KSTEPS = SK / (32 * CPL);
   V av[2][MI], bv[2][NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) av[0][mi] = lds_frag<V>(cur + swz<SK>(wm * WM + mi * 32 + li, lg));
+  for (int mi = 0; mi < MI; ++mi) frag<SK>(cur, wm * WM + mi * 32 + li, lg * CPL, av[0][mi]);
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
-    bv[0][ni] = lds_frag<V>(cur + BM * SK + swz<SK>(wn * WN + ni * 32 + li, lg));
+  for (int ni = 0; ni < NI; ++ni) frag<SK>(cur + BM * SK, wn * WN + ni * 32 + li, lg * CPL, bv[0][ni]);
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     const int b = ks & 1;
     if (ks + 1 < KSTEPS) {
+      const int c0 = (2 * (ks + 1) + lg) * CPL;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        av[b ^ 1][mi] = lds_frag<V>(cur + swz<SK>(wm * WM + mi * 32 + li, 2 * (ks + 1) + lg));
+      for (int mi = 0; mi < MI; ++mi) frag<SK>(cur, wm * WM + mi * 32 + li, c0, av[b ^ 1][mi]);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        bv[b ^ 1][ni] =
-            lds_frag<V>(cur + BM * SK + swz<SK>(wn * WN + ni * 32 + li, 2 * (ks + 1) + lg));
+        frag<SK>(cur + BM * SK, wn * WN + ni * 32 + li, c0, bv[b ^ 1][ni]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = mfma(av[b][mi], bv[b][ni], acc[mi * NI + ni]);
-    after_kstep(ks);
+    after_kstep(ks, KSTEPS);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -206,6 +234,16 @@ struct MfmaI8 {
   }
 };
 
+// v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 (format 0) and no block
+// scales: 32 bytes of k per lane, fp32 accumulation (kept as raw bits in the
+// int32 accumulator registers).
+struct MfmaF8 {
+  __device__ i32x16 operator()(i32x8 a, i32x8 b, i32x16 c) const {
+    return __builtin_bit_cast(i32x16, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                          a, b, __builtin_bit_cast(f32x16, c), 0, 0, 0, 0, 0, 0));
+  }
+};
+
 struct MfmaF16 {
   __device__ i32x16 operator()(f16x8 a, f16x8 b, i32x16 c) const {
     return __builtin_bit_cast(i32x16, __builtin_amdgcn_mfma_f32_32x32x16_f16(
@@ -213,20 +251,43 @@ struct MfmaF16 {
   }
 };
 
+// The loads of one stage spread over the k-steps of another stage's MFMAs:
+// after k-step ks of ksteps, the row groups j with j * ksteps / G == ks.
+template <int BM, int BN, int NW, int SK>
+struct SpreadLoads {
+  const OperandTile<BM, NW, SK> &A;
+  const OperandTile<BN, NW, SK> &B;
+  uint8_t *buf;
+  int kb;
+  bool on;
+  __device__ void operator()(int ks, int ksteps) const {
+    constexpr int GA = OperandTile<BM, NW, SK>::G, GB = OperandTile<BN, NW, SK>::G;
+    if (!on) return;
+#pragma unroll
+    for (int j = 0; j < GA; ++j)
+      if (j * ksteps / GA == ks) A.load_group(buf, kb, j);
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+      if (j * ksteps / GB == ks) B.load_group(buf + BM * SK, kb, j);
+  }
+};
+
+// What a k-loop multiplies: int8 codes (int32 sums), fp16 (the outlier
+// product) or E4M3 codes (fp32 sums).
+enum class Op { I8, F16, F8 };
+
 // Pipelined k-loop over nstages 128-byte stages of A and B through a ring of
 // NST LDS buffers. At step it the block waits for stage it only (the NST - 2
 // younger stages stay in flight), synchronizes (which also frees the buffer of
 // stage it - 1), issues stage it + NST - 1 into that buffer and runs the MFMAs
-// of stage it. fp16 selects the outlier-product MFMAs (uniform across the
-// block).
-template <int BM, int BN, int WM, int WN, int MI, int NI, int NST, int NW, int SK>
+// of stage it.
+template <int BM, int BN, int WM, int WN, int MI, int NI, int NST, int NW, int SK, Op OP>
 __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
                              const OperandTile<BN, NW, SK> &B,
-                             int64_t nstages, bool fp16, int wm, int wn, int li, int lg,
+                             int64_t nstages, int wm, int wn, int li, int lg,
                              i32x16 *acc) {
   constexpr int STAGE = (BM + BN) * SK;
   constexpr int LPS = OperandTile<BM, NW, SK>::G + OperandTile<BN, NW, SK>::G;  // per lane per stage
-  constexpr int KSTEPS = SK / 32;
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   if (nstages <= 0) return;
 #pragma unroll
@@ -253,30 +314,25 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
     const bool more = nx < nstages;
     uint8_t *buf = smem + (nx % NST) * STAGE;
     const int kb = (int)(nx * SK);
-    constexpr int GA = OperandTile<BM, NW, SK>::G, GB = OperandTile<BN, NW, SK>::G;
     if (NST == 2 && more) {
       A.load(buf, kb);
       B.load(buf + BM * SK, kb);
     }
-    auto issue = [&](int ks) {
-      if (NST == 2 || !more) return;
-#pragma unroll
-      for (int j = 0; j < GA; ++j)
-        if (j * KSTEPS / GA == ks) A.load_group(buf, kb, j);
-#pragma unroll
-      for (int j = 0; j < GB; ++j)
-        if (j * KSTEPS / GB == ks) B.load_group(buf + BM * SK, kb, j);
-    };
+    const SpreadLoads<BM, BN, NW, SK> issue{A, B, buf, kb, NST > 2 && more};
     const uint8_t *cur = smem + (it % NST) * STAGE;
-    if (fp16)
+    if constexpr (OP == Op::F16)
       stage_mfma<BM, WM, WN, MI, NI, SK, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
+    else if constexpr (OP == Op::F8)
+      stage_mfma<BM, WM, WN, MI, NI, SK, i32x8>(cur, wm, wn, li, lg, acc, MfmaF8(), issue);
     else
       stage_mfma<BM, WM, WN, MI, NI, SK, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 }
 
-template <int BM, int BN, int NWN, int SK, bool DBG>
+// F8: the operands are E4M3 codes (fp32 sums, dequantized by 1 / 448^2)
+// instead of int8 codes (int32 sums, 1 / 127^2).
+template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>
 __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   using T = TileCfg<BM, BN, NWN, SK>;
   constexpr int NW = T::NW, TH = T::THREADS;
@@ -301,14 +357,15 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   // Y = C m s / 127^2 + X_O W_O. With int8 outlier weights W_O = q s / 127, so
   // Y = s / 127 * (C m / 127 + X_O q): the int8 part is scaled by m / 127
   // before the 16-bit MFMAs add X_O q, and s / 127 is applied last.
-  const bool i8w = a.ep.int8w != 0;
+  const bool i8w = !F8 && a.ep.int8w != 0;
+  constexpr float kDequant = F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f;
   // Rows past M take a NaN row scale. Their values fall outside the Y resource
   // when stored, and fmax ignores a NaN, so the column maxima skip them with no
   // per-row test (per-element row masks would stay live across the store loop).
   for (int i = t; i < BM; i += TH) sm[i] = (m0 + i < a.M) ? a.m[m0 + i] : __builtin_nanf("");
   for (int i = t; i < BN; i += TH) {
     const float sn = (n0 + i < a.N) ? a.s[n0 + i] : 0.f;
-    ss[i] = i8w ? 1.0f / 127.0f : sn * (1.0f / 16129.0f);
+    ss[i] = i8w ? 1.0f / 127.0f : sn * kDequant;
     sf[i] = i8w ? sn * (1.0f / 127.0f) : 1.0f;
   }
 
@@ -326,22 +383,27 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
       B.init(a.wqc, a.ldq, n0, a.N);
     else
       B.init(a.wq, a.K, n0, a.N);
-    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK>(smem, A, B, (Kl + SK - 1) / SK, false, wm, wn, li,
-                                                  lg, acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK, F8 ? Op::F8 : Op::I8>(
+        smem, A, B, (Kl + SK - 1) / SK, wm, wn, li, lg, acc);
   }
 
-  // dequantize in place: C * m[i] * s[n] / 127^2
+  // dequantize in place: C * m[i] * s[n] / 127^2 (or / 448^2)
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int cl = wn * WN + ni * 32 + li;
       const float sc = ss[cl];
+      // the E4M3 sums are fp32 already (reinterpret the whole vector: a
+      // per-element bit cast of the int vector was miscompiled to element 0
+      // of each group of four)
+      const f32x16 accf = __builtin_bit_cast(f32x16, acc[mi * NI + ni]);
       f32x16 f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        f[r] = (float)acc[mi * NI + ni][r] * (sm[rl] * sc);
+        const float c = F8 ? accf[r] : (float)acc[mi * NI + ni][r];
+        f[r] = c * (sm[rl] * sc);
       }
       if constexpr (DBG) {
         const bool colok = n0 + cl < a.N;
@@ -365,8 +427,8 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
     OperandTile<BN, NW, SK> B;
     A.init(a.xo, a.ldo * 2, m0, a.M);
     B.init(a.wot, a.ldo * 2, n0, a.N);
-    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK>(smem, A, B, (2 * count + SK - 1) / SK, true, wm,
-                                                  wn, li, lg, acc);
+    kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK, Op::F16>(smem, A, B, (2 * count + SK - 1) / SK,
+                                                           wm, wn, li, lg, acc);
   }
 
   // store Y (fp16, round to nearest even); rows past M fall outside the resource
@@ -401,14 +463,14 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int NWN, int SK, bool DBG>
+template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>
 hipError_t launch_prefill(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
   using T = TileCfg<BM, BN, NWN, SK>;
-  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, NWN, SK, DBG>,
+  hipError_t e = hipFuncSetAttribute((const void *)k_gemm_prefill<BM, BN, NWN, SK, DBG, F8>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, NWN, SK, DBG>), dim3((unsigned)tiles),
+  hipExtLaunchKernelGGL((k_gemm_prefill<BM, BN, NWN, SK, DBG, F8>), dim3((unsigned)tiles),
                         dim3(T::THREADS), T::LDS, stream, (hipEvent_t)ev.begin,
                         (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();

@@ -4,8 +4,12 @@
 namespace llmint8 {
 
 hipError_t launch_gemm_narrow(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return a.cdbg ? gemm_detail::launch_prefill<256, 128, 2, 128, true>(a, ev, stream)
-                : gemm_detail::launch_prefill<256, 128, 2, 128, false>(a, ev, stream);
+  using namespace gemm_detail;
+  if (a.fp8)
+    return a.cdbg ? launch_prefill<256, 128, 2, 128, true, true>(a, ev, stream)
+                  : launch_prefill<256, 128, 2, 128, false, true>(a, ev, stream);
+  return a.cdbg ? launch_prefill<256, 128, 2, 128, true, false>(a, ev, stream)
+                : launch_prefill<256, 128, 2, 128, false, false>(a, ev, stream);
 }
 
 }  // namespace llmint8

@@ -51,8 +51,10 @@ hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, f
                          const DetectPlan &plan, const DetectOut &out, hipStream_t stream);
 
 // Row quantization for the public call: outlier columns from an index list.
+// Codec (CodecI8 or CodecE4M3) picks the 8-bit encoding of every quantizer.
+template <class Codec>
 hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                               const int32_t *idx, const int32_t *count, int8_t *Xq, float *m,
+                               const int32_t *idx, const int32_t *count, uint8_t *Xq, float *m,
                                hipStream_t stream);
 
 // Row quantization inside the layer: outlier columns from the detection
@@ -61,19 +63,22 @@ hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t 
 // Xq rows have pitch ldq (a multiple of 128) and are zero past their last
 // column up to the next multiple of 128; xo rows have pitch ldo (a multiple of
 // 64) and are zero from |O| up to the next multiple of 64.
+template <class Codec>
 hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                                  const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, int8_t *Xq, int64_t ldq, float *m,
+                                 const int32_t *count, uint8_t *Xq, int64_t ldq, float *m,
                                  uint16_t *xo, int64_t ldo, hipStream_t stream);
 
 // Column absmax + quantize + transpose of W [K x N] into Wq [N x K]; the two
 // halves also run alone (s: column maxima out, then the scales the codes use).
-hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
+template <class Codec>
+hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, uint8_t *Wq,
                           float *s, hipStream_t stream);
 hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, float *s,
                                  hipStream_t stream);
+template <class Codec>
 hipError_t launch_colwise_quant(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
-                                const float *s, int8_t *Wq, hipStream_t stream);
+                                const float *s, uint8_t *Wq, hipStream_t stream);
 
 // Compacted copy Wqc [N x K] (first K - |O| bytes of each row) of Wq without
 // the outlier columns; a no-op unless the outlier share calls for it.
@@ -102,6 +107,7 @@ struct GemmArgs {
   int32_t *cdbg;         // optional [M x N] int32
   int64_t M, N, K, ldq, ldo, ldw, ldy;
   EpilogueOpts ep;
+  int fp8;               // xq and wq hold E4M3 codes instead of int8 ones
 };
 
 // Caller-supplied events (may be null) that the GEMM kernel's own dispatch

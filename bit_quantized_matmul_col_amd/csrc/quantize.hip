@@ -29,26 +29,31 @@ __device__ inline unsigned chunk_bits(const uint32_t *mask, int64_t ch) {
   return (mask[ch >> 2] >> ((ch & 3) * 8)) & 0xffu;
 }
 
-// Codes of the 8 fp16 of a chunk, outlier columns zeroed, packed little-endian.
+// Codes of the 8 fp16 of a chunk, outlier columns (and a zero row) zeroed,
+// packed little-endian.
+template <class Codec>
 __device__ inline u32x2 quant_chunk(const u32x4 &v, unsigned obits, float inv, bool zero_row) {
-  u32x2 out = {0u, 0u};
+  float t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t w = v[e >> 1];
-    const float x = (e & 1) ? fp16_hi(w) : fp16_lo(w);
-    int q = 0;
-    if (!zero_row && !((obits >> e) & 1u)) q = quant_i8(x, inv);
-    out[e >> 2] |= ((uint32_t)q & 0xffu) << (8 * (e & 3));
+    t[e] = ((e & 1) ? fp16_hi(w) : fp16_lo(w)) * inv;
   }
+  u32x2 out = {Codec::code4(t), Codec::code4(t + 4)};
+  const unsigned drop = zero_row ? 0xffu : obits;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((drop >> e) & 1u) out[e >> 2] &= ~(0xffu << (8 * (e & 3)));
   return out;
 }
 
 // Public row quantization: one block per row; the outlier set is given as an
 // index list, turned into an LDS bitmask first.
+template <class Codec>
 __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict__ X, int64_t K,
                                                       int64_t ldx, const int32_t *__restrict__ idx,
                                                       const int32_t *__restrict__ count_ptr,
-                                                      int8_t *__restrict__ Xq,
+                                                      uint8_t *__restrict__ Xq,
                                                       float *__restrict__ m) {
   extern __shared__ uint32_t smask[];
   __shared__ float red[4];
@@ -80,11 +85,11 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
   mx = block_max256(mx, red);
   if (t == 0) m[i] = mx;
   const bool zero_row = !(mx > 0.f);
-  const float inv = zero_row ? 0.f : inv_scale(mx);
-  int8_t *qrow = Xq + i * K;
+  const float inv = zero_row ? 0.f : inv_scale_of<Codec>(mx);
+  uint8_t *qrow = Xq + i * K;
   for (int64_t ch = t; ch < nch; ch += 256) {
     const u32x4 v = *(const u32x4 *)(row + ch * 8);
-    *(u32x2 *)(qrow + ch * 8) = quant_chunk(v, chunk_bits(smask, ch), inv, zero_row);
+    *(u32x2 *)(qrow + ch * 8) = quant_chunk<Codec>(v, chunk_bits(smask, ch), inv, zero_row);
   }
 }
 
@@ -95,11 +100,12 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
 // Xq (pitch ldq) are zero past their last column up to the next multiple of
 // 128 bytes and rows of xo (pitch ldo) from |O| up to the next multiple of 64,
 // so the GEMM can run whole 128-byte k stages.
+template <class Codec>
 __global__ __launch_bounds__(256) void k_rowquant_layer(
     const uint16_t *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const uint32_t *__restrict__ omask,
     const int32_t *__restrict__ wprefix, const int32_t *__restrict__ count_ptr,
-    int8_t *__restrict__ Xq, int64_t ldq, float *__restrict__ m, uint16_t *__restrict__ xo,
+    uint8_t *__restrict__ Xq, int64_t ldq, float *__restrict__ m, uint16_t *__restrict__ xo,
     int64_t ldo) {
   extern __shared__ u32x4 srow_v[];
   uint8_t *srow = (uint8_t *)srow_v;
@@ -124,8 +130,8 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   mx = block_max256(mx, red);
   if (t == 0) m[i] = mx;
   const bool zero_row = !(mx > 0.f);
-  const float inv = zero_row ? 0.f : inv_scale(mx);
-  int8_t *qrow = Xq + i * ldq;
+  const float inv = zero_row ? 0.f : inv_scale_of<Codec>(mx);
+  uint8_t *qrow = Xq + i * ldq;
   uint16_t *orow = xo + i * ldo;
   const int64_t opad = (count + 63) / 64 * 64;
   for (int64_t p = count + t; p < opad; p += 256) orow[p] = 0;
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   for (int64_t ch = t; ch < nch; ch += 256) {
     const u32x4 v = *(const u32x4 *)(row + ch * 8);
     const unsigned ob = chunk_bits(omask, ch);
-    const u32x2 q = quant_chunk(v, ob, inv, zero_row);
+    const u32x2 q = quant_chunk<Codec>(v, ob, inv, zero_row);
     // rank of column 8ch in the outlier list
     const int64_t wd = ch >> 2;
     const int sh = (int)(ch & 3) * 8;
@@ -213,10 +219,11 @@ __global__ void k_fill_u32(unsigned *__restrict__ p, int64_t n, unsigned v) {
 // Quantize and transpose a 128 (k) x 64 (n) tile of W into Wq [N x K]: read
 // 128-byte row segments of W, transpose the int8 codes through LDS, write
 // 128-byte segments of Wq rows.
+template <class Codec>
 __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W, int64_t K,
                                                   int64_t N, int64_t ldw,
                                                   const float *__restrict__ s,
-                                                  int8_t *__restrict__ Wq) {
+                                                  uint8_t *__restrict__ Wq) {
   constexpr int TK = 128, TN = 64, PITCH = TK + 16;
   __shared__ __attribute__((aligned(16))) uint8_t st[TN * PITCH];
   __shared__ float sinv[TN];
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W
     const int64_t n = n0 + t;
     const float a = (n < N) ? s[n] : 0.f;
     szero[t] = !(a > 0.f);
-    sinv[t] = (a > 0.f) ? inv_scale(a) : 0.f;
+    sinv[t] = (a > 0.f) ? inv_scale_of<Codec>(a) : 0.f;
   }
   __syncthreads();
 #pragma unroll
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W
       const int nl = ch * 8 + e;
       const uint32_t w = v[e >> 1];
       const float x = (e & 1) ? fp16_hi(w) : fp16_lo(w);
-      const int code = szero[nl] ? 0 : quant_i8(x, sinv[nl]);
+      const uint32_t code = szero[nl] ? 0u : Codec::code(x * sinv[nl]);
       st[nl * PITCH + r] = (uint8_t)code;
     }
   }
@@ -302,24 +309,40 @@ __global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ W
 
 }  // namespace
 
+template <class Codec>
 hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                               const int32_t *idx, const int32_t *count, int8_t *Xq, float *m,
+                               const int32_t *idx, const int32_t *count, uint8_t *Xq, float *m,
                                hipStream_t stream) {
   const size_t lds = (size_t)((K + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_rowquant_idx, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx, idx,
-                     count, Xq, m);
+  hipLaunchKernelGGL(k_rowquant_idx<Codec>, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx,
+                     idx, count, Xq, m);
   return hipGetLastError();
 }
+template hipError_t launch_rowquant_idx<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                 const int32_t *, const int32_t *, uint8_t *,
+                                                 float *, hipStream_t);
+template hipError_t launch_rowquant_idx<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                   const int32_t *, const int32_t *, uint8_t *,
+                                                   float *, hipStream_t);
 
+template <class Codec>
 hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                                  const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, int8_t *Xq, int64_t ldq, float *m,
+                                 const int32_t *count, uint8_t *Xq, int64_t ldq, float *m,
                                  uint16_t *xo, int64_t ldo, hipStream_t stream) {
   const size_t lds = (K <= kCompactMaxK) ? (size_t)ldq : 0;
-  hipLaunchKernelGGL(k_rowquant_layer, dim3((unsigned)M), dim3(256), lds, stream, X, M, K, ldx,
-                     omask, wprefix, count, Xq, ldq, m, xo, ldo);
+  hipLaunchKernelGGL(k_rowquant_layer<Codec>, dim3((unsigned)M), dim3(256), lds, stream, X, M, K,
+                     ldx, omask, wprefix, count, Xq, ldq, m, xo, ldo);
   return hipGetLastError();
 }
+template hipError_t launch_rowquant_layer<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                   const uint32_t *, const int32_t *,
+                                                   const int32_t *, uint8_t *, int64_t, float *,
+                                                   uint16_t *, int64_t, hipStream_t);
+template hipError_t launch_rowquant_layer<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                     const uint32_t *, const int32_t *,
+                                                     const int32_t *, uint8_t *, int64_t, float *,
+                                                     uint16_t *, int64_t, hipStream_t);
 
 hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, float *s,
                                  hipStream_t stream) {
@@ -338,19 +361,30 @@ hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_
   return hipGetLastError();
 }
 
+template <class Codec>
 hipError_t launch_colwise_quant(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
-                                const float *s, int8_t *Wq, hipStream_t stream) {
-  hipLaunchKernelGGL(k_colquant, dim3((unsigned)((K + 127) / 128), (unsigned)((N + 63) / 64)),
-                     dim3(256), 0, stream, W, K, N, ldw, s, Wq);
+                                const float *s, uint8_t *Wq, hipStream_t stream) {
+  hipLaunchKernelGGL(k_colquant<Codec>,
+                     dim3((unsigned)((K + 127) / 128), (unsigned)((N + 63) / 64)), dim3(256), 0,
+                     stream, W, K, N, ldw, s, Wq);
   return hipGetLastError();
 }
+template hipError_t launch_colwise_quant<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                  const float *, uint8_t *, hipStream_t);
+template hipError_t launch_colwise_quant<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
+                                                    const float *, uint8_t *, hipStream_t);
 
-hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, int8_t *Wq,
+template <class Codec>
+hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, uint8_t *Wq,
                           float *s, hipStream_t stream) {
   const hipError_t e = launch_colwise_absmax(W, K, N, ldw, s, stream);
   if (e != hipSuccess) return e;
-  return launch_colwise_quant(W, K, N, ldw, s, Wq, stream);
+  return launch_colwise_quant<Codec>(W, K, N, ldw, s, Wq, stream);
 }
+template hipError_t launch_colwise<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,
+                                            uint8_t *, float *, hipStream_t);
+template hipError_t launch_colwise<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
+                                              uint8_t *, float *, hipStream_t);
 
 hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
                              const uint32_t *omask, const int32_t *wprefix, const int32_t *count,

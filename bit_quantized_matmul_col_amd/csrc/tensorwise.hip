@@ -97,7 +97,7 @@ hipError_t launch_quantize_tensorwise(const uint16_t *W, int64_t K, int64_t N, i
                      w_absmax, scratch, N, (float *)nullptr, (int64_t)0, (const float *)nullptr,
                      (int32_t *)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_colwise_quant(W, K, N, ldw, scratch, Wq, stream);
+  return launch_colwise_quant<CodecI8>(W, K, N, ldw, scratch, (uint8_t *)Wq, stream);
 }
 
 hipError_t launch_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,

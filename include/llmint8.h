@@ -206,6 +206,48 @@ int llmint8_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t l
                               int32_t *C_debug, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/*
+ * FP8 (E4M3) variant of the decomposition: the same outlier split, with the
+ * 8-bit part coded in E4M3 instead of int8 (the INT8/FP8 page, CSDN, sections
+ * 2 and 4: FP8 E4M3 has 4 exponent and 3 mantissa bits, its largest value is
+ * about 448, and wide-ranged inputs need a scale before the cast). E4M3 here
+ * is the OCP 8-bit format: bias 7, subnormals, no infinities, 0x7f/0xff NaN.
+ *   codes:  q = e4m3(x * fl32(448 / absmax)), nearest value, ties to even;
+ *           absmax per row of X (outlier columns excluded) and per column of W,
+ *           exactly as in steps 2 and 3 above; a zero absmax gives code 0.
+ *   matmul: C = value(Xq8) . value(Wq8)^T, products exact, summed by the
+ *           E4M3 MFMA into fp32 accumulators;
+ *   merge:  Y = fp16( C * m[i] * s[n] / 448^2 + X_O . W_O ).
+ * The codes are bit-exact with that definition. C is not: one MFMA adds 64
+ * products keeping fewer bits than fp32 (errors up to about 2^-13 of the sum
+ * of the magnitudes measured on MI355X).
+ *
+ * llmint8_quantize_colwise_fp8: as llmint8_quantize_colwise, E4M3 codes.
+ *   Wq8 [N x K] uint8 E4M3 codes; col_absmax [N] fp32.
+ * llmint8_quantize_rowwise_fp8: as llmint8_quantize_rowwise, E4M3 codes.
+ *   Xq8 [M x K] uint8 E4M3 codes (0 on outlier columns); row_absmax [M] fp32.
+ * llmint8_linear_fp8: the whole FP8 layer, any M (the large-M kernels), with
+ *   the arguments of llmint8_linear_ex except:
+ *   Wq8, col_absmax  from llmint8_quantize_colwise_fp8;
+ *   C_debug    optional [M x N] fp32 output (leading dimension N): C;
+ *   workspace  at least llmint8_linear_fp8_workspace_size(M, K, N) bytes;
+ *   opts       may be NULL; outlier_weights must be LLMINT8_OUTLIER_W_FP16
+ *              (else LLMINT8_ERR_INVALID_ARG); the events, bias,
+ *              y_col_absmax and x_col_absmax act as for llmint8_linear_ex.
+ */
+int llmint8_quantize_colwise_fp8(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                 uint8_t *Wq8, float *col_absmax, void *stream);
+int llmint8_quantize_rowwise_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                 const int32_t *idx, const int32_t *count, uint8_t *Xq8,
+                                 float *row_absmax, void *stream);
+size_t llmint8_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N);
+int llmint8_linear_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                       const uint8_t *Wq8, const float *col_absmax,
+                       const uint16_t *W, int64_t ldw, int64_t N, float threshold,
+                       uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, float *C_debug,
+                       void *workspace, size_t workspace_bytes, void *stream,
+                       const llmint8_linear_opts *opts);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *llmint8_status_string(int status);
 

@@ -63,6 +63,11 @@ L.llmint8_quantize_tensorwise_workspace_size.restype = sz
 L.llmint8_linear_tensorwise.argtypes = [p, i64, i64, i64, p, p, i64, p, p, i64, p, p, p, sz, p]
 L.llmint8_linear_tensorwise_workspace_size.argtypes = [i64, i64, i64]
 L.llmint8_linear_tensorwise_workspace_size.restype = sz
+L.llmint8_quantize_colwise_fp8.argtypes = [p, i64, i64, i64, p, p, p]
+L.llmint8_quantize_rowwise_fp8.argtypes = [p, i64, i64, i64, p, p, p, p, p]
+L.llmint8_linear_fp8.argtypes = L.llmint8_linear_ex.argtypes
+L.llmint8_linear_fp8_workspace_size.argtypes = [i64, i64, i64]
+L.llmint8_linear_fp8_workspace_size.restype = sz
 L.llmint8_find_outliers_workspace_size.argtypes = [i64, i64]
 L.llmint8_find_outliers_workspace_size.restype = sz
 A, B, MIS = 0x100000, 0x200000, 0x300008   # 16-byte aligned fakes and a misaligned one
@@ -88,6 +93,10 @@ def ltw(name, X=A, M=4, K=64, ldx=64, Wq=B, sw=A, N=32, bias=N0, Y=B, ldy=32, xa
         ws=A, wsb=0):
     res[name] = L.llmint8_linear_tensorwise(X, M, K, ldx, Wq, sw, N, bias, Y, ldy, xa, cdbg, ws,
                                             wsb, None)
+def lfp8(name, size=C.sizeof(Opts), ow=0, W=A, t=6.0, M=4, cdbg=N0, wsb=0, opts=True):
+    o = Opts(size, None, None, ow, None, None, None)
+    res[name] = L.llmint8_linear_fp8(A, M, 64, 64, B, A, W, 32, 32, t, B, 32, None, cdbg, A, wsb,
+                                     None, C.byref(o) if opts else None)
 colwise("colwise_null_W", W=N0)
 colwise("colwise_K0", K=0)
 colwise("colwise_ld_short", ldw=16)
@@ -135,6 +144,17 @@ ltw("ltw_misaligned_bias", bias=MIS)
 ltw("ltw_misaligned_x_absmax", xa=MIS)
 ltw("ltw_N_not_mult8", N=36, ldy=40)
 ltw("ltw_workspace_small", wsb=64)
+res["cfp8_null_Wq8"] = L.llmint8_quantize_colwise_fp8(A, 64, 32, 32, None, A, None)
+res["cfp8_N_not_mult8"] = L.llmint8_quantize_colwise_fp8(A, 64, 30, 32, B, A, None)
+res["rfp8_idx_without_count"] = L.llmint8_quantize_rowwise_fp8(A, 4, 64, 64, A, None, B, A, None)
+res["rfp8_misaligned_Xq8"] = L.llmint8_quantize_rowwise_fp8(A, 4, 64, 64, None, None, MIS, A, None)
+lfp8("lfp8_int8_weights_rejected", ow=1, wsb=1 << 40)
+lfp8("lfp8_struct_size_old", size=24)
+lfp8("lfp8_null_W_finite_threshold", W=N0)
+lfp8("lfp8_null_W_inf_small_ws", W=N0, t=math.inf)
+lfp8("lfp8_no_opts_small_ws", opts=False)
+lfp8("lfp8_misaligned_cdbg", cdbg=MIS, wsb=1 << 40)
+res["ws_fp8_small_m"] = L.llmint8_linear_fp8_workspace_size(8, 4096, 4096)
 res["ws_size_ok"] = L.llmint8_workspace_size(32, 4096, 4096)
 res["qtw_ws"] = L.llmint8_quantize_tensorwise_workspace_size(4096, 11008)
 res["qtw_ws_bad"] = L.llmint8_quantize_tensorwise_workspace_size(4096, 0)
@@ -167,6 +187,11 @@ EXPECTED = {
     "qtw_no_workspace": 4, "qtw_K_too_big": 3,
     "ltw_null_Wq": 1, "ltw_null_X": 1, "ltw_ldy_short": 1, "ltw_misaligned_bias": 2,
     "ltw_misaligned_x_absmax": 2, "ltw_N_not_mult8": 2, "ltw_workspace_small": 4,
+    "cfp8_null_Wq8": 1, "cfp8_N_not_mult8": 2, "rfp8_idx_without_count": 1,
+    "rfp8_misaligned_Xq8": 2,
+    "lfp8_int8_weights_rejected": 1, "lfp8_struct_size_old": 1,
+    "lfp8_null_W_finite_threshold": 1, "lfp8_null_W_inf_small_ws": 4,
+    "lfp8_no_opts_small_ws": 4, "lfp8_misaligned_cdbg": 2,
 }
 
 
@@ -188,6 +213,9 @@ def test_invalid_arguments_are_rejected_before_any_hip_call():
     # per-tensor layer: the column maxima for W; the int8 copy of X and the scales
     assert res["qtw_ws"] >= 11008 * 4 and res["qtw_ws_bad"] == 0
     assert res["ltw_ws"] >= 2048 * 4096 + 2048 * 4 + 11008 * 4 and res["ltw_ws_bad"] == 0
+    # FP8 layer: the large-M layout at every M (int8 + fp16 copies of X, room for
+    # a compacted Wq8)
+    assert res["ws_fp8_small_m"] >= 8 * 4096 * 3 + 4096 * 4096
 
 
 def test_status_strings():

@@ -461,3 +461,133 @@ def test_tensorwise_loses_more_than_mixed_decomposition(dev):
     err_m = np.abs(Ym.cpu().numpy().astype(np.float64) - exact).mean()
     err_t = np.abs(Yt.cpu().numpy().astype(np.float64) - exact).mean()
     assert err_t > 5 * err_m, (err_t, err_m)
+
+
+# --- the FP8 (E4M3) variant ---------------------------------------------------------------
+# Codes (E4M3 bytes), scales and the outlier set are bit-exact. The 8-bit
+# product C is summed by the E4M3 MFMA on the GPU and exactly in the oracle.
+# One v_mfma_f32_32x32x64_f8f6f4 adds 64 exact products with less than fp32
+# precision: measured on MI355X its error reaches 2^-13 of the block's sum of
+# magnitudes (an fp32 sequential sum stays near 2^-24). C is therefore
+# compared within (2^-12 + K * 2^-30) * sum_k |x_k w_k| (the block bound with a
+# factor 2 of margin plus fp32 accumulation across the K / 64 blocks); Y keeps
+# the layer's 1e-2 abs + 1e-2 rel bar.
+
+def all_fp16_row():
+    """One row holding every finite fp16 value of magnitude <= 448 (both signs),
+    padded with zeros to a multiple of 16; its absmax is 448, so the scale is
+    exactly 1 and the codes are the E4M3 encoding of each value itself."""
+    pos = np.arange(0x5F01, dtype=np.uint16)  # 0 .. 448
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    pad = (-vals.size) % 16
+    return np.concatenate([vals, np.zeros(pad, np.uint16)]).view(np.float16)[None, :]
+
+
+def test_fp8_codes_of_every_fp16_value(dev):
+    torch, lm = dev
+    say("case fp8 codes of every fp16 value up to 448")
+    X = all_fp16_row()
+    Xq, m = lm.llmint8_quantize_rowwise_fp8(to_gpu(torch, X))
+    ref_q, ref_m = oracle.quantize_rowwise_fp8(X)
+    torch.cuda.synchronize()
+    assert ref_m[0] == 448.0 and m.cpu().numpy()[0] == 448.0
+    got = Xq.cpu().numpy()
+    bad = np.flatnonzero(got[0] != ref_q[0])
+    assert bad.size == 0, [(hex(X.view(np.uint16)[0, b]), got[0, b], ref_q[0, b]) for b in bad[:8]]
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (33, 272), (300, 1040)])
+def test_fp8_rowwise_codes(dev, M, K):
+    torch, lm = dev
+    say(f"case fp8 rowwise M={M} K={K}")
+    X, _, _ = workloads.random_case(M, K, 8, seed=M + K, n_out=3)
+    X[0, :] = 0.0  # a zero row
+    Xd = to_gpu(torch, X)
+    for thr in (6.0, math.inf):
+        idx_d, cnt_d = lm.llmint8_find_outliers(Xd, thr)
+        Xq, m = lm.llmint8_quantize_rowwise_fp8(Xd, idx_d, cnt_d)
+        idx = oracle.find_outliers(X, thr)
+        ref_q, ref_m = oracle.quantize_rowwise_fp8(X, idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(m.cpu().numpy().view(np.uint32), ref_m.view(np.uint32))
+        assert np.array_equal(Xq.cpu().numpy(), ref_q)
+
+
+@pytest.mark.parametrize("K,N", [(16, 8), (272, 200), (4096, 520)])
+def test_fp8_colwise_codes(dev, K, N):
+    torch, lm = dev
+    say(f"case fp8 colwise K={K} N={N}")
+    _, W, _ = workloads.random_case(4, K, N, seed=K + N)
+    W[:, 0] = 0.0  # a zero column
+    Wq, s = lm.llmint8_quantize_colwise_fp8(to_gpu(torch, W))
+    ref_q, ref_s = oracle.quantize_colwise_fp8(W)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(Wq.cpu().numpy(), ref_q)
+
+
+def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None):
+    M, K = X.shape
+    N = W.shape[1]
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise_fp8(Wd)
+    if ref_w is None:
+        ref_w = oracle.quantize_colwise_fp8(W)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    bd = to_gpu(torch, bias) if bias is not None else None
+    Y = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, threshold, C_debug=C, outlier_count=cnt, bias=bd)
+    Yp = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, threshold, bias=bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yp.view(torch.int16)), "debug/production Y differ"
+    ref = oracle.linear_fp8(X, W, threshold, Wq8=ref_w[0], s=ref_w[1], rows=rows)
+    assert int(cnt.item()) == ref["idx"].size
+    if rows is None:
+        c, y = C.cpu().numpy(), Y.cpu().numpy()
+    else:
+        rt = torch.from_numpy(np.asarray(rows)).cuda()
+        c, y = C.index_select(0, rt).cpu().numpy(), Y.index_select(0, rt).cpu().numpy()
+    mag = np.abs(oracle.e4m3_value(ref["Xq"])) @ np.abs(oracle.e4m3_value(ref["Wq"])).T
+    err = np.abs(c.astype(np.float64) - ref["C"])
+    assert np.all(err <= (2.0 ** -12 + K * 2.0 ** -30) * mag + 1e-30), f"C error {err.max():.3g}"
+    Yr = ref["Y"] if bias is None else oracle.add_bias(ref["Y"], bias)
+    assert_y_close(y, Yr, "fp8 Y")
+    return int(cnt.item())
+
+
+FP8_CASES = [(1, 256, 136), (5, 4096, 520), (48, 2048, 1032), (257, 784, 520), (300, 1024, 264),
+             (700, 1008, 200)]
+
+
+@pytest.mark.parametrize("M,K,N", FP8_CASES)
+@pytest.mark.parametrize("threshold", [6.0, math.inf, 3.0, 0.0])
+def test_fp8_layer(dev, M, K, N, threshold):
+    torch, lm = dev
+    say(f"case fp8 layer M={M} K={K} N={N} threshold={threshold}")
+    X, W, _ = workloads.random_case(M, K, N, seed=3 * M + K + N, n_out=3)
+    check_fp8_layer(torch, lm, X, W, threshold)
+
+
+def test_fp8_layer_bias_and_column_absmax(dev):
+    torch, lm = dev
+    say("case fp8 layer with bias and Y column absmax")
+    X, W, _ = workloads.random_case(300, 1024, 264, seed=5, n_out=3)
+    b = (np.random.default_rng(2).standard_normal(264) * 0.5).astype(np.float16)
+    check_fp8_layer(torch, lm, X, W, 6.0, bias=b)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise_fp8(Wd)
+    ycm = torch.full((264,), 1e30, dtype=torch.float32, device="cuda")
+    Y = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, 6.0, y_col_absmax=ycm)
+    torch.cuda.synchronize()
+    assert np.array_equal(ycm.cpu().numpy(),
+                          np.abs(Y.cpu().numpy().astype(np.float32)).max(axis=0))
+
+
+def test_fp8_workload_sampled(dev):
+    torch, lm = dev
+    wl = workloads.WORKLOADS["prefill"]
+    say("case fp8 layer on the prefill workload (sampled rows)")
+    X, W = workloads.make_x(wl), workloads.make_w(wl)
+    n = check_fp8_layer(torch, lm, X, W, wl.threshold, rows=sample_rows(wl.M))
+    assert n >= len(workloads.planted_columns(wl))
+    torch.cuda.empty_cache()
