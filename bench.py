@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -45,11 +46,19 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc", f)
                             "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that editing a comment
+    does not mark the counters as taken on a different kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -53,9 +53,9 @@ __device__ inline int quant_i8(float x, float inv) {
 
 // The two 8-bit encodings of the layer. Each maps t = x * fl32(qmax / absmax)
 // to a code byte: int8 rounds half to even and clamps to [-127, 127]; E4M3
-// (the FP8 format of the INT8/FP8 page, sections 2 and 4: 4 exponent bits,
-// 3 mantissa bits, largest value 448) takes the nearest value, ties to even,
-// by the hardware conversion. |t| never exceeds qmax by more than the fp32
+// (the FP8 format of the "INT8 vs FP8 vs GPTQ" page, sections 2 and 4: 4
+// exponent bits, 3 mantissa bits, largest value 448) takes the nearest value,
+// ties to even, by the hardware conversion. |t| never exceeds qmax by more than the fp32
 // rounding of the scale, which both encodings take to +-qmax.
 struct CodecI8 {
   static constexpr double kQmax = 127.0;

@@ -208,9 +208,10 @@ int llmint8_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t l
 
 /*
  * FP8 (E4M3) variant of the decomposition: the same outlier split, with the
- * 8-bit part coded in E4M3 instead of int8 (the INT8/FP8 page, CSDN, sections
- * 2 and 4: FP8 E4M3 has 4 exponent and 3 mantissa bits, its largest value is
- * about 448, and wide-ranged inputs need a scale before the cast). E4M3 here
+ * 8-bit part coded in E4M3 instead of int8 (the "INT8 vs FP8 vs GPTQ" page,
+ * mlqm.cn, sections 2 and 4: FP8 E4M3 has 4 exponent and 3 mantissa bits, its
+ * largest value is about 448, and wide-ranged inputs need a scale before the
+ * cast). E4M3 here
  * is the OCP 8-bit format: bias 7, subnormals, no infinities, 0x7f/0xff NaN.
  *   codes:  q = e4m3(x * fl32(448 / absmax)), nearest value, ties to even;
  *           absmax per row of X (outlier columns excluded) and per column of W,

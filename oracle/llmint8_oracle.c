@@ -30,7 +30,7 @@
  *        need not be).
  *   [P5] also section 2 (the traditional 8-bit quantization uses one scale for
  *        the whole matrix).
- *   [P4] "Model quantization in practice: INT8 vs FP8" (CSDN) sections 2 and 4
+ *   [P4] "INT8 vs FP8 vs GPTQ" page (mlqm.cn) sections 2 and 4 (二, 四)
  *        (FP8 E4M3: 4 exponent bits, 3 mantissa bits, largest value about 448;
  *        an alternative to INT8 at the same 8-bit size; wide-ranged activations
  *        need a scale before the cast).

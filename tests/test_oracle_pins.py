@@ -390,9 +390,9 @@ def test_bias_is_added_after_the_rescale():
 
 
 # --- FP8 (E4M3) variant ------------------------------------------------------------
-# The INT8/FP8 page (CSDN, sections 2 and 4): E4M3 has 4 exponent bits and 3
-# mantissa bits, its largest value is about 448, and wide-ranged activations
-# need a scale before the cast.
+# The "INT8 vs FP8 vs GPTQ" page (mlqm.cn, sections 2 and 4): E4M3 has 4
+# exponent bits and 3 mantissa bits, its largest value is about 448, and
+# wide-ranged activations need a scale before the cast.
 
 def test_e4m3_format_facts():
     codes = np.arange(256, dtype=np.uint8)
