@@ -88,12 +88,47 @@ double wave_fill(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t cus) {
 // operand bytes per MFMA and runs 4 waves; measured on the 7B, 13B and 70B
 // shapes it is 3-10% slower even where its waves are 90% full against 67%,
 // so it is taken as 30% slower.
-bool narrow_tiles(int64_t M, int64_t N) {
+int cu_count() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
+  return cus;
+}
+
+bool narrow_tiles(int64_t M, int64_t N, int cus) {
   return 0.7 * wave_fill(M, N, 256, 128, cus) > wave_fill(M, N, 256, 256, cus);
+}
+
+// Columns [0, n1) of the output in whole waves of 256x256 tiles, or 0 when
+// splitting does not pay. The last wave of a 256x256 launch runs
+// tiles % cus blocks while the rest of the chip idles; putting the columns of
+// those tiles into a second launch of 256x128 tiles (half the work each, in
+// one wave) turns that wave into about half a wave plus the launch gap.
+int64_t wide_columns(int64_t M, int64_t N, int cus) {
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int64_t tiles = tm * tn, full_waves = tiles / cus;
+  if (full_waves == 0 || tiles % cus == 0) return 0;
+  const int64_t tn1 = full_waves * cus / tm;  // tile columns of the full waves
+  if (tn1 <= 0 || tn1 >= tn) return 0;
+  const int64_t n1 = tn1 * 256;
+  const int64_t narrow_blocks = tm * ((N - n1 + 127) / 128);
+  return narrow_blocks <= cus ? n1 : 0;
+}
+
+// The same GEMM restricted to output columns [n0, n0 + ncols).
+GemmArgs column_slice(const GemmArgs &a, int64_t n0, int64_t ncols) {
+  GemmArgs b = a;
+  b.wq = a.wq + n0 * a.K;
+  b.wqc = a.wqc ? a.wqc + n0 * a.ldq : nullptr;
+  b.s = a.s + n0;
+  b.wot = a.wot ? a.wot + n0 * a.ldo : nullptr;
+  b.y = a.y + n0;
+  b.cdbg = a.cdbg ? a.cdbg + n0 : nullptr;
+  if (a.ep.bias) b.ep.bias = a.ep.bias + n0;
+  if (a.ep.ycmax) b.ep.ycmax = a.ep.ycmax + n0;
+  b.N = ncols;
+  return b;
 }
 
 }  // namespace
@@ -120,9 +155,18 @@ hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t
                 : launch_prefill<256, 256, W, S, false, false>(a, ev, stream);
 }
 
-hipError_t launch_gemm(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return narrow_tiles(a.M, a.N) ? launch_gemm_narrow(a, ev, stream)
-                                : launch_gemm_wide(a, ev, stream);
+hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream) {
+  GemmArgs a = args;
+  if (a.ldc == 0) a.ldc = a.N;
+  const int cus = cu_count();
+  if (narrow_tiles(a.M, a.N, cus)) return launch_gemm_narrow(a, ev, stream);
+  const int64_t n1 = wide_columns(a.M, a.N, cus);
+  if (n1 == 0) return launch_gemm_wide(a, ev, stream);
+  // the begin event goes with the first launch, the end event with the second
+  const hipError_t e =
+      launch_gemm_wide(column_slice(a, 0, n1), GemmEvents{ev.begin, nullptr}, stream);
+  if (e != hipSuccess) return e;
+  return launch_gemm_narrow(column_slice(a, n1, a.N - n1), GemmEvents{nullptr, ev.end}, stream);
 }
 
 }  // namespace llmint8

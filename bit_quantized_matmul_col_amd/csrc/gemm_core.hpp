@@ -409,13 +409,13 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
         const bool colok = n0 + cl < a.N;
         int64_t rows = a.M - m0;
         rows = rows < BM ? rows : BM;
-        const rsrc_t rc = make_rsrc(a.cdbg + m0 * a.N, rows * a.N * 4);
+        const rsrc_t rc = make_rsrc(a.cdbg + m0 * a.ldc, rows * a.ldc * 4);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
           if (colok)
             __builtin_amdgcn_raw_buffer_store_b32(acc[mi * NI + ni][r], rc,
-                                                  (rl * (int)a.N + (int)(n0 + cl)) * 4, 0, 0);
+                                                  (rl * (int)a.ldc + (int)(n0 + cl)) * 4, 0, 0);
         }
       }
       acc[mi * NI + ni] = __builtin_bit_cast(i32x16, f);

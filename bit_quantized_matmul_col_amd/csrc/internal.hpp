@@ -108,6 +108,7 @@ struct GemmArgs {
   int64_t M, N, K, ldq, ldo, ldw, ldy;
   EpilogueOpts ep;
   int fp8;               // xq and wq hold E4M3 codes instead of int8 ones
+  int64_t ldc;           // row pitch of cdbg (0: N)
 };
 
 // Caller-supplied events (may be null) that the GEMM kernel's own dispatch
@@ -118,7 +119,8 @@ struct GemmEvents {
 };
 
 // Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
-// tile shape (256x256 or 256x128) from the problem size.
+// tile shapes (256x256, 256x128, or whole waves of 256x256 tiles followed by
+// the remaining columns in 256x128 tiles) from the problem size.
 hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);

@@ -420,14 +420,17 @@ void ora_quantize_rowwise_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t l
 void ora_gemm_fp8(const uint8_t *Xq8, const uint8_t *Wq8, int64_t M, int64_t N, int64_t K,
                   double *C)
 {
+    double value[256]; /* ora_e4m3_value of every code, looked up below */
+    for (int c = 0; c < 256; ++c)
+        value[c] = ora_e4m3_value((uint8_t)c);
     double *xv = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t k = 0; k < K; ++k)
-            xv[k] = ora_e4m3_value(Xq8[i * K + k]);
+            xv[k] = value[Xq8[i * K + k]];
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
-                acc += xv[k] * ora_e4m3_value(Wq8[n * K + k]);
+                acc += xv[k] * value[Wq8[n * K + k]];
             C[i * N + n] = acc;
         }
     }

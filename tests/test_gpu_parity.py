@@ -526,7 +526,7 @@ def test_fp8_colwise_codes(dev, K, N):
     assert np.array_equal(Wq.cpu().numpy(), ref_q)
 
 
-def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None):
+def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None, ycmax=False):
     M, K = X.shape
     N = W.shape[1]
     Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
@@ -536,7 +536,9 @@ def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None
     C = torch.empty((M, N), dtype=torch.float32, device="cuda")
     cnt = torch.empty(1, dtype=torch.int32, device="cuda")
     bd = to_gpu(torch, bias) if bias is not None else None
-    Y = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, threshold, C_debug=C, outlier_count=cnt, bias=bd)
+    ycm = torch.full((N,), 1e30, dtype=torch.float32, device="cuda") if ycmax else None
+    Y = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, threshold, C_debug=C, outlier_count=cnt, bias=bd,
+                              y_col_absmax=ycm)
     Yp = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, threshold, bias=bd)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Yp.view(torch.int16)), "debug/production Y differ"
@@ -552,6 +554,9 @@ def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None
     assert np.all(err <= (2.0 ** -12 + K * 2.0 ** -30) * mag + 1e-30), f"C error {err.max():.3g}"
     Yr = ref["Y"] if bias is None else oracle.add_bias(ref["Y"], bias)
     assert_y_close(y, Yr, "fp8 Y")
+    if ycmax:
+        assert np.array_equal(ycm.cpu().numpy(),
+                              np.abs(Y.cpu().numpy().astype(np.float32)).max(axis=0))
     return int(cnt.item())
 
 
@@ -591,3 +596,33 @@ def test_fp8_workload_sampled(dev):
     n = check_fp8_layer(torch, lm, X, W, wl.threshold, rows=sample_rows(wl.M))
     assert n >= len(workloads.planted_columns(wl))
     torch.cuda.empty_cache()
+
+
+# --- the large-M GEMM in two launches ------------------------------------------------------
+# 2304 x 7432 outputs make 9 x 30 = 270 tiles of 256 x 256 on 256 CUs: the
+# first 28 tile columns (252 tiles) run as one launch and the remaining 264
+# columns (ragged) as 256 x 128 tiles in a second launch. Every output, the
+# int32 accumulators, the bias and the Y column maxima cross that boundary.
+
+@pytest.mark.parametrize("variant", ["int8", "fp8"])
+def test_gemm_split_into_wide_and_narrow_launches(dev, variant):
+    torch, lm = dev
+    M, K, N = 2304, 64, 7432
+    say(f"case GEMM split into two launches {variant} M={M} K={K} N={N}")
+    X, W, _ = workloads.random_case(M, K, N, seed=17, n_out=2)
+    b = (np.random.default_rng(4).standard_normal(N) * 0.5).astype(np.float16)
+    Xd, Wd, bd = to_gpu(torch, X), to_gpu(torch, W), to_gpu(torch, b)
+    ycm = torch.full((N,), 1e30, dtype=torch.float32, device="cuda")
+    if variant == "int8":
+        Wq, s = lm.llmint8_quantize_colwise(Wd)
+        C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        Y = lm.llmint8_linear(Xd, Wq, s, Wd, 6.0, C_debug=C, bias=bd, y_col_absmax=ycm)
+        ref = oracle.linear(X, W, 6.0, bias=b)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), ref["C"]), "C differs"
+    else:
+        check_fp8_layer(torch, lm, X, W, 6.0, bias=b, ycmax=True)
+        return
+    y = Y.cpu().numpy()
+    assert_y_close(y, ref["Y"], "Y")
+    assert np.array_equal(ycm.cpu().numpy(), np.abs(y.astype(np.float32)).max(axis=0))
