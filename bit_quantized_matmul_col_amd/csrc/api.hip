@@ -406,7 +406,7 @@ LLMINT8_EXPORT int llmint8_quantize_rowwise_fp8(const uint16_t *X, int64_t M, in
 
 LLMINT8_EXPORT size_t llmint8_linear_fp8_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
-  return make_layout(M, K, N, true, true).total;
+  return make_layout(M, K, N, true).total;
 }
 
 LLMINT8_EXPORT int llmint8_linear_fp8(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
@@ -432,12 +432,26 @@ LLMINT8_EXPORT int llmint8_linear_fp8(const uint16_t *X, int64_t M, int64_t K, i
   if ((outlier_count_out && !aligned16(outlier_count_out)) || (C_debug && !aligned16(C_debug)))
     return LLMINT8_ERR_UNSUPPORTED;
   if (ldy >= kMaxTileLd || N >= kMaxTileLd) return LLMINT8_ERR_UNSUPPORTED;
-  const Layout L = make_layout(M, K, N, true, true);
+  const Layout L = make_layout(M, K, N, true);
   if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
   const GemmEvents ev{o.gemm_begin_event, o.gemm_end_event};
   const EpilogueOpts ep{0, o.bias, o.y_col_absmax};
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  if (M <= kDecodeMaxM) {
+    const DecodePlan dp = decode_plan(M, K, N);
+    const int64_t kw = (K + 31) / 32;
+    uint32_t *omask = (uint32_t *)(ws + L.omask);
+    float *pmax = (float *)(ws + L.pmask);
+    DecodeDetectArgs det{X, (int)M, K, ldx, kw, threshold, omask, pmax, o.x_col_absmax,
+                         o.y_col_absmax, N};
+    DecodeGemmArgs g{X, (const int8_t *)Wq8, col_absmax, omask, pmax, W, (int32_t *)(ws + L.part),
+                     (float *)(ws + L.m), outlier_count_out, Y, (int32_t *)C_debug,
+                     M, N, K, kw, dp.kc, ldx, ldw, ldy, dp.det_blocks, dp.kb, ep, 1};
+    return hip_status(launch_decode(det, g, dp, ev, s));
+  }
   return hip_status(prefill_layer(X, M, K, ldx, (const int8_t *)Wq8, col_absmax, W, ldw, N,
                                   threshold, Y, ldy, outlier_count_out, (int32_t *)C_debug,
-                                  (uint8_t *)workspace, L, o, ev, ep, true, (hipStream_t)stream));
+                                  ws, L, o, ev, ep, true, s));
 }

@@ -158,8 +158,22 @@ __device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st,
   }
 }
 
+// Four E4M3 codes of the fp16 pairs (w0, w1) for the scale inv = fl32(448 /
+// absmax): the fp32 products, then the hardware conversion (nearest, ties to
+// even).
+__device__ inline uint32_t codes4_e4m3(uint32_t w0, uint32_t w1, float inv) {
+#pragma clang fp contract(off)
+  const float t[4] = {fp16_lo(w0) * inv, fp16_hi(w0) * inv, fp16_lo(w1) * inv,
+                      fp16_hi(w1) * inv};
+  return CodecE4M3::code4(t);
+}
+
 // Quantize the stage's X chunks into LDS, then contract them with the Wq bytes.
-template <int MB>
+// F8: E4M3 codes and v_mfma_f32_16x16x128_f8f6f4, which takes the Wq bytes of
+// two consecutive int8 steps (j = 2 jj, 2 jj + 1) per lane and the X codes of
+// the same k, so both operands see the same k in every slot; the fp32 sums
+// are kept as raw bits in the int32 accumulators.
+template <int MB, bool F8>
 __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const float *sinv,
                                    i32x4 *acc, int wv, int lane, int c16, int g) {
   __syncthreads();  // sinv ready; the previous stage's MFMAs are done with sx
@@ -170,19 +184,43 @@ __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const
     const int row = wv + 4 * u;
     const float inv = sinv[row];
     u32x2 out;
-    out[0] = codes4(st.x[u][0], st.x[u][1], inv) & keep_lo;
-    out[1] = codes4(st.x[u][2], st.x[u][3], inv) & keep_hi;
+    if constexpr (F8) {
+      out[0] = codes4_e4m3(st.x[u][0], st.x[u][1], inv) & keep_lo;
+      out[1] = codes4_e4m3(st.x[u][2], st.x[u][3], inv) & keep_hi;
+    } else {
+      out[0] = codes4(st.x[u][0], st.x[u][1], inv) & keep_lo;
+      out[1] = codes4(st.x[u][2], st.x[u][3], inv) & keep_hi;
+    }
     *(u32x2 *)(sx + row * kXPitch + 8 * lane) = out;
   }
   __syncthreads();
+  if constexpr (F8) {
 #pragma unroll
-  for (int j = 0; j < kSubK / 64; ++j)
+    for (int jj = 0; jj < kSubK / 128; ++jj) {
+      i32x8 bv;
+      bv.lo = __builtin_bit_cast(i32x4, st.b[2 * jj]);
+      bv.hi = __builtin_bit_cast(i32x4, st.b[2 * jj + 1]);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const i32x4 av = *(const i32x4 *)(sx + (mb * 16 + c16) * kXPitch + 64 * j + 16 * g);
-      acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4, st.b[j]),
-                                                       acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint8_t *xr = sx + (mb * 16 + c16) * kXPitch + 16 * g;
+        i32x8 av;
+        av.lo = *(const i32x4 *)(xr + 128 * jj);
+        av.hi = *(const i32x4 *)(xr + 128 * jj + 64);
+        acc[mb] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                       av, bv, __builtin_bit_cast(f32x4, acc[mb]), 0, 0, 0, 0, 0, 0));
+      }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSubK / 64; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const i32x4 av = *(const i32x4 *)(sx + (mb * 16 + c16) * kXPitch + 64 * j + 16 * g);
+        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4, st.b[j]),
+                                                         acc[mb], 0, 0, 0);
+      }
+  }
 }
 
 // Block (tile, kb). Wave w owns 16 output columns; lane (c16 = l % 16,
@@ -193,7 +231,7 @@ __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const
 // count. Two register stages alternate so that the next stage's loads are in
 // flight while the current one is quantized and contracted; no load is issued
 // under a branch that the following waits would have to merge.
-template <int MB, int NST>
+template <int MB, int NST, bool F8>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sx[MB * 16 * kXPitch];
   __shared__ float spart[4][64];
@@ -233,7 +271,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   if (t < 64) {
     const float mx = __builtin_fmaxf(__builtin_fmaxf(spart[0][t], spart[1][t]),
                                      __builtin_fmaxf(spart[2][t], spart[3][t]));
-    sinv[t] = (t < a.M && mx > 0.f) ? inv_scale(mx) : 0.f;
+    sinv[t] = (t < a.M && mx > 0.f) ? (F8 ? inv_scale_of<CodecE4M3>(mx) : inv_scale(mx)) : 0.f;
     if (kb == 0 && blockIdx.x == 0 && t < a.M) a.m[t] = mx;
   }
 
@@ -242,26 +280,26 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (i32x4){0, 0, 0, 0};
 
   if constexpr (NST == 1) {
-    decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+    decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
   } else if constexpr (NST == 2) {
-    decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
-    decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
+    decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
+    decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
   } else {
     const int nst = (int)((k_end - k_begin + kSubK - 1) / kSubK);
     int64_t k0 = k_begin;
     int i = 0;
     for (; i + 2 < nst; i += 2, k0 += 2 * kSubK) {  // stages i + 1 and i + 2 exist
       decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
-      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
       decode_load<MB>(a, s0, k0 + 2 * kSubK, k_end, brow, wv, lane, g);
-      decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
     }
     if (nst - i == 2) {
       decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
-      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
-      decode_step<MB>(s1, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
     } else {
-      decode_step<MB>(s0, sx, sinv, acc, wv, lane, c16, g);
+      decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
     }
   }
 
@@ -278,8 +316,9 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
 }
 
 // Block (tile, row group of 16): 64 columns x 16 rows, 4 outputs per thread
-// (rows wv + 4 i, column lane). KB is the number of K splits.
-template <int KB>
+// (rows wv + 4 i, column lane). KB is the number of K splits; F8: the partial
+// sums are fp32 (added in split order) and the dequantization is / 448^2.
+template <int KB, bool F8>
 __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   __shared__ int slist[kListWords * 32];             // outlier columns of one window
   __shared__ int swsum[4];
@@ -313,15 +352,22 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   uint32_t mw = outl ? __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0) : 0u;
 
   float y[4], yo[4] = {0.f, 0.f, 0.f, 0.f};
-  const float sd = scol * (1.0f / 16129.0f);
+  const float sd = scol * (F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int cacc = 0;
+    float cf = 0.f;
 #pragma unroll
-    for (int k = 0; k < KB; ++k) cacc += pp[i][k];
+    for (int k = 0; k < KB; ++k) {
+      if constexpr (F8)
+        cf += __builtin_bit_cast(float, pp[i][k]);
+      else
+        cacc += pp[i][k];
+    }
     const int row = rbase + wv + 4 * i;
-    if (a.cdbg && row < a.M && colok) a.cdbg[(int64_t)row * a.N + col] = cacc;
-    y[i] = (float)cacc * (mrow[i] * sd);
+    if (a.cdbg && row < a.M && colok)
+      a.cdbg[(int64_t)row * a.N + col] = F8 ? __builtin_bit_cast(int, cf) : cacc;
+    y[i] = (F8 ? cf : (float)cacc) * (mrow[i] * sd);
   }
 
   // fp16 outlier terms, outlier columns in ascending order (yo: with int8
@@ -430,28 +476,48 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   }
 }
 
-template <int MB>
+template <int MB, bool F8>
 hipError_t launch_decode_gemm(const DecodeGemmArgs &a, int tiles, int kb, const GemmEvents &ev,
                               hipStream_t stream) {
   const int64_t nst = (a.kc + kSubK - 1) / kSubK;
   const hipEvent_t b = (hipEvent_t)ev.begin, e = (hipEvent_t)ev.end;
   if (nst == 1)
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 1>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
-                          a);
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 1, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
+                          0u, a);
   else if (nst == 2)
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 2>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
-                          a);
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 2, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
+                          0u, a);
   else
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 0>), dim3(tiles, kb), dim3(256), 0, stream, b, e, 0u,
-                          a);
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 0, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
+                          0u, a);
   return hipGetLastError();
 }
 
-template <int KB>
+template <int KB, bool F8>
 hipError_t launch_decode_epilogue(const DecodeGemmArgs &a, int tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((k_decode_epilogue<KB>), dim3(tiles, (unsigned)((a.M + 15) / 16)), dim3(256),
-                     0, stream, a);
+  hipLaunchKernelGGL((k_decode_epilogue<KB, F8>), dim3(tiles, (unsigned)((a.M + 15) / 16)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool F8>
+hipError_t launch_decode_kernels(const DecodeGemmArgs &gemm, const DecodePlan &plan,
+                                 const GemmEvents &ev, hipStream_t stream) {
+  hipError_t e;
+  switch ((int)((gemm.M + 15) / 16)) {
+    case 1: e = launch_decode_gemm<1, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    case 2: e = launch_decode_gemm<2, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    case 3: e = launch_decode_gemm<3, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
+    default: e = launch_decode_gemm<4, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  switch (plan.kb) {
+    case 1: return launch_decode_epilogue<1, F8>(gemm, plan.tiles, stream);
+    case 2: return launch_decode_epilogue<2, F8>(gemm, plan.tiles, stream);
+    case 4: return launch_decode_epilogue<4, F8>(gemm, plan.tiles, stream);
+    case 8: return launch_decode_epilogue<8, F8>(gemm, plan.tiles, stream);
+    default: return launch_decode_epilogue<16, F8>(gemm, plan.tiles, stream);
+  }
 }
 
 }  // namespace
@@ -477,23 +543,10 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream) {
   hipLaunchKernelGGL(k_decode_detect, dim3(plan.det_blocks), dim3(256), 0, stream, det);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int mb = (int)((gemm.M + 15) / 16);
-  switch (mb) {
-    case 1: e = launch_decode_gemm<1>(gemm, plan.tiles, plan.kb, ev, stream); break;
-    case 2: e = launch_decode_gemm<2>(gemm, plan.tiles, plan.kb, ev, stream); break;
-    case 3: e = launch_decode_gemm<3>(gemm, plan.tiles, plan.kb, ev, stream); break;
-    default: e = launch_decode_gemm<4>(gemm, plan.tiles, plan.kb, ev, stream); break;
-  }
-  if (e != hipSuccess) return e;
-  switch (plan.kb) {
-    case 1: return launch_decode_epilogue<1>(gemm, plan.tiles, stream);
-    case 2: return launch_decode_epilogue<2>(gemm, plan.tiles, stream);
-    case 4: return launch_decode_epilogue<4>(gemm, plan.tiles, stream);
-    case 8: return launch_decode_epilogue<8>(gemm, plan.tiles, stream);
-    default: return launch_decode_epilogue<16>(gemm, plan.tiles, stream);
-  }
+  return gemm.fp8 ? launch_decode_kernels<true>(gemm, plan, ev, stream)
+                  : launch_decode_kernels<false>(gemm, plan, ev, stream);
 }
 
 }  // namespace llmint8

@@ -103,8 +103,10 @@ bool narrow_tiles(int64_t M, int64_t N, int cus) {
 // Columns [0, n1) of the output in whole waves of 256x256 tiles, or 0 when
 // splitting does not pay. The last wave of a 256x256 launch runs
 // tiles % cus blocks while the rest of the chip idles; putting the columns of
-// those tiles into a second launch of 256x128 tiles (half the work each, in
-// one wave) turns that wave into about half a wave plus the launch gap.
+// those tiles into a second launch of 128x256 tiles (half the work each, still
+// two waves per SIMD, in one wave) turns that wave into about half a wave plus
+// the launch gap. (256x128 tiles with one wave per SIMD measured 0.63 of a
+// full wave for the same half of the work.)
 int64_t wide_columns(int64_t M, int64_t N, int cus) {
   const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
   const int64_t tiles = tm * tn, full_waves = tiles / cus;
@@ -112,8 +114,8 @@ int64_t wide_columns(int64_t M, int64_t N, int cus) {
   const int64_t tn1 = full_waves * cus / tm;  // tile columns of the full waves
   if (tn1 <= 0 || tn1 >= tn) return 0;
   const int64_t n1 = tn1 * 256;
-  const int64_t narrow_blocks = tm * ((N - n1 + 127) / 128);
-  return narrow_blocks <= cus ? n1 : 0;
+  const int64_t tail_blocks = ((M + 127) / 128) * ((N - n1 + 255) / 256);
+  return tail_blocks <= cus ? n1 : 0;
 }
 
 // The same GEMM restricted to output columns [n0, n0 + ncols).
@@ -166,7 +168,7 @@ hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t s
   const hipError_t e =
       launch_gemm_wide(column_slice(a, 0, n1), GemmEvents{ev.begin, nullptr}, stream);
   if (e != hipSuccess) return e;
-  return launch_gemm_narrow(column_slice(a, n1, a.N - n1), GemmEvents{nullptr, ev.end}, stream);
+  return launch_gemm_tail(column_slice(a, n1, a.N - n1), GemmEvents{nullptr, ev.end}, stream);
 }
 
 }  // namespace llmint8

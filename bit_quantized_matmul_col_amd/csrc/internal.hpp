@@ -120,10 +120,11 @@ struct GemmEvents {
 
 // Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
 // tile shapes (256x256, 256x128, or whole waves of 256x256 tiles followed by
-// the remaining columns in 256x128 tiles) from the problem size.
+// the remaining columns in 128x256 tiles) from the problem size.
 hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
+hipError_t launch_gemm_tail(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 
 // Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
 // its slice of X itself.
@@ -155,6 +156,7 @@ struct DecodeGemmArgs {
   int det_blocks;
   int kb;             // K splits (partial sums per output)
   EpilogueOpts ep;
+  int fp8;            // E4M3 codes of X and Wq (fp32 partial sums) instead of int8
 };
 
 struct DecodePlan {

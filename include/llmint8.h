@@ -136,7 +136,7 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
  *       the kernel starts and when it completes (no separate stream commands),
  *       so a caller can time the dominant kernel of the layer with
  *       hipEventElapsedTime. When the GEMM runs as two launches (whole waves
- *       of 256x256 tiles, then the remaining columns in 256x128 tiles), the
+ *       of 256x256 tiles, then the remaining columns in 128x256 tiles), the
  *       first launch stamps the begin event and the second the end event.
  *   outlier_weights  LLMINT8_OUTLIER_W_FP16 (default) or LLMINT8_OUTLIER_W_INT8:
  *       keep only the int8 weight (walkthrough page, sections 2.4 and 6: the
@@ -229,8 +229,9 @@ int llmint8_linear_tensorwise(const uint16_t *X, int64_t M, int64_t K, int64_t l
  *   Wq8 [N x K] uint8 E4M3 codes; col_absmax [N] fp32.
  * llmint8_quantize_rowwise_fp8: as llmint8_quantize_rowwise, E4M3 codes.
  *   Xq8 [M x K] uint8 E4M3 codes (0 on outlier columns); row_absmax [M] fp32.
- * llmint8_linear_fp8: the whole FP8 layer, any M (the large-M kernels), with
- *   the arguments of llmint8_linear_ex except:
+ * llmint8_linear_fp8: the whole FP8 layer (small-M and large-M paths as for
+ *   llmint8_linear, without the single-kernel one), with the arguments of
+ *   llmint8_linear_ex except:
  *   Wq8, col_absmax  from llmint8_quantize_colwise_fp8;
  *   C_debug    optional [M x N] fp32 output (leading dimension N): C;
  *   workspace  at least llmint8_linear_fp8_workspace_size(M, K, N) bytes;

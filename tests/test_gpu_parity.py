@@ -601,7 +601,7 @@ def test_fp8_workload_sampled(dev):
 # --- the large-M GEMM in two launches ------------------------------------------------------
 # 2304 x 7432 outputs make 9 x 30 = 270 tiles of 256 x 256 on 256 CUs: the
 # first 28 tile columns (252 tiles) run as one launch and the remaining 264
-# columns (ragged) as 256 x 128 tiles in a second launch. Every output, the
+# columns (ragged) as 128 x 256 tiles in a second launch. Every output, the
 # int32 accumulators, the bias and the Y column maxima cross that boundary.
 
 @pytest.mark.parametrize("variant", ["int8", "fp8"])
