@@ -9,8 +9,8 @@
 // (clamped address, result masked afterwards) so that all of a thread's loads are in
 // flight before its first wait.
 //
-// k_decode_detect: block b owns 256 columns of X over all M rows. It writes the
-//   outlier bits of its columns (8 mask words) and, per row, the absmax over
+// k_decode_detect: block b owns 128 columns of X over all M rows. It writes the
+//   outlier bits of its columns (4 mask words) and, per row, the absmax over
 //   its kept columns; the row absmax over all kept columns is the max of these.
 // k_decode_gemm: block (tile, kb) owns 64 output columns and one K range. It
 //   reduces the partial maxima to m[i], quantizes its slice of X into LDS while
@@ -24,8 +24,10 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int kDetCols = 256;      // columns per detection block
-constexpr int kDetRows = 8;        // row phases per detection block (32 x 8 threads)
+constexpr int kDetCols = 128;      // columns per detection block (256: 1.2 us slower per step)
+constexpr int kDetChunks = kDetCols / 8;            // 16-byte column chunks per block
+constexpr int kDetRows = 256 / kDetChunks;          // row phases per detection block
+constexpr int kDetRowIters = kDecodeMaxM / kDetRows;  // rows per thread
 constexpr int kTileN = 64;         // output columns per GEMM / epilogue block
 constexpr int kSubK = 512;         // k bytes staged per GEMM stage
 constexpr int kXPitch = kSubK + 16;
@@ -38,26 +40,27 @@ constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
 __device__ inline u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
 
 __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
+  static_assert(kDetCols % 64 == 0, "whole waves of column flags");
   __shared__ float scol[kDetRows][kDetCols];
   __shared__ uint32_t sflag[kDetCols / 32];
   const int t = threadIdx.x;
-  const int c = t & 31, ph = t >> 5;
+  const int c = t % kDetChunks, ph = t / kDetChunks;
   const int64_t col0 = (int64_t)blockIdx.x * kDetCols + c * 8;
   const bool colok = col0 < a.K;
   const uint16_t *base = a.X + (colok ? col0 : 0);
   if (a.ycmax)  // the epilogue's column maxima start from zero
-    for (int64_t n = (int64_t)blockIdx.x * kDetCols + t; n < a.N; n += (int64_t)gridDim.x * kDetCols)
+    for (int64_t n = (int64_t)blockIdx.x * 256 + t; n < a.N; n += (int64_t)gridDim.x * 256)
       a.ycmax[n] = 0.f;
   // a caller-supplied column absmax decides the outlier columns
   float xc = 0.f;
-  if (a.xcmax) {
+  if (a.xcmax && t < kDetCols) {
     const int64_t col = (int64_t)blockIdx.x * kDetCols + t;
     xc = a.xcmax[col < a.K ? col : 0];
   }
 
-  u32x4 v[8];
+  u32x4 v[kDetRowIters];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kDetRowIters; ++j) {
     const int row = ph + kDetRows * j;
     const bool ok = colok && row < a.M;
     const u32x4 x = *(const u32x4 *)(base + (ok ? (int64_t)row * a.ldx : 0));
@@ -65,13 +68,13 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   }
   float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) absmax8(v[j], cm);
+  for (int j = 0; j < kDetRowIters; ++j) absmax8(v[j], cm);
 #pragma unroll
   for (int e = 0; e < 8; ++e) scol[ph][c * 8 + e] = cm[e];
   __syncthreads();
 
   // column t of the block: outlier when its max over all rows reaches the threshold
-  {
+  if (t < kDetCols) {  // whole waves
     float mx = 0.f;
 #pragma unroll
     for (int p = 0; p < kDetRows; ++p) mx = __builtin_fmaxf(mx, scol[p][t]);
@@ -89,10 +92,11 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
     if (w < a.kw) a.omask[w] = sflag[t];
   }
 
-  // per-row max over the block's kept columns; the 32 lanes of a row phase reduce
+  // per-row max over the block's kept columns; the kDetChunks lanes of a row
+  // phase (consecutive lanes) reduce
   const unsigned ob = (sflag[c >> 2] >> ((c & 3) * 8)) & 0xffu;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kDetRowIters; ++j) {
     const int row = ph + kDetRows * j;
     float mx = 0.f;
 #pragma unroll
@@ -101,7 +105,8 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
       mx = ((ob >> e) & 1u) ? mx : __builtin_fmaxf(mx, __builtin_fabsf(x));
     }
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
+    for (int off = kDetChunks / 2; off > 0; off >>= 1)
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
     if (c == 0 && row < a.M) a.pmax[(int64_t)blockIdx.x * a.M + row] = mx;
   }
 }
