@@ -560,8 +560,9 @@ def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None
     return int(cnt.item())
 
 
-FP8_CASES = [(1, 256, 136), (5, 4096, 520), (48, 2048, 1032), (257, 784, 520), (300, 1024, 264),
-             (700, 1008, 200)]
+# small M (split-K decode kernels, ragged K and N included) and large M
+FP8_CASES = [(1, 256, 136), (5, 4096, 520), (17, 272, 8), (48, 2048, 1032), (64, 1008, 200),
+             (65, 784, 136), (257, 784, 520), (300, 1024, 264), (700, 1008, 200)]
 
 
 @pytest.mark.parametrize("M,K,N", FP8_CASES)
