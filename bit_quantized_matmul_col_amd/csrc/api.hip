@@ -148,9 +148,10 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
                                                (uint8_t *)xq, ldq, m, xo, ldo, s)
             : launch_rowquant_layer<CodecI8>(X, M, K, ldx, omask, wprefix, count, (uint8_t *)xq,
                                              ldq, m, xo, ldo, s);
-  if (e == hipSuccess) e = launch_compact_wq(Wq, M, K, N, omask, wprefix, count, wqc, ldq, s);
-  if (e == hipSuccess && (Wf || int8w))
-    e = launch_gather_wot(Wf, ldw, Wq, K, N, idx, count, wot, ldo, s);
+  if (e == hipSuccess) {
+    const WeightSideArgs w{Wf, ldw, Wq, M, K, N, idx, count, wot, ldo, omask, wprefix, wqc, ldq, 0};
+    e = launch_weight_side(w, Wf || int8w, s);
+  }
   if (e == hipSuccess) {
     // the GEMM's outlier product runs when it has weight rows (gathered above)
     const uint16_t *wo_src = (Wf || int8w) ? wot : nullptr;

@@ -80,18 +80,27 @@ template <class Codec>
 hipError_t launch_colwise_quant(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
                                 const float *s, uint8_t *Wq, hipStream_t stream);
 
-// Compacted copy Wqc [N x K] (first K - |O| bytes of each row) of Wq without
-// the outlier columns; a no-op unless the outlier share calls for it.
-hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
-                             const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
-                             int8_t *Wqc, int64_t ldq, hipStream_t stream);
-
-// W_O^T [N x ldo] fp16: row n holds W[idx[p], n] for p < |O|, then zeros up to
-// the next multiple of 64. With W null it holds the int8 codes Wq[n, idx[p]]
-// instead (exact in fp16; the epilogue applies s[n] / 127).
-hipError_t launch_gather_wot(const uint16_t *W, int64_t ldw, const int8_t *Wq, int64_t K,
-                             int64_t N, const int32_t *idx, const int32_t *count, uint16_t *wot,
-                             int64_t ldo, hipStream_t stream);
+// Weight side of a large-M call, one launch: W_O^T [N x ldo] fp16, whose row n
+// holds W[idx[p], n] for p < |O| (or, with W null, the int8 codes Wq[n, idx[p]],
+// exact in fp16; the epilogue applies s[n] / 127), zeros up to the next
+// multiple of 64; and, when the outlier share calls for it, the compacted copy
+// Wqc [N x ldq] of Wq without the outlier columns.
+struct WeightSideArgs {
+  const uint16_t *W;      // fp16 weight [K x N] (null: gather the int8 codes)
+  int64_t ldw;
+  const int8_t *Wq;       // [N x K]
+  int64_t M, K, N;
+  const int32_t *idx;     // ascending outlier columns
+  const int32_t *count;   // [1]
+  uint16_t *wot;
+  int64_t ldo;
+  const uint32_t *omask;  // outlier bitmask
+  const int32_t *wprefix; // outliers in the mask words before w
+  int8_t *wqc;
+  int64_t ldq;
+  int64_t gather_blocks;  // set by the launcher
+};
+hipError_t launch_weight_side(const WeightSideArgs &a, bool gather, hipStream_t stream);
 
 struct GemmArgs {
   const int8_t *xq;      // [M x ldq] int8 (compacted rows when compaction is on)

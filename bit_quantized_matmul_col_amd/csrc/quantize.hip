@@ -264,49 +264,6 @@ __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W
   }
 }
 
-// Compacted copy of Wq rows without the outlier columns. One row per block
-// iteration: each thread compresses 32 bytes (one mask word) into LDS, then
-// the row goes out with 16-byte stores, its tail zeroed up to 16 bytes.
-__global__ __launch_bounds__(256) void k_compact_wq(const int8_t *__restrict__ Wq, int64_t M,
-                                                    int64_t K, int64_t N,
-                                                    const uint32_t *__restrict__ omask,
-                                                    const int32_t *__restrict__ wprefix,
-                                                    const int32_t *__restrict__ count_ptr,
-                                                    int8_t *__restrict__ Wqc, int64_t ldq) {
-  extern __shared__ u32x4 srow_v[];
-  uint8_t *srow = (uint8_t *)srow_v;
-  const int count = *count_ptr;
-  if (!use_compaction(count, K, M)) return;
-  const int t = threadIdx.x;
-  const int64_t kw = (K + 31) / 32;
-  const int64_t kk = K - count;
-  const int64_t kpad = (kk + 127) / 128 * 128;
-  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-    const int8_t *row = Wq + n * K;
-    for (int64_t w = t; w < kw; w += 256) {
-      const uint32_t v = omask[w];
-      int64_t dst = 32 * w - wprefix[w];
-      const int nb = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
-      for (int h = 0; h < nb; h += 16) {
-        const u32x4 d = *(const u32x4 *)(row + 32 * w + h);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (!((v >> (h + e)) & 1u)) {
-            srow[dst] = (uint8_t)((d[e >> 2] >> (8 * (e & 3))) & 0xffu);
-            ++dst;
-          }
-        }
-      }
-    }
-    for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
-    __syncthreads();
-    int8_t *out = Wqc + n * ldq;
-    for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
-      *(u32x4 *)(out + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
-    __syncthreads();
-  }
-}
-
 }  // namespace
 
 template <class Codec>
@@ -386,14 +343,5 @@ template hipError_t launch_colwise<CodecI8>(const uint16_t *, int64_t, int64_t, 
 template hipError_t launch_colwise<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
                                               uint8_t *, float *, hipStream_t);
 
-hipError_t launch_compact_wq(const int8_t *Wq, int64_t M, int64_t K, int64_t N,
-                             const uint32_t *omask, const int32_t *wprefix, const int32_t *count,
-                             int8_t *Wqc, int64_t ldq, hipStream_t stream) {
-  if (!use_compaction((int)K, K, M)) return hipSuccess;  // never applies at this shape
-  int64_t blocks = N < 1024 ? N : 1024;
-  hipLaunchKernelGGL(k_compact_wq, dim3((unsigned)blocks), dim3(256), (size_t)ldq, stream, Wq, M,
-                     K, N, omask, wprefix, count, Wqc, ldq);
-  return hipGetLastError();
-}
 
 }  // namespace llmint8
