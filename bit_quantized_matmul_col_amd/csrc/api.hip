@@ -143,14 +143,11 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
   const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
   uint16_t *wot = (uint16_t *)(ws + L.wot);
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
-  if (e == hipSuccess)
-    e = fp8 ? launch_rowquant_layer<CodecE4M3>(X, M, K, ldx, omask, wprefix, count,
-                                               (uint8_t *)xq, ldq, m, xo, ldo, s)
-            : launch_rowquant_layer<CodecI8>(X, M, K, ldx, omask, wprefix, count, (uint8_t *)xq,
-                                             ldq, m, xo, ldo, s);
   if (e == hipSuccess) {
+    const RowQuantArgs r{X, M, K, ldx, omask, wprefix, count, (uint8_t *)xq, ldq, m, xo, ldo};
     const WeightSideArgs w{Wf, ldw, Wq, M, K, N, idx, count, wot, ldo, omask, wprefix, wqc, ldq, 0};
-    e = launch_weight_side(w, Wf || int8w, s);
+    e = fp8 ? launch_layer_prep<CodecE4M3>(r, w, Wf || int8w, s)
+            : launch_layer_prep<CodecI8>(r, w, Wf || int8w, s);
   }
   if (e == hipSuccess) {
     // the GEMM's outlier product runs when it has weight rows (gathered above)

@@ -57,18 +57,6 @@ hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t 
                                const int32_t *idx, const int32_t *count, uint8_t *Xq, float *m,
                                hipStream_t stream);
 
-// Row quantization inside the layer: outlier columns from the detection
-// bitmask; also gathers the outlier columns into xo [M x ldo] and, when the
-// outlier share calls for it, writes compacted rows (K - |O| kept columns).
-// Xq rows have pitch ldq (a multiple of 128) and are zero past their last
-// column up to the next multiple of 128; xo rows have pitch ldo (a multiple of
-// 64) and are zero from |O| up to the next multiple of 64.
-template <class Codec>
-hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                                 const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, uint8_t *Xq, int64_t ldq, float *m,
-                                 uint16_t *xo, int64_t ldo, hipStream_t stream);
-
 // Column absmax + quantize + transpose of W [K x N] into Wq [N x K]; the two
 // halves also run alone (s: column maxima out, then the scales the codes use).
 template <class Codec>
@@ -100,7 +88,31 @@ struct WeightSideArgs {
   int64_t ldq;
   int64_t gather_blocks;  // set by the launcher
 };
-hipError_t launch_weight_side(const WeightSideArgs &a, bool gather, hipStream_t stream);
+
+// Row quantization inside the layer: outlier columns from the detection
+// bitmask; also gathers the outlier columns into xo [M x ldo] and, when the
+// outlier share calls for it, writes compacted rows (K - |O| kept columns).
+// Xq rows have pitch ldq (a multiple of 128) and are zero past their last
+// column up to the next multiple of 128; xo rows have pitch ldo (a multiple of
+// 64) and are zero from |O| up to the next multiple of 64.
+struct RowQuantArgs {
+  const uint16_t *X;
+  int64_t M, K, ldx;
+  const uint32_t *omask;
+  const int32_t *wprefix;
+  const int32_t *count;
+  uint8_t *Xq;
+  int64_t ldq;
+  float *m;
+  uint16_t *xo;
+  int64_t ldo;
+};
+
+// Row quantization and the weight side of a large-M call in one launch
+// (gather: the outlier product needs W_O^T).
+template <class Codec>
+hipError_t launch_layer_prep(const RowQuantArgs &r, const WeightSideArgs &w, bool gather,
+                             hipStream_t stream);
 
 struct GemmArgs {
   const int8_t *xq;      // [M x ldq] int8 (compacted rows when compaction is on)

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
   }
 }
 
-// Row quantization inside the layer. One block per row. Besides Xq and m it
+// Row quantization inside the layer, row i (one block). Besides Xq and m it
 // gathers the row's outlier entries into xo (position = rank of the column in
 // the ascending outlier list) and, in compaction mode, writes the kept codes
 // contiguously (staged in LDS so the global stores stay 16-byte wide). Rows of
@@ -101,19 +101,18 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
 // 128 bytes and rows of xo (pitch ldo) from |O| up to the next multiple of 64,
 // so the GEMM can run whole 128-byte k stages.
 template <class Codec>
-__global__ __launch_bounds__(256) void k_rowquant_layer(
-    const uint16_t *__restrict__ X, int64_t M, int64_t K, int64_t ldx,
-    const uint32_t *__restrict__ omask,
-    const int32_t *__restrict__ wprefix, const int32_t *__restrict__ count_ptr,
-    uint8_t *__restrict__ Xq, int64_t ldq, float *__restrict__ m, uint16_t *__restrict__ xo,
-    int64_t ldo) {
-  extern __shared__ u32x4 srow_v[];
-  uint8_t *srow = (uint8_t *)srow_v;
+__device__ void rowquant_row(int64_t i, const RowQuantArgs &a, uint8_t *srow) {
   __shared__ float red[4];
-  const int64_t i = blockIdx.x;
+  const uint16_t *X = a.X;
+  const int64_t M = a.M, K = a.K, ldx = a.ldx, ldq = a.ldq, ldo = a.ldo;
+  const uint32_t *omask = a.omask;
+  const int32_t *wprefix = a.wprefix;
   const int t = threadIdx.x;
-  const int count = *count_ptr;
+  const int count = *a.count;
   const bool compact = use_compaction(count, K, M);
+  uint8_t *Xq = a.Xq;
+  float *m = a.m;
+  uint16_t *xo = a.xo;
 
   const uint16_t *row = X + i * ldx;
   const int64_t nch = K / 8;
@@ -167,6 +166,126 @@ __global__ __launch_bounds__(256) void k_rowquant_layer(
   } else {
     for (int64_t c16 = K / 16 + t; c16 < ldq / 16; c16 += 256)
       *(u32x4 *)(qrow + c16 * 16) = (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
+// W_O^T [N x ldo] (fp16): row n holds W[idx[p], n] for p < |O|, zeros up to the
+// next multiple of 64. Block b covers 64 columns of W, 64 outlier rows per
+// step, transposed through LDS.
+__device__ void gather_wot_block(int64_t b, const WeightSideArgs &a) {
+  __shared__ __attribute__((aligned(16))) uint16_t st[64 * 72];  // [n][p], pitch 72
+  const int count = *a.count;
+  const int t = threadIdx.x;
+  const int64_t n0 = b * 64;
+  const int64_t pad = (count + 63) / 64 * 64;
+  for (int64_t p0 = 0; p0 < pad; p0 += 64) {
+    u32x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int p = q >> 3, ch = q & 7;  // 64 rows x 8 chunks of 8 fp16
+      const int64_t n = n0 + ch * 8;
+      const bool ok = p0 + p < count && n < a.N;
+      const int64_t src = ok ? (int64_t)a.idx[p0 + p] * a.ldw + n : 0;
+      const u32x4 x = *(const u32x4 *)(a.W + src);
+      v[u] = ok ? x : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int p = q >> 3, ch = q & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = v[u][e >> 1];
+        st[(ch * 8 + e) * 72 + p] = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = t + 256 * u;
+      const int nl = q >> 3, ch = q & 7;  // 64 output rows x 8 chunks
+      const int64_t n = n0 + nl;
+      if (n < a.N)
+        *(u32x4 *)(a.wot + n * a.ldo + p0 + ch * 8) = *(const u32x4 *)(st + nl * 72 + ch * 8);
+    }
+    __syncthreads();
+  }
+}
+
+// The int8 outlier-weight form of W_O^T [N x ldo]: row n holds the codes
+// Wq[n, idx[p]] as fp16 (exact) for p < |O|, zeros up to the next multiple of
+// 64. Block b covers 64 rows of Wq; a row's codes are gathered by 4 threads.
+__device__ void gather_codes_block(int64_t b, const WeightSideArgs &a) {
+  const int count = *a.count;
+  const int t = threadIdx.x;
+  const int64_t n = b * 64 + (t >> 2);
+  if (n >= a.N) return;
+  const int pad = (count + 63) / 64 * 64;
+  const int8_t *row = a.Wq + n * a.K;
+  for (int p = t & 3; p < pad; p += 4) {
+    const int q = p < count ? row[a.idx[p]] : 0;
+    a.wot[n * a.ldo + p] = f2h((float)q);
+  }
+}
+
+// Compacted copy Wqc of the Wq rows without the outlier columns, when the
+// outlier share calls for it. Block b of nb takes rows b, b + nb, ...: each
+// thread compresses 32 bytes (one mask word) into LDS, then the row goes out
+// with 16-byte stores, its tail zeroed up to the 128-byte pitch.
+__device__ void compact_block(int64_t b, int64_t nb, const WeightSideArgs &a, uint8_t *srow) {
+  const int count = *a.count;
+  if (!use_compaction(count, a.K, a.M)) return;
+  const int t = threadIdx.x;
+  const int64_t K = a.K;
+  const int64_t kw = (K + 31) / 32;
+  const int64_t kk = K - count;
+  const int64_t kpad = (kk + 127) / 128 * 128;
+  for (int64_t n = b; n < a.N; n += nb) {
+    const int8_t *row = a.Wq + n * K;
+    for (int64_t w = t; w < kw; w += 256) {
+      const uint32_t v = a.omask[w];
+      int64_t dst = 32 * w - a.wprefix[w];
+      const int nbytes = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
+      for (int h = 0; h < nbytes; h += 16) {
+        const u32x4 d = *(const u32x4 *)(row + 32 * w + h);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (!((v >> (h + e)) & 1u)) {
+            srow[dst] = (uint8_t)((d[e >> 2] >> (8 * (e & 3))) & 0xffu);
+            ++dst;
+          }
+        }
+      }
+    }
+    for (int64_t k = kk + t; k < kpad; k += 256) srow[k] = 0;
+    __syncthreads();
+    int8_t *out = a.wqc + n * a.ldq;
+    for (int64_t c16 = t; c16 < kpad / 16; c16 += 256)
+      *(u32x4 *)(out + c16 * 16) = *(const u32x4 *)(srow + c16 * 16);
+    __syncthreads();
+  }
+}
+
+// The preparation of a large-M call after detection, in one launch: blocks
+// [0, M) quantize the rows of X, the next gather_blocks gather W_O^T, the rest
+// compact Wq (their counts are fixed by the host; the work they find depends on
+// the outlier count on the device).
+template <class Codec>
+__global__ __launch_bounds__(256) void k_layer_prep(RowQuantArgs r, WeightSideArgs w) {
+  extern __shared__ u32x4 srow_v[];
+  uint8_t *srow = (uint8_t *)srow_v;
+  const int64_t b = blockIdx.x;
+  if (b < r.M) {
+    rowquant_row<Codec>(b, r, srow);
+  } else if (b < r.M + w.gather_blocks) {
+    if (w.W)
+      gather_wot_block(b - r.M, w);
+    else
+      gather_codes_block(b - r.M, w);
+  } else {
+    const int64_t c0 = r.M + w.gather_blocks;
+    compact_block(b - c0, gridDim.x - c0, w, srow);
   }
 }
 
@@ -283,23 +402,21 @@ template hipError_t launch_rowquant_idx<CodecE4M3>(const uint16_t *, int64_t, in
                                                    float *, hipStream_t);
 
 template <class Codec>
-hipError_t launch_rowquant_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                                 const uint32_t *omask, const int32_t *wprefix,
-                                 const int32_t *count, uint8_t *Xq, int64_t ldq, float *m,
-                                 uint16_t *xo, int64_t ldo, hipStream_t stream) {
-  const size_t lds = (K <= kCompactMaxK) ? (size_t)ldq : 0;
-  hipLaunchKernelGGL(k_rowquant_layer<Codec>, dim3((unsigned)M), dim3(256), lds, stream, X, M, K,
-                     ldx, omask, wprefix, count, Xq, ldq, m, xo, ldo);
+hipError_t launch_layer_prep(const RowQuantArgs &r, const WeightSideArgs &args, bool gather,
+                             hipStream_t stream) {
+  WeightSideArgs w = args;
+  w.gather_blocks = gather ? (w.N + 63) / 64 : 0;
+  // compaction never applies when even |O| = K would not pay (M below ~313)
+  const int64_t cblocks = use_compaction((int)w.K, w.K, w.M) ? (w.N < 1024 ? w.N : 1024) : 0;
+  const size_t lds = (r.K <= kCompactMaxK) ? (size_t)r.ldq : 0;
+  const int64_t blocks = r.M + w.gather_blocks + cblocks;
+  hipLaunchKernelGGL(k_layer_prep<Codec>, dim3((unsigned)blocks), dim3(256), lds, stream, r, w);
   return hipGetLastError();
 }
-template hipError_t launch_rowquant_layer<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,
-                                                   const uint32_t *, const int32_t *,
-                                                   const int32_t *, uint8_t *, int64_t, float *,
-                                                   uint16_t *, int64_t, hipStream_t);
-template hipError_t launch_rowquant_layer<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
-                                                     const uint32_t *, const int32_t *,
-                                                     const int32_t *, uint8_t *, int64_t, float *,
-                                                     uint16_t *, int64_t, hipStream_t);
+template hipError_t launch_layer_prep<CodecI8>(const RowQuantArgs &, const WeightSideArgs &, bool,
+                                               hipStream_t);
+template hipError_t launch_layer_prep<CodecE4M3>(const RowQuantArgs &, const WeightSideArgs &,
+                                                 bool, hipStream_t);
 
 hipError_t launch_colwise_absmax(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, float *s,
                                  hipStream_t stream) {

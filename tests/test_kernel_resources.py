@@ -16,7 +16,7 @@ def test_every_kernel_reported():
     res = json.load(open(RES))
     names = " ".join(res)
     for k in ("k_gemm_prefill", "k_decode_gemm", "k_decode_fused", "k_detect_partial",
-              "k_rowquant_layer", "k_colquant", "k_quant_tensor"):
+              "k_layer_prep", "k_colquant", "k_quant_tensor"):
         assert k in names, k
 
 
