@@ -25,7 +25,7 @@ int64_t pitch_o(int64_t K) { return (K + 63) / 64 * 64; }
 
 // Offsets (bytes) of the regions a call carves out of its workspace.
 struct Layout {
-  size_t pmask, omask, wprefix, nidx, idx, count, xq, m, xo, wqc, wot, part, total;
+  size_t pmask, omask, wprefix, idx, count, xq, m, xo, wqc, wot, part, total;
 };
 
 // Small-M layer calls: preparation outputs, split-K partial sums, counters.
@@ -56,8 +56,6 @@ Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefi
   o += up((size_t)p.kw * 4);
   L.wprefix = o;
   o += up((size_t)p.kw * 4);
-  L.nidx = o;
-  o += up((size_t)K * 4);
   if (layer) {
     L.idx = o;
     o += up((size_t)K * 4);
@@ -139,7 +137,7 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
   const bool int8w = ep.int8w != 0;
 
   DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
-              wprefix, idx, (int32_t *)(ws + L.nidx), count, outlier_count_out};
+              wprefix, idx, count, outlier_count_out};
   const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
   uint16_t *wot = (uint16_t *)(ws + L.wot);
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
@@ -202,8 +200,7 @@ LLMINT8_EXPORT int llmint8_find_outliers(const uint16_t *X, int64_t M, int64_t K
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
   uint8_t *ws = (uint8_t *)workspace;
   DetectOut d{nullptr, threshold, nullptr, 0, (uint32_t *)(ws + L.pmask),
-              (uint32_t *)(ws + L.omask), (int32_t *)(ws + L.wprefix), idx,
-              (int32_t *)(ws + L.nidx), count, nullptr};
+              (uint32_t *)(ws + L.omask), (int32_t *)(ws + L.wprefix), idx, count, nullptr};
   return hip_status(launch_detect(X, M, K, ldx, threshold, detect_plan(M, K), d,
                                   (hipStream_t)stream));
 }

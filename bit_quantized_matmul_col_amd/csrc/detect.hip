@@ -11,7 +11,7 @@
 // test as "some entry >= t") and stored as 16 mask words per row chunk.
 // Pass 2 (k_detect_finish): one block ORs the row-chunk masks into LDS (all
 // partial-mask loads in flight at once), scans the per-word popcounts and writes
-// the ascending outlier and kept lists, the per-word prefix and the count. When
+// the ascending outlier list, the per-word prefix and the count. When
 // the caller supplies the column absmax of X, pass 1 is skipped and pass 2
 // compares it with the threshold instead.
 #include "internal.hpp"
@@ -147,15 +147,11 @@ __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restri
   int pos = before + incl - local;
 
   for (int64_t w = w0; w < w1; ++w) {
-    const uint32_t v = smask[w];
+    uint32_t v = smask[w];
     out.wprefix[w] = pos;
-    const int nb = (K - 32 * w < 32) ? (int)(K - 32 * w) : 32;
-    for (int b = 0; b < nb; ++b) {
-      const int32_t k = (int32_t)(32 * w + b);
-      if (v & (1u << b))
-        out.idx[pos++] = k;
-      else
-        out.nidx[k - pos] = k;
+    while (v) {  // the set bits of the word, ascending
+      out.idx[pos++] = (int32_t)(32 * w + __builtin_ctz(v));
+      v &= v - 1u;
     }
   }
   if (t == 0) {

@@ -42,7 +42,6 @@ struct DetectOut {
   uint32_t *omask;   // [kw] outlier bitmask, bit k%32 of word k/32
   int32_t *wprefix;  // [kw] outliers in words before w
   int32_t *idx;      // [K] ascending outlier columns
-  int32_t *nidx;     // [K] ascending kept columns
   int32_t *count;    // [1]
   int32_t *count_copy;  // optional second copy of the count
 };
