@@ -36,11 +36,12 @@ bool narrow_tiles(int64_t M, int64_t N, int cus) {
 
 // Columns [0, n1) of the output in whole waves of 256x256 tiles, or 0 when
 // splitting does not pay. The last wave of a 256x256 launch runs
-// tiles % cus blocks while the rest of the chip idles; putting the columns of
-// those tiles into a second launch of 128x256 tiles (half the work each, still
-// two waves per SIMD, in one wave) turns that wave into about half a wave plus
-// the launch gap. (256x128 tiles with one wave per SIMD measured 0.63 of a
-// full wave for the same half of the work.)
+// tiles % cus blocks while the rest of the chip idles; giving the columns of
+// those tiles to 128x256 tiles instead (half the work each, still two waves
+// per SIMD, at most one wave of them) turns that wave into about half a wave.
+// Both shapes run in one launch, the smaller tiles starting as CUs free up.
+// (256x128 tiles with one wave per SIMD took 0.63 of a full wave for the same
+// half of the work.)
 int64_t wide_columns(int64_t M, int64_t N, int cus) {
   const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
   const int64_t tiles = tm * tn, full_waves = tiles / cus;
@@ -87,11 +88,7 @@ hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t s
   if (narrow_tiles(a.M, a.N, cus)) return launch_gemm_narrow(a, ev, stream);
   const int64_t n1 = wide_columns(a.M, a.N, cus);
   if (n1 == 0) return launch_gemm_wide(a, ev, stream);
-  // the begin event goes with the first launch, the end event with the second
-  const hipError_t e =
-      launch_gemm_wide(column_slice(a, 0, n1), GemmEvents{ev.begin, nullptr}, stream);
-  if (e != hipSuccess) return e;
-  return launch_gemm_tail(column_slice(a, n1, a.N - n1), GemmEvents{nullptr, ev.end}, stream);
+  return launch_gemm_pair(column_slice(a, 0, n1), column_slice(a, n1, a.N - n1), ev, stream);
 }
 
 }  // namespace llmint8

@@ -145,9 +145,9 @@ struct TileCfg {
 };
 
 // Tile coordinates of this block after the XCD-aware renumbering.
-__device__ inline void tile_of_block(int64_t tiles_m, int64_t tiles_n, int64_t &tm, int64_t &tn) {
+__device__ inline void tile_of_block(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t &tm,
+                                     int64_t &tn) {
   const int64_t nb = tiles_m * tiles_n;
-  const int64_t bid = blockIdx.x;
   const int64_t x = bid % kXcds, q = nb / kXcds, rem = nb % kXcds;
   const int64_t v = x * q + (x < rem ? x : rem) + bid / kXcds;
   const int64_t group = kGroupM * tiles_n;
@@ -330,15 +330,14 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
   __syncthreads();  // every wave is done with the ring before it is reused
 }
 
-// F8: the operands are E4M3 codes (fp32 sums, dequantized by 1 / 448^2)
-// instead of int8 codes (int32 sums, 1 / 127^2).
+// One output tile: block bid of the launch's tiles for a. F8: the operands are
+// E4M3 codes (fp32 sums, dequantized by 1 / 448^2) instead of int8 codes
+// (int32 sums, 1 / 127^2).
 template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>
-__global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
+__device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uint8_t *smem) {
   using T = TileCfg<BM, BN, NWN, SK>;
   constexpr int NW = T::NW, TH = T::THREADS;
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
-  extern __shared__ u32x4 smem_v[];
-  uint8_t *smem = (uint8_t *)smem_v;
   float *sm = (float *)(smem + T::NST * T::STAGE);
   float *ss = sm + BM;  // column factor of the int8 dequantization
   float *sf = ss + BN;  // column factor applied at the end (int8 outlier weights)
@@ -347,7 +346,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
   const int wm = wv / NWN, wn = wv % NWN;
   const int li = lane & 31, lg = lane >> 5;
   int64_t tm, tn;
-  tile_of_block((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
+  tile_of_block(bid, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int count = *a.count;
@@ -461,6 +460,43 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
       if (lg == 0 && colok) ycmax_update(a.ep.ycmax, n0 + cl, cmax);
     }
   }
+}
+
+template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>
+__global__ __launch_bounds__(128 * NWN, 1) void k_gemm_prefill(GemmArgs a) {
+  extern __shared__ u32x4 smem_v[];
+  prefill_tile<BM, BN, NWN, SK, DBG, F8>(a, blockIdx.x, (uint8_t *)smem_v);
+}
+
+// Two tile shapes with the same wave count in one launch: blocks [0, blocks1)
+// take the tiles of a1 (whole waves of large tiles), the rest those of a2 (the
+// remaining columns in smaller tiles), which start as soon as CUs free up.
+template <int BM1, int BN1, int BM2, int BN2, int NWN, int SK, bool DBG, bool F8>
+__global__ __launch_bounds__(128 * NWN, 1) void k_gemm_pair(GemmArgs a1, GemmArgs a2,
+                                                           int64_t blocks1) {
+  extern __shared__ u32x4 smem_v[];
+  const int64_t b = blockIdx.x;
+  if (b < blocks1)
+    prefill_tile<BM1, BN1, NWN, SK, DBG, F8>(a1, b, (uint8_t *)smem_v);
+  else
+    prefill_tile<BM2, BN2, NWN, SK, DBG, F8>(a2, b - blocks1, (uint8_t *)smem_v);
+}
+
+template <int BM1, int BN1, int BM2, int BN2, int NWN, int SK, bool DBG, bool F8>
+hipError_t launch_pair(const GemmArgs &a1, const GemmArgs &a2, const GemmEvents &ev,
+                       hipStream_t stream) {
+  using T1 = TileCfg<BM1, BN1, NWN, SK>;
+  using T2 = TileCfg<BM2, BN2, NWN, SK>;
+  constexpr int LDS = T1::LDS > T2::LDS ? T1::LDS : T2::LDS;
+  auto *kern = k_gemm_pair<BM1, BN1, BM2, BN2, NWN, SK, DBG, F8>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  if (e != hipSuccess) return e;
+  const int64_t blocks1 = ((a1.M + BM1 - 1) / BM1) * ((a1.N + BN1 - 1) / BN1);
+  const int64_t blocks2 = ((a2.M + BM2 - 1) / BM2) * ((a2.N + BN2 - 1) / BN2);
+  hipExtLaunchKernelGGL(kern, dim3((unsigned)(blocks1 + blocks2)), dim3(T1::THREADS), LDS, stream,
+                        (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a1, a2, blocks1);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>

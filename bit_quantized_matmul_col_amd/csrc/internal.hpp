@@ -139,12 +139,13 @@ struct GemmEvents {
 };
 
 // Large-M tiled GEMM with the fused dequantize + outlier epilogue; picks the
-// tile shapes (256x256, 256x128, or whole waves of 256x256 tiles followed by
-// the remaining columns in 128x256 tiles) from the problem size.
+// tile shapes (256x256, 256x128, or whole waves of 256x256 tiles and the
+// remaining columns in 128x256 tiles, in one launch) from the problem size.
 hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
-hipError_t launch_gemm_tail(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
+hipError_t launch_gemm_pair(const GemmArgs &a1, const GemmArgs &a2, const GemmEvents &ev,
+                            hipStream_t stream);
 
 // Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
 // its slice of X itself.

@@ -135,9 +135,7 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
  *       the caller) that the GEMM kernel's own dispatch on `stream` stamps when
  *       the kernel starts and when it completes (no separate stream commands),
  *       so a caller can time the dominant kernel of the layer with
- *       hipEventElapsedTime. When the GEMM runs as two launches (whole waves
- *       of 256x256 tiles, then the remaining columns in 128x256 tiles), the
- *       first launch stamps the begin event and the second the end event.
+ *       hipEventElapsedTime.
  *   outlier_weights  LLMINT8_OUTLIER_W_FP16 (default) or LLMINT8_OUTLIER_W_INT8:
  *       keep only the int8 weight (walkthrough page, sections 2.4 and 6: the
  *       int8 weights replace the fp16 ones); W may then be NULL at any

@@ -599,17 +599,17 @@ def test_fp8_workload_sampled(dev):
     torch.cuda.empty_cache()
 
 
-# --- the large-M GEMM in two launches ------------------------------------------------------
+# --- the large-M GEMM with two tile shapes -------------------------------------------------
 # 2304 x 7432 outputs make 9 x 30 = 270 tiles of 256 x 256 on 256 CUs: the
-# first 28 tile columns (252 tiles) run as one launch and the remaining 264
-# columns (ragged) as 128 x 256 tiles in a second launch. Every output, the
+# first 28 tile columns (252 tiles) run as 256 x 256 tiles and the remaining 264
+# columns (ragged) as 128 x 256 tiles in the same launch. Every output, the
 # int32 accumulators, the bias and the Y column maxima cross that boundary.
 
 @pytest.mark.parametrize("variant", ["int8", "fp8"])
 def test_gemm_split_into_wide_and_narrow_launches(dev, variant):
     torch, lm = dev
     M, K, N = 2304, 64, 7432
-    say(f"case GEMM split into two launches {variant} M={M} K={K} N={N}")
+    say(f"case GEMM with two tile shapes {variant} M={M} K={K} N={N}")
     X, W, _ = workloads.random_case(M, K, N, seed=17, n_out=2)
     b = (np.random.default_rng(4).standard_normal(N) * 0.5).astype(np.float16)
     Xd, Wd, bd = to_gpu(torch, X), to_gpu(torch, W), to_gpu(torch, b)
