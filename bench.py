@@ -148,6 +148,31 @@ def accuracy(torch, lm, X_host, W_host, Xd, Wd, threshold, n_rows=16):
     return out
 
 
+def vendor_int8_gemm(torch, M, K, N, dev, reps=20):
+    """Reference point, not part of the layer: the plain int8 GEMM of the same
+    shape (Xq . Wq^T over all of K, int32 out, no outlier product, no
+    dequantization) through torch._int_mm, which ROCm runs on hipBLASLt."""
+    a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+    b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev)
+    try:
+        for _ in range(3):
+            torch._int_mm(a, b.t())
+    except Exception as e:  # not every shape is supported by the library
+        return {"library": "torch._int_mm (hipBLASLt)", "error": repr(e)[:120]}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch._int_mm(a, b.t())
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tops = 2 * M * N * K / (ms * 1e-3) / 1e12
+    return {"library": "torch._int_mm (hipBLASLt)", "work": "2MNK int8 ops, int32 out",
+            "ms": round(ms, 6), "TOPS": round(tops, 2),
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+
+
 def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8=False):
     """The oracle as it stands, single-threaded, on a bounded sample. Its weight
     quantization (load time, like the GPU's) is done first and not timed."""
@@ -390,6 +415,8 @@ def main():
         "quantize_colwise": {"ms": round(colwise_ms, 5), "algorithmic_bytes": colwise_bytes,
                              "GB_per_s": round(colwise_bytes / (colwise_ms * 1e-3) / 1e9, 2)},
     }
+    if not hbm_bound:
+        out["vendor_int8_gemm"] = vendor_int8_gemm(torch, wl.M, wl.K, wl.N, dev)
     if not args.no_accuracy:
         del graph
         out["accuracy"] = accuracy(torch, lm, X_host[0], W_host, Xs[0], W0, threshold)
