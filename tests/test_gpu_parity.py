@@ -574,19 +574,26 @@ def test_fp8_layer(dev, M, K, N, threshold):
     check_fp8_layer(torch, lm, X, W, threshold)
 
 
-def test_fp8_layer_bias_and_column_absmax(dev):
+@pytest.mark.parametrize("M,K,N", [(5, 4096, 520), (48, 2048, 1032), (300, 1024, 264)])
+def test_fp8_layer_options(dev, M, K, N):
+    # bias and the Y column absmax (checked against the oracle and the stored Y),
+    # then a supplied X column absmax (same outlier count, bit-identical Y), on
+    # the small-M and the large-M path
     torch, lm = dev
-    say("case fp8 layer with bias and Y column absmax")
-    X, W, _ = workloads.random_case(300, 1024, 264, seed=5, n_out=3)
-    b = (np.random.default_rng(2).standard_normal(264) * 0.5).astype(np.float16)
-    check_fp8_layer(torch, lm, X, W, 6.0, bias=b)
+    say(f"case fp8 layer options M={M} K={K} N={N}")
+    X, W, _ = workloads.random_case(M, K, N, seed=M + 5, n_out=3)
+    b = (np.random.default_rng(2).standard_normal(N) * 0.5).astype(np.float16)
+    check_fp8_layer(torch, lm, X, W, 6.0, bias=b, ycmax=True)
     Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
     Wq, s = lm.llmint8_quantize_colwise_fp8(Wd)
-    ycm = torch.full((264,), 1e30, dtype=torch.float32, device="cuda")
-    Y = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, 6.0, y_col_absmax=ycm)
+    xcm = to_gpu(torch, np.abs(X.astype(np.float32)).max(axis=0))
+    c0 = torch.empty(1, dtype=torch.int32, device="cuda")
+    c1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    Y0 = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, 6.0, outlier_count=c0)
+    Y1 = lm.llmint8_linear_fp8(Xd, Wq, s, Wd, 6.0, outlier_count=c1, x_col_absmax=xcm)
     torch.cuda.synchronize()
-    assert np.array_equal(ycm.cpu().numpy(),
-                          np.abs(Y.cpu().numpy().astype(np.float32)).max(axis=0))
+    assert int(c0.item()) == int(c1.item()) == oracle.find_outliers(X, 6.0).size
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
 
 
 def test_fp8_workload_sampled(dev):
