@@ -1,0 +1,51 @@
+"""The benchmark's host-side bookkeeping (no GPU): the algorithmic byte and op
+counts it reports, its copy of the library's compaction rule, and its refusal
+of a multi-GPU run."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_decode_call_bytes():
+    # 2MK (X) + KN (Wq) + 4N (scales) + 2|O|N (fp16 outlier rows) + 2MN (Y)
+    call, gemm, ops, flops = bench.step_work(32, 4096, 4096, 4, False)
+    assert call == 2 * 32 * 4096 + 4096 * 4096 + 4 * 4096 + 2 * 4 * 4096 + 2 * 32 * 4096
+    assert call == 17350656
+    # the small-M GEMM kernel reads Wq and X and writes the int32 split sums
+    assert gemm == 4096 * 4096 + 2 * 32 * 4096 + 4 * 32 * 4096
+    assert ops == 2 * 32 * 4096 * (4096 - 4) and flops == 2 * 32 * 4096 * 4
+    # int8-only weights: the outlier rows come out of Wq, already counted
+    assert bench.step_work(32, 4096, 4096, 4, False, int8w=True)[0] == call - 2 * 4 * 4096
+
+
+def test_large_m_work():
+    M, K, N, n = 2048, 4096, 11008, 20
+    call, gemm, ops, flops = bench.step_work(M, K, N, n, False)
+    assert ops == 2 * M * N * (K - n) and flops == 2 * M * N * n
+    assert gemm == N * K + 4 * N + M * K + 4 * M + 2 * M * n + 2 * n * N + 2 * M * N
+    # compaction: the 8-bit operands shrink to the K - |O| kept columns
+    gemm_c = bench.step_work(M, K, N, n, True)[1]
+    assert gemm - gemm_c == (N + M) * n
+
+
+def test_compaction_rule_matches_the_library():
+    # M * |O| * 16 > 5000 * (2K - |O|), K <= 32768, and never on the small-M path
+    assert bench.uses_compaction(400, 1024, 1000)
+    # no M of the small-M path reaches the rule: M <= 64 < 5000 / 16
+    assert not bench.uses_compaction(64, 1024, 1024, any_m=True)
+    assert bench.uses_compaction(4096, 5120, 1218)  # the 13b workload
+    assert not bench.uses_compaction(2048, 4096, 20)  # prefill
+    assert not bench.uses_compaction(100000, 40000, 20000)  # K above the LDS staging cap
+    for M, K, n in [(313, 1000, 1000), (312, 1000, 1000), (700, 1008, 300)]:
+        assert bench.uses_compaction(M, K, n) == (M * n * 16 > 5000 * (2 * K - n))
+
+
+def test_multi_gpu_run_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr
