@@ -145,8 +145,8 @@ struct DecodeStage {
 };
 
 template <int MB>
-__device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
-                                   int64_t k_end, const int8_t *brow, int wv, int lane, int g) {
+__device__ inline void decode_load_x(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
+                                     int64_t k_end, int wv, int lane) {
   const int64_t kx = k0 + 8 * lane;
   st.kok = kx < k_end;
   const int64_t kxc = st.kok ? kx : 0;
@@ -156,11 +156,23 @@ __device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st,
     const int row = wv + 4 * u;
     st.x[u] = *(const u32x4 *)(a.X + (int64_t)(row < a.M ? row : 0) * a.ldx + kxc);
   }
+}
+
+template <int MB>
+__device__ inline void decode_load_b(DecodeStage<MB> &st, int64_t k0, int64_t k_end,
+                                     const int8_t *brow, int g) {
 #pragma unroll
   for (int j = 0; j < kSubK / 64; ++j) {
     const int64_t k = k0 + 64 * j + 16 * g;
     st.b[j] = *(const u32x4 *)(brow + (k < k_end ? k : 0));
   }
+}
+
+template <int MB>
+__device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
+                                   int64_t k_end, const int8_t *brow, int wv, int lane, int g) {
+  decode_load_x<MB>(a, st, k0, k_end, wv, lane);
+  decode_load_b<MB>(st, k0, k_end, brow, g);
 }
 
 // Four E4M3 codes of the fp16 pairs (w0, w1) for the scale inv = fl32(448 /
@@ -173,15 +185,10 @@ __device__ inline uint32_t codes4_e4m3(uint32_t w0, uint32_t w1, float inv) {
   return CodecE4M3::code4(t);
 }
 
-// Quantize the stage's X chunks into LDS, then contract them with the Wq bytes.
-// F8: E4M3 codes and v_mfma_f32_16x16x128_f8f6f4, which takes the Wq bytes of
-// two consecutive int8 steps (j = 2 jj, 2 jj + 1) per lane and the X codes of
-// the same k, so both operands see the same k in every slot; the fp32 sums
-// are kept as raw bits in the int32 accumulators.
+// Quantize the stage's X chunks into the LDS buffer sx.
 template <int MB, bool F8>
-__device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const float *sinv,
-                                   i32x4 *acc, int wv, int lane, int c16, int g) {
-  __syncthreads();  // sinv ready; the previous stage's MFMAs are done with sx
+__device__ inline void decode_quant(const DecodeStage<MB> &st, uint8_t *sx, const float *sinv,
+                                    int wv, int lane) {
   const uint32_t ob = st.kok ? (st.mw >> (8 * (lane & 3))) & 0xffu : 0xffu;
   const uint32_t keep_lo = keep_bytes(ob & 0xfu), keep_hi = keep_bytes(ob >> 4);
 #pragma unroll
@@ -198,7 +205,16 @@ __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const
     }
     *(u32x2 *)(sx + row * kXPitch + 8 * lane) = out;
   }
-  __syncthreads();
+}
+
+// Contract the stage's X codes in sx with its Wq bytes.
+// F8: E4M3 codes and v_mfma_f32_16x16x128_f8f6f4, which takes the Wq bytes of
+// two consecutive int8 steps (j = 2 jj, 2 jj + 1) per lane and the X codes of
+// the same k, so both operands see the same k in every slot; the fp32 sums
+// are kept as raw bits in the int32 accumulators.
+template <int MB, bool F8>
+__device__ inline void decode_mma(const DecodeStage<MB> &st, const uint8_t *sx, i32x4 *acc,
+                                  int c16, int g) {
   if constexpr (F8) {
 #pragma unroll
     for (int jj = 0; jj < kSubK / 128; ++jj) {
@@ -228,17 +244,30 @@ __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const
   }
 }
 
+// One stage through a single LDS buffer: quantize, then contract.
+template <int MB, bool F8>
+__device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const float *sinv,
+                                   i32x4 *acc, int wv, int lane, int c16, int g) {
+  __syncthreads();  // sinv ready; the previous stage's MFMAs are done with sx
+  decode_quant<MB, F8>(st, sx, sinv, wv, lane);
+  __syncthreads();
+  decode_mma<MB, F8>(st, sx, acc, c16, g);
+}
+
 // Block (tile, kb). Wave w owns 16 output columns; lane (c16 = l % 16,
 // g = l / 16) supplies, for MFMA step j, the 16 Wq bytes at k = 64 j + 16 g of
 // its column and reads the matching Xq bytes from LDS. MB 16-row blocks cover M.
 // NST is the number of 512-byte stages of the block's K range when it is 1 or
 // 2 (straight-line code, all loads issued before the first wait), 0 for any
-// count. Two register stages alternate so that the next stage's loads are in
-// flight while the current one is quantized and contracted; no load is issued
-// under a branch that the following waits would have to merge.
+// count. With two stages, both are quantized into LDS buffers of their own
+// before either is contracted, so only the MFMAs wait for the Wq stream. For
+// any count, two register stages alternate so that the next stage's loads are
+// in flight while the current one is quantized and contracted. No load is
+// issued under a branch that the following waits would have to merge.
 template <int MB, int NST, bool F8>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t sx[MB * 16 * kXPitch];
+  constexpr int kStageBytes = MB * 16 * kXPitch;
+  __shared__ __attribute__((aligned(16))) uint8_t sx[(NST == 2 ? 2 : 1) * kStageBytes];
   __shared__ float spart[4][64];
   __shared__ float sinv[64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -262,8 +291,16 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   }
 
   DecodeStage<MB> s0, s1;
-  decode_load<MB>(a, s0, k_begin, k_end, brow, wv, lane, g);
-  if constexpr (NST == 2) decode_load<MB>(a, s1, k_begin + kSubK, k_end, brow, wv, lane, g);
+  if constexpr (NST == 2) {
+    // both X stages ahead of the Wq bytes: loads complete in issue order, so
+    // the X codes of both stages can be formed while Wq is still streaming
+    decode_load_x<MB>(a, s0, k_begin, k_end, wv, lane);
+    decode_load_x<MB>(a, s1, k_begin + kSubK, k_end, wv, lane);
+    decode_load_b<MB>(s0, k_begin, k_end, brow, g);
+    decode_load_b<MB>(s1, k_begin + kSubK, k_end, brow, g);
+  } else {
+    decode_load<MB>(a, s0, k_begin, k_end, brow, wv, lane, g);
+  }
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first wait
 
   float pm = 0.f;
@@ -287,8 +324,12 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   if constexpr (NST == 1) {
     decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
   } else if constexpr (NST == 2) {
-    decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
-    decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
+    __syncthreads();  // sinv ready
+    decode_quant<MB, F8>(s0, sx, sinv, wv, lane);
+    decode_quant<MB, F8>(s1, sx + kStageBytes, sinv, wv, lane);
+    __syncthreads();
+    decode_mma<MB, F8>(s0, sx, acc, c16, g);
+    decode_mma<MB, F8>(s1, sx + kStageBytes, acc, c16, g);
   } else {
     const int nst = (int)((k_end - k_begin + kSubK - 1) / kSubK);
     int64_t k0 = k_begin;
@@ -348,13 +389,15 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     mrow[i] = a.m[rowc];
   }
   const float scol = a.s[colc];
-  const float bcol = a.ep.bias ? h2f(a.ep.bias[colc]) : 0.f;
+  // loads without a condition (a bias-less call reads its bias bits from s):
+  // a load under a branch is waited for at once, and with it every earlier one
+  const uint16_t braw = (a.ep.bias ? a.ep.bias : (const uint16_t *)a.s)[colc];
   // the outlier product runs with fp16 weight rows or with the int8 codes
   const bool i8w = a.ep.int8w != 0;
   const bool outl = a.w || i8w;
   const __amdgpu_buffer_rsrc_t mrs =
       __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
-  uint32_t mw = outl ? __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0) : 0u;
+  uint32_t mw = __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0);
 
   float y[4], yo[4] = {0.f, 0.f, 0.f, 0.f};
   const float sd = scol * (F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f);
@@ -461,6 +504,7 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   }
 
   const float oscale = i8w ? scol * (1.0f / 127.0f) : 1.0f;
+  const float bcol = a.ep.bias ? h2f(braw) : 0.f;
   float cmax = 0.f;  // |Y| of this column over the block's rows
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

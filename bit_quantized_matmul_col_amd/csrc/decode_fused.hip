@@ -9,7 +9,9 @@
 //
 // Block b (512 threads, persistent over the 16-column tiles b, b + G, ...):
 //  1. loads all of X into registers, then issues the Wq loads of its first tile
-//     (they stream while 2-5 run);
+//     (they stream while 2-5 run). Loads complete in issue order, so no value
+//     loaded after the Wq bytes is used before the tile's MFMAs: a use any
+//     earlier would wait for the whole Wq stream, and 2-5 with it;
 //  2. X in registers: thread (c, h) holds the 16-byte chunk c
 //     (columns 8c .. 8c+7) of rows h, h + R, ... (R = 512 / (K / 8));
 //  3. column absmax over all rows with packed 16-bit max on the magnitude bits
@@ -75,7 +77,7 @@ __device__ inline uint32_t pmax16(uint32_t a, uint32_t b) {
 // Layout of the dynamic LDS (byte offsets); P = K + 16 is the Xq row pitch
 // (16 rows that one MFMA operand reads fall in distinct bank groups).
 struct FusedLds {
-  int xq, red, list, inv, m, bits, rmax, xo0, ycm, misc, total;
+  int xq, red, list, inv, m, bits, pos, rmax, xo0, ycm, misc, total;
 };
 
 __host__ __device__ constexpr FusedLds fused_lds(int K, int MB) {
@@ -96,6 +98,9 @@ __host__ __device__ constexpr FusedLds fused_lds(int K, int MB) {
   o += 64 * 4;
   L.bits = o;  // outlier bits of each 8-column chunk
   o += K / 8;
+  o = (o + 15) & ~15;
+  L.pos = o;  // list position of each chunk's first outlier column, uint16
+  o += K / 8 * 2;
   o = (o + 15) & ~15;
   L.rmax = o;  // per-wave row maxima [8][32]
   o += kWaves * 32 * 4;
@@ -138,7 +143,7 @@ __device__ inline uint32_t wave_rows_max(uint32_t *v, int lane) {
   return r;
 }
 
-template <int K, int MB>
+template <int K, int MB, bool I8W>
 __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   constexpr int C = K / 8;               // 16-byte chunks per X row
   constexpr int R = kThreads / C;        // threads sharing a chunk
@@ -159,48 +164,69 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   uint8_t *sbits = lds + L.bits;
   uint32_t *srmax = (uint32_t *)(lds + L.rmax);
   int *stotal = (int *)(lds + L.misc);
+  uint16_t *spos = (uint16_t *)(lds + L.pos);
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int G = gridDim.x;
 
   // Per-tile registers: the wave's Wq bytes (wave wv owns k bytes [wv * KW,
-  // (wv + 1) * KW)), the column scale of the thread's output and, for threads
-  // t < 128, 16 bytes of the W rows of the first batch of outlier columns.
+  // (wv + 1) * KW)), the column scale and bias bits of the thread's output and
+  // the weights of the first batch of outlier columns: 8 fp16 entries of their
+  // W rows, or (I8W) two int8 codes. All are loaded without a condition and
+  // used only in the tile's epilogue.
   static_assert(MB == 1, "one output per thread");
   struct TileRegs {
     u32x4 b[KS];
-    float sc, bias;
+    float sc;
+    uint32_t braw;
     u32x4 wo;
+    int q0, q1;
   };
-  auto load_b = [&](TileRegs &tr, int tile) {
+  // a bias-less call reads its bias bits from s (ignored afterwards)
+  const uint16_t *bias_src = a.ep.bias ? a.ep.bias : (const uint16_t *)a.s;
+  auto load_cols = [&](TileRegs &tr, int tile) {
+    const int no = tile * kTileCols + (t & 15);
+    tr.sc = a.s[no < a.N ? no : a.N - 1];
+    tr.braw = bias_src[no < a.N ? no : a.N - 1];
+  };
+  auto load_wq = [&](TileRegs &tr, int tile) {
     const int n = tile * kTileCols + c16;
     const int8_t *row = a.wq + (int64_t)(n < a.N ? n : a.N - 1) * K + wv * KW + 16 * g;
 #pragma unroll
     for (int j = 0; j < KS; ++j) tr.b[j] = *(const u32x4 *)(row + 64 * j);
-    const int no = tile * kTileCols + (t & 15);
-    tr.sc = a.s[no < a.N ? no : a.N - 1];
-    tr.bias = a.ep.bias ? h2f(a.ep.bias[no < a.N ? no : a.N - 1]) : 0.f;
   };
-  // W rows of outlier columns p0 .. p0 + 63 for the tile: thread t < 128 loads
-  // row p0 + t / 2, columns 8 (t % 2) .. + 8 of the tile
-  // (with int8 outlier weights: the codes Wq[n, k] of those columns as fp16)
-  auto load_wo = [&](int tile, int p0, int np) {
-    const int p = t >> 1, half = t & 1;
-    const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
-    const int nc = tile * kTileCols + 8 * half;
-    if (a.ep.int8w) {
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c0 = nc + 2 * e, c1 = c0 + 1;
-        const int q0 = a.wq[(int64_t)(c0 < a.N ? c0 : a.N - 1) * K + kk];
-        const int q1 = a.wq[(int64_t)(c1 < a.N ? c1 : a.N - 1) * K + kk];
-        v[e] = (uint32_t)f2h((float)q0) | ((uint32_t)f2h((float)q1) << 16);
-      }
-      return v;
+  auto load_b = [&](TileRegs &tr, int tile) {
+    load_wq(tr, tile);
+    load_cols(tr, tile);
+  };
+  // Weights of outlier columns p0 .. p0 + 63 (np of them, at least one) for
+  // the tile. fp16: thread t loads row p0 + (t / 2) % 64, columns 8 (t % 2) ..
+  // + 8 of the tile (threads t >= 128 repeat the loads of t % 128). I8W: thread
+  // t loads the codes Wq[n, k] of outlier p0 + t / 8 for the two columns
+  // n = 2 (t % 8), + 1 of the tile.
+  auto load_wo = [&](TileRegs &tr, int tile, int p0, int np) {
+    if constexpr (I8W) {
+      const int p = t >> 3;
+      const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+      const int c0 = tile * kTileCols + 2 * (t & 7), c1 = c0 + 1;
+      tr.q0 = a.wq[(int64_t)(c0 < a.N ? c0 : a.N - 1) * K + kk];
+      tr.q1 = a.wq[(int64_t)(c1 < a.N ? c1 : a.N - 1) * K + kk];
+    } else {
+      const int p = (t >> 1) & (kBatch - 1), half = t & 1;
+      const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
+      const int nc = tile * kTileCols + 8 * half;
+      tr.wo = *(const u32x4 *)(a.w + kk * a.ldw + (nc < a.N ? nc : a.N - 8));
     }
-    return *(const u32x4 *)(a.w + kk * a.ldw + (nc < a.N ? nc : a.N - 8));
+  };
+  // stage the batch's weights as fp16 [kBatch][16] in swo
+  auto stage_wo = [&](const TileRegs &tr, uint16_t *swo) {
+    if constexpr (I8W) {
+      *(uint32_t *)(swo + (t >> 3) * 16 + 2 * (t & 7)) =
+          (uint32_t)f2h((float)tr.q0) | ((uint32_t)f2h((float)tr.q1) << 16);
+    } else {
+      if (t < 2 * kBatch) *(u32x4 *)(swo + (t >> 1) * 16 + 8 * (t & 1)) = tr.wo;
+    }
   };
   // 2. X: chunk c of rows h + R j (rows past M read as zero: harmless for every
   //    max, and their codes are replaced by zeros). X is issued before Wq: loads
@@ -212,6 +238,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     xc0 = *(const f32x4 *)(a.xcmax + 8 * c);
     xc1 = *(const f32x4 *)(a.xcmax + 8 * c + 4);
   }
+  // the first tile's scales and bias bits ahead of everything else: they may
+  // be used as soon as they arrive
+  TileRegs tr0, tr1;
+  load_cols(tr0, blockIdx.x);
   u32x4 xv[MR];
   {
     // one buffer resource over rows 0 .. M-1: rows past M read as zero and
@@ -225,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(r * a.ldx * 2 + 16 * c), 0, 0));
     }
   }
-  TileRegs tr0, tr1;
-  load_b(tr0, blockIdx.x);
+  __builtin_amdgcn_sched_barrier(0);  // every X load ahead of the Wq bytes
+  load_wq(tr0, blockIdx.x);
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. column magnitudes, as 16-bit patterns, two per 32-bit word
@@ -323,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     int pos = incl - cnt;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
+      spos[lane * CPL + q] = (uint16_t)pos;
       uint32_t bb = cb[q];
       while (bb) {
         slist[pos++] = (uint16_t)(8 * (lane * CPL + q) + __builtin_ctz(bb));
@@ -336,21 +367,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   }
   __syncthreads();
 
-  // first batch of the fp16 outlier product: its X entries (tile independent)
-  // and the W rows of the first tile, in flight while the codes are computed
+  // first batch of the outlier product: the weights of the first tile are
+  // loaded now (behind the Wq bytes, used after the MFMAs); the X entries come
+  // from the registers below
   const int total = *stotal;
-  const bool outl = total > 0 && (a.w || a.ep.int8w);
+  const bool outl = total > 0 && (a.w || I8W);
   const int np0 = total < kBatch ? total : kBatch;
-  float xo0[2] = {0.f, 0.f};
-  if (outl) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {  // 16 rows x 64 columns, two per thread
-      const int q = t + kThreads * u, r = q / kBatch, p = q % kBatch;
-      const int64_t kk = slist[p < np0 ? p : np0 - 1];
-      xo0[u] = h2f(a.X[(int64_t)(r < a.M ? r : a.M - 1) * a.ldx + kk]);
-    }
-    if (t < 2 * kBatch) tr0.wo = load_wo(blockIdx.x, 0, np0);
-  }
+  if (outl) load_wo(tr0, blockIdx.x, 0, np0);
 
   // 5. int8 codes into LDS; rows M .. MB * 16 - 1 are zero
   {
@@ -366,10 +389,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
       *(u32x2 *)(sxq + r * P + 8 * c) = out;
     }
   }
+  // X entries of the first batch, [16][kBatch] fp32: each thread places the
+  // outlier columns of its chunk (list positions from spos)
   float *sxo0 = (float *)(lds + L.xo0);
-  if (outl) {
-    sxo0[t] = xo0[0];
-    sxo0[t + kThreads] = xo0[1];
+  if (ob != 0u) {
+    uint32_t bb = ob;
+    int p = spos[c];
+    while (bb && p < kBatch) {
+      const int e = __builtin_ctz(bb);
+      bb &= bb - 1u;
+#pragma unroll
+      for (int j = 0; j < MR; ++j) {
+        const uint32_t w = xv[j][e >> 1];
+        sxo0[(h + R * j) * kBatch + p] = h2f((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+      }
+      ++p;
+    }
   }
   __syncthreads();
 
@@ -420,8 +455,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
         const int np = (total - p0 < kBatch) ? total - p0 : kBatch;
         // the first batch was loaded ahead; later ones are loaded here
         const float *xs = p0 == 0 ? sxo0 : sxo;
-        if (t < 2 * kBatch)
-          *(u32x4 *)(swo + (t >> 1) * 16 + 8 * (t & 1)) = p0 == 0 ? tr.wo : load_wo(tile, p0, np);
+        if (p0 == 0) {
+          stage_wo(tr, swo);
+        } else {
+          TileRegs tw;
+          load_wo(tw, tile, p0, np);
+          stage_wo(tw, swo);
+        }
         if (p0 > 0) {
           for (int q = t; q < MB * 16 * kBatch; q += kThreads) {  // X entries
             const int r = q / kBatch, p = q % kBatch;
@@ -441,13 +481,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
       }
     }
     // with int8 outlier weights the outlier terms carry the codes: times s / 127
-    const float oscale = a.ep.int8w ? tr.sc * (1.0f / 127.0f) : 1.0f;
+    const float oscale = I8W ? tr.sc * (1.0f / 127.0f) : 1.0f;
+    const float bias = a.ep.bias ? h2f((uint16_t)tr.braw) : 0.f;
     float cmax = 0.f;
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int q = t + kThreads * u;
       const int orow = q >> 4, n = tile * kTileCols + (q & 15);
-      const float v = y[u] + yo[u] * oscale + tr.bias;
+      const float v = y[u] + yo[u] * oscale + bias;
       if (q < MB * 256 && orow < a.M && n < a.N) a.y[(int64_t)orow * a.ldy + n] = f2h(v);
       cmax = (q < MB * 256 && orow < a.M) ? __builtin_fmaxf(cmax, stored_abs(v)) : cmax;
     }
@@ -470,14 +511,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     const int t1 = tile + G;
     if (t1 < a.tiles) {
       load_b(tr1, t1);
-      if (outl && t < 2 * kBatch) tr1.wo = load_wo(t1, 0, np0);
+      if (outl) load_wo(tr1, t1, 0, np0);
     }
     run_tile(tr0, tile);
     if (t1 >= a.tiles) break;
     const int t2 = t1 + G;
     if (t2 < a.tiles) {
       load_b(tr0, t2);
-      if (outl && t < 2 * kBatch) tr0.wo = load_wo(t2, 0, np0);
+      if (outl) load_wo(tr0, t2, 0, np0);
     }
     run_tile(tr1, t1);
     if (t2 >= a.tiles) break;
@@ -485,10 +526,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   }
 }
 
-template <int K, int MB>
+template <int K, int MB, bool I8W>
 hipError_t launch_fused_kmb(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream) {
   constexpr FusedLds L = fused_lds(K, MB);
-  hipError_t e = hipFuncSetAttribute((const void *)k_decode_fused<K, MB>,
+  hipError_t e = hipFuncSetAttribute((const void *)k_decode_fused<K, MB, I8W>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
@@ -496,14 +537,15 @@ hipError_t launch_fused_kmb(const FusedArgs &a, const GemmEvents &ev, hipStream_
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int grid = a.tiles < cus ? a.tiles : cus;
-  hipExtLaunchKernelGGL((k_decode_fused<K, MB>), dim3(grid), dim3(kThreads), L.total, stream,
+  hipExtLaunchKernelGGL((k_decode_fused<K, MB, I8W>), dim3(grid), dim3(kThreads), L.total, stream,
                         (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();
 }
 
 template <int K>
 hipError_t launch_fused_k(const FusedArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  return launch_fused_kmb<K, 1>(a, ev, stream);
+  return a.ep.int8w ? launch_fused_kmb<K, 1, true>(a, ev, stream)
+                    : launch_fused_kmb<K, 1, false>(a, ev, stream);
 }
 
 }  // namespace
