@@ -8,10 +8,10 @@
 // kernel needs none: every block recomputes what it needs from X.
 //
 // Block b (512 threads, persistent over the 16-column tiles b, b + G, ...):
-//  1. loads all of X into registers, then issues the Wq loads of its first tile
-//     (they stream while 2-5 run). Loads complete in issue order, so no value
-//     loaded after the Wq bytes is used before the tile's MFMAs: a use any
-//     earlier would wait for the whole Wq stream, and 2-5 with it;
+//  1. loads all of X into registers and, once X has arrived, issues the Wq
+//     loads of its first tile (they stream while 3-5 run). Loads complete in
+//     issue order, so no value loaded after the Wq bytes is used before the
+//     tile's MFMAs: a use any earlier would wait for the whole Wq stream;
 //  2. X in registers: thread (c, h) holds the 16-byte chunk c
 //     (columns 8c .. 8c+7) of rows h, h + R, ... (R = 512 / (K / 8));
 //  3. column absmax over all rows with packed 16-bit max on the magnitude bits
@@ -20,7 +20,8 @@
 //     walkthrough, sections 2.3 and 4.2);
 //  4. row absmax over the kept columns the same way, reduced across the block;
 //     fl32(127 / m) per row (pitfalls page, section 1);
-//  5. int8 codes of every row into LDS (outlier columns zero), once per block;
+//  5. int8 codes of the rows below M into LDS (outlier columns zero), once per
+//     block;
 //  6. per tile: 16x16x64 int8 MFMAs with the wave's eighth of K, a fixed-order
 //     sum of the eight wave partials in LDS (exact int32 C), dequantize by
 //     m_i * s_j / 127^2, add the fp16 outlier terms X_O . W_O in fp32 (pitfalls
@@ -190,14 +191,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     tr.sc = a.s[no < a.N ? no : a.N - 1];
     tr.braw = bias_src[no < a.N ? no : a.N - 1];
   };
-  auto load_wq = [&](TileRegs &tr, int tile) {
+  auto load_wq = [&](TileRegs &tr, int tile, int dep) {
     const int n = tile * kTileCols + c16;
-    const int8_t *row = a.wq + (int64_t)(n < a.N ? n : a.N - 1) * K + wv * KW + 16 * g;
+    const int8_t *row = a.wq + (int64_t)(n < a.N ? n : a.N - 1) * K + wv * KW + 16 * g + dep;
 #pragma unroll
     for (int j = 0; j < KS; ++j) tr.b[j] = *(const u32x4 *)(row + 64 * j);
   };
   auto load_b = [&](TileRegs &tr, int tile) {
-    load_wq(tr, tile);
+    load_wq(tr, tile, 0);
     load_cols(tr, tile);
   };
   // Weights of outlier columns p0 .. p0 + 63 (np of them, at least one) for
@@ -255,16 +256,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(r * a.ldx * 2 + 16 * c), 0, 0));
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // every X load ahead of the Wq bytes
-  load_wq(tr0, blockIdx.x);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. column magnitudes, as 16-bit patterns, two per 32-bit word
+  // 3. column magnitudes, as 16-bit patterns, two per 32-bit word. X is
+  // waited for before the Wq loads are issued: measured on this hardware, a
+  // load issued together with the Wq stream returns only when the stream is
+  // nearly done, and everything up to the MFMAs depends on X.
   uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < MR; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) cm[e] = pmax16(cm[e], xv[j][e] & 0x7fff7fffu);
+  // a zero the compiler cannot see through, computed from the column maxima:
+  // added to the Wq addresses, it keeps their loads behind the wait for X
+  int xdep = (int)cm[0];
+  asm volatile("v_and_b32 %0, 0, %0" : "+v"(xdep));
+  load_wq(tr0, blockIdx.x, xdep);
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (R > 1) {
     u32x4 *scm = (u32x4 *)sred;  // [R][C]
     scm[h * C + c] = (u32x4){cm[0], cm[1], cm[2], cm[3]};
@@ -375,18 +383,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   const int np0 = total < kBatch ? total : kBatch;
   if (outl) load_wo(tr0, blockIdx.x, 0, np0);
 
-  // 5. int8 codes into LDS; rows M .. MB * 16 - 1 are zero
+  // 5. int8 codes into LDS for rows below M (the MFMA rows past M only reach
+  //    outputs that are never stored, so their LDS rows are left as they are)
   {
     const uint32_t kl = keep_bytes(ob & 0xfu), kh = keep_bytes(ob >> 4);
 #pragma unroll
     for (int j = 0; j < MR; ++j) {
       const int r = h + R * j;
-      const float inv = sinv[r];
-      u32x2 out;
-      out[0] = codes4(xv[j][0], xv[j][1], inv) & kl;
-      out[1] = codes4(xv[j][2], xv[j][3], inv) & kh;
-      if (r >= a.M) out = (u32x2){0u, 0u};
-      *(u32x2 *)(sxq + r * P + 8 * c) = out;
+      if (r < a.M) {
+        const float inv = sinv[r];
+        u32x2 out;
+        out[0] = codes4(xv[j][0], xv[j][1], inv) & kl;
+        out[1] = codes4(xv[j][2], xv[j][3], inv) & kh;
+        *(u32x2 *)(sxq + r * P + 8 * c) = out;
+      }
     }
   }
   // X entries of the first batch, [16][kBatch] fp32: each thread places the
@@ -401,7 +411,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
 #pragma unroll
       for (int j = 0; j < MR; ++j) {
         const uint32_t w = xv[j][e >> 1];
-        sxo0[(h + R * j) * kBatch + p] = h2f((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+        if (h + R * j < a.M)
+          sxo0[(h + R * j) * kBatch + p] = h2f((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
       }
       ++p;
     }
