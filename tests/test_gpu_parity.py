@@ -143,9 +143,11 @@ def test_small_m_structure(dev, M, K, N):
 
 # Shapes of the single-kernel small-M path (K in {1024, 2048, 4096}): one and
 # several 16-column tiles per block (N = 11008 gives 688 tiles), partial last
-# tiles, 1 to 64 rows.
+# tiles, 1 to 64 rows. With K = 2048 and 1024 two and four threads share an X
+# chunk, so the rows below M end inside a thread group (M = 3, 10, 13).
 FUSED = [(1, 4096, 8), (5, 4096, 4104), (16, 2048, 24), (17, 2048, 11008), (32, 4096, 11008),
-         (33, 1024, 520), (64, 1024, 4096), (32, 1024, 16)]
+         (33, 1024, 520), (64, 1024, 4096), (32, 1024, 16), (3, 1024, 264), (10, 2048, 136),
+         (13, 1024, 4096)]
 
 
 @pytest.mark.parametrize("M,K,N", FUSED)
