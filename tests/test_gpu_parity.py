@@ -228,21 +228,26 @@ def test_deterministic(dev):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-def test_strided_inputs(dev):
+# one shape per path: split-K small M, the single kernel (M <= 16, K = 1024),
+# large M
+@pytest.mark.parametrize("M,K,N", [(50, 128, 40), (8, 1024, 40), (130, 256, 72)])
+def test_strided_inputs(dev, M, K, N):
     torch, lm = dev
-    say("case strided leading dimensions")
-    X, W, _ = workloads.random_case(50, 128, 40, 14, n_out=2)
-    Xd_big = torch.zeros((50, 160), dtype=torch.float16, device="cuda")
-    Xd_big[:, :128] = to_gpu(torch, X)
-    Wd_big = torch.zeros((128, 56), dtype=torch.float16, device="cuda")
-    Wd_big[:, :40] = to_gpu(torch, W)
-    Xv, Wv = Xd_big[:, :128], Wd_big[:, :40]
+    say(f"case strided leading dimensions M={M} K={K} N={N}")
+    X, W, _ = workloads.random_case(M, K, N, 14, n_out=2)
+    Xd_big = torch.zeros((M, K + 32), dtype=torch.float16, device="cuda")
+    Xd_big[:, :K] = to_gpu(torch, X)
+    Wd_big = torch.zeros((K, N + 16), dtype=torch.float16, device="cuda")
+    Wd_big[:, :N] = to_gpu(torch, W)
+    Xv, Wv = Xd_big[:, :K], Wd_big[:, :N]
     Wq, s = lm.llmint8_quantize_colwise(Wv)
-    Yd_big = torch.full((50, 48), 7.0, dtype=torch.float16, device="cuda")
-    lm.llmint8_linear(Xv, Wq, s, Wv, 6.0, Y=Yd_big[:, :40])
+    Yd_big = torch.full((M, N + 8), 7.0, dtype=torch.float16, device="cuda")
+    C = torch.zeros((M, N), dtype=torch.int32, device="cuda")
+    lm.llmint8_linear(Xv, Wq, s, Wv, 6.0, Y=Yd_big[:, :N], C_debug=C)
     ref = oracle.linear(X, W, 6.0)
-    assert_y_close(Yd_big[:, :40].cpu().numpy(), ref["Y"], "Y")
-    assert torch.all(Yd_big[:, 40:] == 7.0)
+    assert np.array_equal(C.cpu().numpy(), ref["C"])
+    assert_y_close(Yd_big[:, :N].cpu().numpy(), ref["Y"], "Y")
+    assert torch.all(Yd_big[:, N:] == 7.0)
 
 
 # --- the five workloads ----------------------------------------------------------
