@@ -41,9 +41,17 @@ HBM_BOUND = ("tiny", "decode")
 DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources that define the GEMM kernels (small-M and large-M)
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc", f)
-                  for f in ("common.hpp", "internal.hpp", "decode.hip", "decode_fused.hip",
-                            "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")]
+# Sources of the GEMM kernels whose HBM counters are committed: the small-M
+# kernels (up to 64 rows) and the large-M ones, digested separately so that a
+# change to one family leaves the other's counters valid.
+_CSRC = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc")
+KERNEL_SOURCES = {
+    "small_m": [os.path.join(_CSRC, f) for f in
+                ("common.hpp", "internal.hpp", "decode.hip", "decode_fused.hip")],
+    "large_m": [os.path.join(_CSRC, f) for f in
+                ("common.hpp", "internal.hpp", "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")],
+}
+SMALL_M_MAX = 64  # rows up to which the layer runs the small-M kernels
 
 
 def _code_only(text: str) -> str:
@@ -54,9 +62,14 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_digest() -> str:
+def kernel_family(workload: str) -> str:
+    import workloads
+    return "small_m" if workloads.WORKLOADS[workload].M <= SMALL_M_MAX else "large_m"
+
+
+def kernel_source_digest(family: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(p, encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -75,7 +88,7 @@ def read_traffic(workload: str, variant: str = "int8"):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_digest") != kernel_source_digest():
+    if vals.get("kernel_source_digest") != kernel_source_digest(kernel_family(workload)):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])

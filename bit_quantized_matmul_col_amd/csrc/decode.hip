@@ -349,14 +349,18 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
     }
   }
 
-  // partial sums: lane holds rows 4g + r of each 16-row block, column ncol
+  // partial sums: lane holds rows 4g + r of each 16-row block, column ncol.
+  // Nontemporal stores: the epilogue kernel reads them once, and lines left
+  // dirty in L2 would only lengthen the write-back at the end of this kernel
+  // (measured 0.08 us per decode call).
   if (ncol < a.N) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = mb * 16 + 4 * g + r;
-        if (row < a.M) a.part[((int64_t)kb * a.M + row) * a.N + ncol] = acc[mb][r];
+        if (row < a.M)
+          __builtin_nontemporal_store(acc[mb][r], &a.part[((int64_t)kb * a.M + row) * a.N + ncol]);
       }
   }
 }
