@@ -434,30 +434,40 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uin
   int64_t rows = a.M - m0;
   rows = rows < BM ? rows : BM;
   const rsrc_t ry = make_rsrc(a.y + m0 * a.ldy, rows * a.ldy * 2);
+  // the NI column blocks of a row are stored back to back, so that the wave
+  // writes whole 128-byte lines of Y (the halves of a line written far apart
+  // reached HBM as partial-line writes)
+  bool colok[NI];
+  float fin[NI], bcol[NI], cmax[NI];  // cmax: |Y| of the column over the wave's rows
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     const int cl = wn * WN + ni * 32 + li;
-    const bool colok = n0 + cl < a.N;
-    const float fin = sf[cl];
-    const float b = (a.ep.bias && colok) ? h2f(a.ep.bias[n0 + cl]) : 0.f;
-    float cmax = 0.f;  // |Y| of this column over the wave's rows
+    colok[ni] = n0 + cl < a.N;
+    fin[ni] = sf[cl];
+    bcol[ni] = (a.ep.bias && colok[ni]) ? h2f(a.ep.bias[n0 + cl]) : 0.f;
+    cmax[ni] = 0.f;
+  }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const f32x16 f = __builtin_bit_cast(f32x16, acc[mi * NI + ni]);
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const float y = f[r] * fin + b;
-        if (colok)
+    for (int r = 0; r < 16; ++r) {
+      const int rl = wm * WM + mi * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int cl = wn * WN + ni * 32 + li;
+        const float y = __builtin_bit_cast(f32x16, acc[mi * NI + ni])[r] * fin[ni] + bcol[ni];
+        if (colok[ni])
           __builtin_amdgcn_raw_buffer_store_b16(f2h(y), ry,
                                                 (rl * (int)a.ldy + (int)(n0 + cl)) * 2, 0, 0);
-        cmax = __builtin_fmaxf(cmax, stored_abs(y));
+        cmax[ni] = __builtin_fmaxf(cmax[ni], stored_abs(y));
       }
     }
-    if (a.ep.ycmax) {
+  if (a.ep.ycmax) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
       // lanes l and l + 32 hold the same column
-      cmax = __builtin_fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      if (lg == 0 && colok) ycmax_update(a.ep.ycmax, n0 + cl, cmax);
+      const float cm = __builtin_fmaxf(cmax[ni], __shfl_xor(cmax[ni], 32, 64));
+      if (lg == 0 && colok[ni]) ycmax_update(a.ep.ycmax, n0 + wn * WN + ni * 32 + li, cm);
     }
   }
 }
