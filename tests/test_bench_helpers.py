@@ -49,3 +49,31 @@ def test_multi_gpu_run_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert out.returncode == 2
     assert "one GPU" in out.stderr
+
+
+def test_counter_digest_families(tmp_path, monkeypatch):
+    # decode-sized workloads read the small-M kernels' counters, the others the
+    # large-M ones; each digest covers only its own family's sources
+    assert bench.kernel_family("decode") == "small_m" and bench.kernel_family("tiny") == "small_m"
+    for w in ("prefill", "13b", "70b"):
+        assert bench.kernel_family(w) == "large_m"
+    small = set(map(os.path.basename, bench.KERNEL_SOURCES["small_m"]))
+    large = set(map(os.path.basename, bench.KERNEL_SOURCES["large_m"]))
+    assert "decode.hip" in small and "decode.hip" not in large
+    assert "gemm_core.hpp" in large and "gemm_core.hpp" not in small
+    # comments and blank space do not change a digest; code does
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }  // one\n")
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "small_m", [str(src)])
+    d0 = bench.kernel_source_digest("small_m")
+    src.write_text("/* header */\nint f() {\n  return 1;\n}\n// two\n")
+    assert bench.kernel_source_digest("small_m") == d0
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_digest("small_m") != d0
+
+
+def test_committed_counters_match_the_sources():
+    # every committed counter summary was taken on the kernels as they are
+    for w in ("decode", "prefill", "13b", "70b"):
+        for v in ("int8", "fp8"):
+            assert bench.read_traffic(w, v) is not None, (w, v)
