@@ -641,3 +641,42 @@ def test_gemm_split_into_wide_and_narrow_launches(dev, variant):
     y = Y.cpu().numpy()
     assert_y_close(y, ref["Y"], "Y")
     assert np.array_equal(ycm.cpu().numpy(), np.abs(y.astype(np.float32)).max(axis=0))
+
+
+# --- seeded random shapes ----------------------------------------------------------
+
+def _random_shapes(n, seed):
+    """Shapes over all three layer paths: the single kernel (M <= 16, K in
+    {1024, 2048, 4096}), the split-K small-M kernels (M <= 64) and the large-M
+    GEMM, with ragged M, K a multiple of 16 and N a multiple of 8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = i % 3
+        if kind == 0:
+            M, K = int(rng.integers(1, 17)), int(rng.choice([1024, 2048, 4096]))
+        elif kind == 1:
+            M, K = int(rng.integers(1, 65)), 16 * int(rng.integers(1, 260))
+        else:
+            M, K = int(rng.integers(65, 400)), 16 * int(rng.integers(1, 130))
+        N = 8 * int(rng.integers(1, 140))
+        u = float(rng.uniform(1.5, 8.0))
+        threshold = float(rng.choice([0.0, math.inf, u, u, u]))  # mostly a real split
+        out.append((M, K, N, threshold, int(rng.integers(0, 6)), 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,threshold,n_out,seed", _random_shapes(24, 2024))
+def test_random_shapes(dev, M, K, N, threshold, n_out, seed):
+    torch, lm = dev
+    say(f"case random M={M} K={K} N={N} threshold={threshold} n_out={n_out} seed={seed}")
+    X, W, _ = workloads.random_case(M, K, N, seed=seed, n_out=n_out)
+    run_all(torch, lm, X, W, threshold)
+
+
+@pytest.mark.parametrize("M,K,N,threshold,n_out,seed", _random_shapes(12, 2025))
+def test_random_shapes_fp8(dev, M, K, N, threshold, n_out, seed):
+    torch, lm = dev
+    say(f"case random fp8 M={M} K={K} N={N} threshold={threshold} n_out={n_out} seed={seed}")
+    X, W, _ = workloads.random_case(M, K, N, seed=seed, n_out=n_out)
+    check_fp8_layer(torch, lm, X, W, threshold)
