@@ -27,7 +27,7 @@ namespace {
 constexpr int kDetCols = 128;      // columns per detection block (256: 1.2 us slower per step)
 constexpr int kDetChunks = kDetCols / 8;            // 16-byte column chunks per block
 constexpr int kDetRows = 256 / kDetChunks;          // row phases per detection block
-constexpr int kDetRowIters = kDecodeMaxM / kDetRows;  // rows per thread
+constexpr int kDetRowIters = kDecodeMaxM / kDetRows;  // rows per thread up to kDecodeMaxM
 constexpr int kTileN = 64;         // output columns per GEMM / epilogue block
 constexpr int kSubK = 512;         // k bytes staged per GEMM stage
 constexpr int kXPitch = kSubK + 16;
@@ -39,6 +39,9 @@ constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
 
 __device__ inline u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
 
+// RI rows per thread: the launch takes the fewest that cover M (loads of rows
+// past M, clamped to row 0, cost 0.3 us per call at M = 32 when RI covered 64)
+template <int RI>
 __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   static_assert(kDetCols % 64 == 0, "whole waves of column flags");
   __shared__ float scol[kDetRows][kDetCols];
@@ -58,9 +61,9 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
     xc = a.xcmax[col < a.K ? col : 0];
   }
 
-  u32x4 v[kDetRowIters];
+  u32x4 v[RI];
 #pragma unroll
-  for (int j = 0; j < kDetRowIters; ++j) {
+  for (int j = 0; j < RI; ++j) {
     const int row = ph + kDetRows * j;
     const bool ok = colok && row < a.M;
     const u32x4 x = *(const u32x4 *)(base + (ok ? (int64_t)row * a.ldx : 0));
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   }
   float cm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < kDetRowIters; ++j) absmax8(v[j], cm);
+  for (int j = 0; j < RI; ++j) absmax8(v[j], cm);
 #pragma unroll
   for (int e = 0; e < 8; ++e) scol[ph][c * 8 + e] = cm[e];
   __syncthreads();
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
   // phase (consecutive lanes) reduce
   const unsigned ob = (sflag[c >> 2] >> ((c & 3) * 8)) & 0xffu;
 #pragma unroll
-  for (int j = 0; j < kDetRowIters; ++j) {
+  for (int j = 0; j < RI; ++j) {
     const int row = ph + kDetRows * j;
     float mx = 0.f;
 #pragma unroll
@@ -595,7 +598,13 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream) {
-  hipLaunchKernelGGL(k_decode_detect, dim3(plan.det_blocks), dim3(256), 0, stream, det);
+  static_assert(kDetRowIters == 4, "detection row iterations");
+  if (det.M <= kDetRows)
+    hipLaunchKernelGGL(k_decode_detect<1>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
+  else if (det.M <= 2 * kDetRows)
+    hipLaunchKernelGGL(k_decode_detect<2>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
+  else
+    hipLaunchKernelGGL(k_decode_detect<4>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return gemm.fp8 ? launch_decode_kernels<true>(gemm, plan, ev, stream)
