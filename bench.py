@@ -48,13 +48,13 @@ HBM_BOUND = ("tiny", "decode")
 DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources that define the GEMM kernels (small-M and large-M)
-# Sources of the GEMM kernels whose HBM counters are committed: the small-M
-# kernels (up to 64 rows) and the large-M ones, digested separately so that a
+# Sources of the GEMM kernels whose HBM counters are committed: the split-K
+# small-M kernels (up to 64 rows; the single-kernel path runs none of the
+# workloads with counters) and the large-M ones, digested separately so that a
 # change to one family leaves the other's counters valid.
 _CSRC = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc")
 KERNEL_SOURCES = {
-    "small_m": [os.path.join(_CSRC, f) for f in
-                ("common.hpp", "internal.hpp", "decode.hip", "decode_fused.hip")],
+    "small_m": [os.path.join(_CSRC, f) for f in ("common.hpp", "internal.hpp", "decode.hip")],
     "large_m": [os.path.join(_CSRC, f) for f in
                 ("common.hpp", "internal.hpp", "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")],
 }
