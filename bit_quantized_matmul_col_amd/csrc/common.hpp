@@ -98,6 +98,21 @@ __device__ inline void absmax8(const u32x4 &v, float *mx) {
 __device__ inline float fp16_lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ inline float fp16_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
+// fl32(x * s) for the fp16 x in the low (fp16_lo_mul) or high (fp16_hi_mul)
+// half of w: one v_fma_mix_f32 with a +0 addend does the conversion and the
+// product with a single fp32 rounding, the same value as converting and then
+// multiplying (only the sign of a zero product can differ).
+__device__ inline float fp16_lo_mul(uint32_t w, float s) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(s));
+  return r;
+}
+__device__ inline float fp16_hi_mul(uint32_t w, float s) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(s));
+  return r;
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));

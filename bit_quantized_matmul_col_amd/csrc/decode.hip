@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
 }
 
 // Four int8 codes of the fp16 pairs (w0, w1) for the scale inv, packed in
-// byte order. The fp32 product x * inv is rounded first; adding 1.5 * 2^23 then
+// byte order. The fp32 product x * inv is rounded first (fp16_lo_mul /
+// fp16_hi_mul; the sign of a zero product does not matter); adding 1.5 * 2^23 then
 // rounds it to the nearest integer, ties to even (the sum's unit in the last
 // place is 1), and leaves that integer in two's complement in the low bits of
 // the sum. The product never exceeds 127 in magnitude by more than a few ulps
@@ -123,10 +124,10 @@ __global__ __launch_bounds__(256) void k_decode_detect(DecodeDetectArgs a) {
 __device__ inline uint32_t codes4(uint32_t w0, uint32_t w1, float inv) {
 #pragma clang fp contract(off)
   const float kMagic = 12582912.0f;
-  const uint32_t q0 = __builtin_bit_cast(uint32_t, fp16_lo(w0) * inv + kMagic);
-  const uint32_t q1 = __builtin_bit_cast(uint32_t, fp16_hi(w0) * inv + kMagic);
-  const uint32_t q2 = __builtin_bit_cast(uint32_t, fp16_lo(w1) * inv + kMagic);
-  const uint32_t q3 = __builtin_bit_cast(uint32_t, fp16_hi(w1) * inv + kMagic);
+  const uint32_t q0 = __builtin_bit_cast(uint32_t, fp16_lo_mul(w0, inv) + kMagic);
+  const uint32_t q1 = __builtin_bit_cast(uint32_t, fp16_hi_mul(w0, inv) + kMagic);
+  const uint32_t q2 = __builtin_bit_cast(uint32_t, fp16_lo_mul(w1, inv) + kMagic);
+  const uint32_t q3 = __builtin_bit_cast(uint32_t, fp16_hi_mul(w1, inv) + kMagic);
   return (q0 & 0xffu) | ((q1 & 0xffu) << 8) | ((q2 & 0xffu) << 16) | (q3 << 24);
 }
 
@@ -180,11 +181,12 @@ __device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st,
 
 // Four E4M3 codes of the fp16 pairs (w0, w1) for the scale inv = fl32(448 /
 // absmax): the fp32 products, then the hardware conversion (nearest, ties to
-// even).
+// even). A zero product always codes as +0 here, where a plain multiply would
+// give -0 for a negative x on a row of scale zero; the sums are the same.
 __device__ inline uint32_t codes4_e4m3(uint32_t w0, uint32_t w1, float inv) {
 #pragma clang fp contract(off)
-  const float t[4] = {fp16_lo(w0) * inv, fp16_hi(w0) * inv, fp16_lo(w1) * inv,
-                      fp16_hi(w1) * inv};
+  const float t[4] = {fp16_lo_mul(w0, inv), fp16_hi_mul(w0, inv), fp16_lo_mul(w1, inv),
+                      fp16_hi_mul(w1, inv)};
   return CodecE4M3::code4(t);
 }
 

@@ -38,29 +38,18 @@ constexpr int kTileCols = 16;
 constexpr int kBatch = 64;     // outlier columns staged per round of the fp16 product
 
 // Four int8 codes of the fp16 pairs (w0, w1) for the scale inv, packed in byte
-// order. v_fma_mix_f32 multiplies the fp16 half by inv with one fp32 rounding
-// (adding +0 changes nothing but the sign of a zero product, which the next
-// step ignores). Adding 1.5 * 2^23 then rounds that product to the nearest
+// order: the fp32 products (fp16_lo_mul / fp16_hi_mul; a zero product's sign
+// does not matter here), then adding 1.5 * 2^23 rounds each to the nearest
 // integer, ties to even, and leaves it in two's complement in the low bits.
 // |x| <= absmax of its row keeps the product within 127 * (1 + 2^-22), so no
 // clamp is needed.
-__device__ inline float mul_lo(uint32_t w, float inv) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(inv));
-  return r;
-}
-__device__ inline float mul_hi(uint32_t w, float inv) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(inv));
-  return r;
-}
 __device__ inline uint32_t codes4(uint32_t w0, uint32_t w1, float inv) {
 #pragma clang fp contract(off)
   const float kMagic = 12582912.0f;
-  const uint32_t q0 = __builtin_bit_cast(uint32_t, mul_lo(w0, inv) + kMagic);
-  const uint32_t q1 = __builtin_bit_cast(uint32_t, mul_hi(w0, inv) + kMagic);
-  const uint32_t q2 = __builtin_bit_cast(uint32_t, mul_lo(w1, inv) + kMagic);
-  const uint32_t q3 = __builtin_bit_cast(uint32_t, mul_hi(w1, inv) + kMagic);
+  const uint32_t q0 = __builtin_bit_cast(uint32_t, fp16_lo_mul(w0, inv) + kMagic);
+  const uint32_t q1 = __builtin_bit_cast(uint32_t, fp16_hi_mul(w0, inv) + kMagic);
+  const uint32_t q2 = __builtin_bit_cast(uint32_t, fp16_lo_mul(w1, inv) + kMagic);
+  const uint32_t q3 = __builtin_bit_cast(uint32_t, fp16_hi_mul(w1, inv) + kMagic);
   return (q0 & 0xffu) | ((q1 & 0xffu) << 8) | ((q2 & 0xffu) << 16) | (q3 << 24);
 }
 
