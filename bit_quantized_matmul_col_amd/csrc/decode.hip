@@ -386,7 +386,13 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   const int64_t colc = colok ? col : 0;
   const int rbase = blockIdx.y * 16;
 
-  // every independent load first: partial sums, scales, the first mask window
+  // every independent load first, the first mask window ahead of the rest:
+  // the outlier chain (mask, list, W rows and X entries) is the longest
+  // dependent path of the block, and loads complete in issue order
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
+  uint32_t mw = __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0);
+
   int pp[4][KB];
   float mrow[4];
 #pragma unroll
@@ -401,34 +407,16 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   // loads without a condition (a bias-less call reads its bias bits from s):
   // a load under a branch is waited for at once, and with it every earlier one
   const uint16_t braw = (a.ep.bias ? a.ep.bias : (const uint16_t *)a.s)[colc];
+  // wait for the mask word alone here (the partial sums stay in flight); left
+  // to itself the compiler sinks its load below all the others
+  asm volatile("" ::"v"(mw));
   // the outlier product runs with fp16 weight rows or with the int8 codes
   const bool i8w = a.ep.int8w != 0;
   const bool outl = a.w || i8w;
-  const __amdgpu_buffer_rsrc_t mrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
-  uint32_t mw = __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0);
-
-  float y[4], yo[4] = {0.f, 0.f, 0.f, 0.f};
-  const float sd = scol * (F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int cacc = 0;
-    float cf = 0.f;
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      if constexpr (F8)
-        cf += __builtin_bit_cast(float, pp[i][k]);
-      else
-        cacc += pp[i][k];
-    }
-    const int row = rbase + wv + 4 * i;
-    if (a.cdbg && row < a.M && colok)
-      a.cdbg[(int64_t)row * a.N + col] = F8 ? __builtin_bit_cast(int, cf) : cacc;
-    y[i] = (F8 ? cf : (float)cacc) * (mrow[i] * sd);
-  }
-
+  float yo[4] = {0.f, 0.f, 0.f, 0.f};
   // fp16 outlier terms, outlier columns in ascending order (yo: with int8
-  // weight codes they are scaled by s / 127 at the end)
+  // weight codes they are scaled by s / 127 at the end); the partial sums are
+  // added after them, so the chain does not wait for the partial sums
   int total_all = 0;
   if (outl) {
     for (int64_t w0 = 0; w0 < a.kw; w0 += kListWords) {
@@ -462,10 +450,23 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
       __syncthreads();
       for (int p0 = 0; p0 < total; p0 += kOutBatch) {
         const int np = (total - p0 < kOutBatch) ? total - p0 : kOutBatch;
-        // W rows and X entries of the batch. Entries past the batch, past N or
-        // past M read clamped addresses: they only reach outputs never stored
-        // or terms never summed.
-        {  // W rows: 32 rows x 8 chunks of 8 columns, one per thread
+        // W rows and X entries of the batch, all loaded before the first LDS
+        // store so that they share one round trip. Entries past the batch,
+        // past N or past M read clamped addresses: they only reach outputs
+        // never stored or terms never summed.
+        {  // X entries first (16 rows x 32 outliers, two per thread), then the
+           // W rows (32 rows x 8 chunks of 8 columns, one per thread)
+          uint32_t xe[2];
+          int xr[2], xp[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int q = t + 256 * h;
+            xr[h] = q >> 5;
+            xp[h] = q & 31;
+            const int row = rbase + xr[h];
+            const int64_t kk = slist[p0 + (xp[h] < np ? xp[h] : np - 1)];
+            xe[h] = a.X[(int64_t)(row < a.M ? row : a.M - 1) * a.ldx + kk];
+          }
           const int p = t >> 3, ch = t & 7;
           const int64_t cc = n0 + 8 * ch;
           const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
@@ -482,14 +483,8 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
             v = *(const u32x4 *)(a.w + kk * a.ldw + (cc < a.N ? cc : a.N - 8));
           }
           *(u32x4 *)(swo + p * kTileN + 8 * ch) = v;
-        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {  // X entries: 16 rows x 32 outliers
-          const int q = t + 256 * h;
-          const int r = q >> 5, p = q & 31;
-          const int row = rbase + r;
-          const int64_t kk = slist[p0 + (p < np ? p : np - 1)];
-          sxo[r][p] = h2f(a.X[(int64_t)(row < a.M ? row : a.M - 1) * a.ldx + kk]);
+          for (int h = 0; h < 2; ++h) sxo[xr[h]][xp[h]] = h2f((uint16_t)xe[h]);
         }
         __syncthreads();
         for (int p = 0; p < np; ++p) {
@@ -510,6 +505,25 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     if (lane == 0) scount[wv] = cnt;
     __syncthreads();
     if (t == 0) *a.count_out = scount[0] + scount[1] + scount[2] + scount[3];
+  }
+
+  float y[4];
+  const float sd = scol * (F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int cacc = 0;
+    float cf = 0.f;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if constexpr (F8)
+        cf += __builtin_bit_cast(float, pp[i][k]);
+      else
+        cacc += pp[i][k];
+    }
+    const int row = rbase + wv + 4 * i;
+    if (a.cdbg && row < a.M && colok)
+      a.cdbg[(int64_t)row * a.N + col] = F8 ? __builtin_bit_cast(int, cf) : cacc;
+    y[i] = (F8 ? cf : (float)cacc) * (mrow[i] * sd);
   }
 
   const float oscale = i8w ? scol * (1.0f / 127.0f) : 1.0f;
