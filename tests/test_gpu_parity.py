@@ -141,6 +141,39 @@ def test_small_m_structure(dev, M, K, N):
     run_all(torch, lm, X, W, 6.0)
 
 
+# The small-M epilogue stages the outlier terms 32 columns at a time: planted
+# columns on both sides of one batch, in rows spread over both 16-row blocks,
+# with fp16 and int8 outlier weights and in the FP8 layer (M = 32, K = 1024,
+# N = 520: the split-K path with two K splits).
+@pytest.mark.parametrize("n", [1, 31, 32, 33])
+@pytest.mark.parametrize("mode", ["fp16", "int8", "fp8"])
+def test_outlier_batch_edges(dev, n, mode):
+    torch, lm = dev
+    M, K, N = 32, 1024, 520
+    say(f"case outlier batch edges n={n} mode={mode}")
+    X, W, _ = workloads.random_case(M, K, N, seed=40 + n, n_out=0)
+    X = np.clip(X, np.float16(-5.0), np.float16(5.0))
+    cols = np.random.default_rng(n).choice(K, n, replace=False)
+    X[(7 * np.arange(n)) % M, cols] = np.float16(20.0)
+    assert oracle.find_outliers(X, 6.0).size == n
+    if mode == "fp16":
+        run_all(torch, lm, X, W, 6.0)
+    elif mode == "fp8":
+        check_fp8_layer(torch, lm, X, W, 6.0)
+    else:
+        Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+        Wq, s = lm.llmint8_quantize_colwise(Wd)
+        C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+        Y = lm.llmint8_linear(Xd, Wq, s, None, 6.0, outlier_weights="int8", C_debug=C,
+                              outlier_count=cnt)
+        torch.cuda.synchronize()
+        ref = oracle.linear(X, W, 6.0, outlier_weights="int8")
+        assert int(cnt.item()) == n
+        assert np.array_equal(C.cpu().numpy(), ref["C"]), "C differs"
+        assert_y_close(Y.cpu().numpy(), ref["Y"], "Y")
+
+
 # Shapes of the single-kernel small-M path (K in {1024, 2048, 4096}): one and
 # several 16-column tiles per block (N = 11008 gives 688 tiles), partial last
 # tiles, 1 to 64 rows. With K = 2048 and 1024 two and four threads share an X
