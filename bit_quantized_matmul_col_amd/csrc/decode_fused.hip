@@ -64,6 +64,17 @@ __device__ inline uint32_t pmax16(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(u16x2, b)));
 }
 
+// Magnitude patterns of the two fp16 in w, with NaN (patterns above 0x7c00)
+// taken as 0: a NaN entry never makes its column an outlier and never sets a
+// row maximum, as with the fmax-based maxima of the other paths. m + 0x3ff
+// reaches bit 15 of its half exactly when m > 0x7c00, and never carries out
+// of the half (m <= 0x7fff).
+__device__ inline uint32_t mag16(uint32_t w) {
+  const uint32_t m = w & 0x7fff7fffu;
+  const uint32_t nan = ((m + 0x03ff03ffu) & 0x80008000u) >> 15;
+  return m & ~(nan * 0xffffu);
+}
+
 // Layout of the dynamic LDS (byte offsets); P = K + 16 is the Xq row pitch
 // (16 rows that one MFMA operand reads fall in distinct bank groups).
 struct FusedLds {
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
 #pragma unroll
   for (int j = 0; j < MR; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cm[e] = pmax16(cm[e], xv[j][e] & 0x7fff7fffu);
+    for (int e = 0; e < 4; ++e) cm[e] = pmax16(cm[e], mag16(xv[j][e]));
   // a zero the compiler cannot see through, computed from the column maxima:
   // added to the Wq addresses, it keeps their loads behind the wait for X
   int xdep = (int)cm[0];
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     for (int j = 0; j < MR; ++j) {
       uint32_t v = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v = pmax16(v, xv[j][e] & keep16[e]);
+      for (int e = 0; e < 4; ++e) v = pmax16(v, mag16(xv[j][e]) & keep16[e]);
       rm[j] = (v & 0xffffu) > (v >> 16) ? (v & 0xffffu) : (v >> 16);
     }
     const uint32_t r = wave_rows_max<MR>(rm, lane);

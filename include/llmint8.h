@@ -33,8 +33,10 @@
  *   - Arguments are validated before any HIP call is made. A failed check
  *     enqueues nothing and leaves every output untouched. Device faults surface
  *     at the caller's next synchronization.
- *   - Inputs must be finite (an infinite entry makes its column an outlier; NaN
- *     inputs give unspecified results).
+ *   - Inputs are meant to be finite. An infinite entry of X makes its column an
+ *     outlier. A NaN entry of X is never an outlier and never sets a row
+ *     absmax, on every path; its own code, and so the row of C and Y it lies
+ *     in, are unspecified. Other rows are unaffected.
  */
 #ifndef LLMINT8_H_
 #define LLMINT8_H_

@@ -39,6 +39,8 @@
  *   - outlier test is |x| >= threshold (inclusive); a column is an outlier when
  *     any of its entries passes it;
  *   - the row absmax of X excludes outlier columns; outlier columns of Xq are 0;
+ *   - a NaN entry never passes the threshold test and never sets an absmax
+ *     (every comparison with NaN is false); its int8 code is 0;
  *   - the column absmax of W runs over all K rows (W is quantized once, at load);
  *   - the scale is applied as x * fl32(127 / absmax): one IEEE fp32 division,
  *     one fp32 multiply, round-half-to-even, clamp to [-127, 127], cast;
@@ -84,10 +86,14 @@ void ora_half_to_float(const uint16_t *h, int64_t n, float *out)
 }
 
 /* The symmetric absmax quantizer of [P5] section 1 with the round/clamp/cast
- * order of [P3] section 3.2: q = clamp(round_half_even(x * inv), -127, 127). */
+ * order of [P3] section 3.2: q = clamp(round_half_even(x * inv), -127, 127).
+ * A NaN entry (the pages do not say; inputs are meant to be finite) codes as 0
+ * here, so that the cast below is always defined. */
 static int8_t ora_quant(float x, float inv)
 {
     float v = x * inv;
+    if (isnan(v))
+        return 0;
     float r = rintf(v);                 /* default mode: round half to even */
     if (r > 127.0f)
         r = 127.0f;

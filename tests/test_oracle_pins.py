@@ -144,6 +144,24 @@ def test_outliers_match_brute_force_and_plants():
     assert idx.tolist() == brute == list(wl.fixed_cols)
 
 
+def test_nan_entries_are_never_outliers_and_never_set_a_row_scale():
+    # the reading taken for non-finite inputs: every comparison with NaN is
+    # false, so a NaN passes no threshold and no absmax; +-inf passes both
+    X = f16([[1.0, np.nan, -2.0, 0.5], [np.nan, 3.0, 0.25, -np.inf], [0.5, 0.5, 8.0, 0.0]])
+    assert oracle.find_outliers(X, 6.0).tolist() == [2, 3]
+    assert oracle.find_outliers(X, 0.0).tolist() == [0, 1, 2, 3]
+    idx = oracle.find_outliers(X, 6.0)
+    Xq, m = oracle.quantize_rowwise(X, idx)
+    assert m.tolist() == [1.0, 3.0, 0.5]
+    assert Xq[0].tolist() == [127, 0, 0, 0]   # NaN codes as 0, column 2 is an outlier
+    assert Xq[1].tolist() == [0, 127, 0, 0]
+    # the columns without NaN give the same codes as the same rows without it
+    Xc = X.copy()
+    Xc[0, 1] = Xc[1, 0] = 0
+    Xq2, m2 = oracle.quantize_rowwise(Xc, idx)
+    assert np.array_equal(Xq2, Xq) and np.array_equal(m2, m)
+
+
 def test_outlier_set_shrinks_as_threshold_grows():
     X, _, _ = workloads.random_case(40, 256, 4, seed=3, n_out=5)
     prev = None
