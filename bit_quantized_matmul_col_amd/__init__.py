@@ -122,6 +122,32 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
         raise ValueError(f"{name} must have {ndim} dimensions")
 
 
+def _need_shape(t: torch.Tensor, name: str, shape: tuple, contiguous: bool = False):
+    """Reject a buffer whose shape differs from the one the kernels write (or
+    read) with the pitches the call passes: they would run past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_vec(t: torch.Tensor, name: str, dtype, n: int, exact: bool = True):
+    """A contiguous vector of n elements (at least n when exact is False)."""
+    _need(t, name, dtype)
+    if not t.is_contiguous() or (t.numel() != n if exact else t.numel() < n):
+        raise ValueError(f"{name} must be a contiguous vector of {'' if exact else 'at least '}"
+                         f"{n} elements, got {tuple(t.shape)}")
+
+
+def _ws(workspace: torch.Tensor):
+    """(pointer, size in bytes) of a caller-supplied device workspace."""
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def _ld(t: torch.Tensor, name: str) -> int:
     if t.stride(1) != 1 and t.shape[1] > 1:
         raise ValueError(f"{name} must have unit stride along its last dimension")
@@ -154,7 +180,7 @@ def llmint8_find_outliers(X: torch.Tensor, threshold: float = 6.0, workspace=Non
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
     _check(lib().llmint8_find_outliers(_ptr(X), M, K, _ld(X, "X"), float(threshold), _ptr(idx),
-                                       _ptr(count), _ptr(workspace), workspace.numel(),
+                                       _ptr(count), *_ws(workspace),
                                        _stream(X)))
     return idx, count
 
@@ -165,10 +191,10 @@ def llmint8_quantize_rowwise(X: torch.Tensor, idx: torch.Tensor | None = None,
     _need(X, "X", torch.float16, 2)
     if (idx is None) != (count is None):
         raise ValueError("idx and count go together")
-    if idx is not None:
-        _need(idx, "idx", torch.int32, 1)
-        _need(count, "count", torch.int32, 1)
     M, K = X.shape
+    if idx is not None:
+        _need_vec(idx, "idx", torch.int32, 1, exact=False)
+        _need_vec(count, "count", torch.int32, 1, exact=False)
     Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
     m = torch.empty((M,), dtype=torch.float32, device=X.device)
     _check(lib().llmint8_quantize_rowwise(_ptr(X), M, K, _ld(X, "X"), _ptr(idx), _ptr(count),
@@ -197,11 +223,11 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
     absmax and decides the outlier columns without a scan of X."""
     _need(X, "X", torch.float16, 2)
     _need(Wq, "Wq", torch.int8, 2)
-    _need(col_absmax, "col_absmax", torch.float32, 1)
     M, K = X.shape
     N = Wq.shape[0]
     if Wq.shape[1] != K or not Wq.is_contiguous():
         raise ValueError("Wq must be contiguous [N, K]")
+    _need_vec(col_absmax, "col_absmax", torch.float32, N)
     if outlier_weights not in ("fp16", "int8"):
         raise ValueError("outlier_weights is 'fp16' or 'int8'")
     if W is not None:
@@ -213,9 +239,12 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, "Y", torch.float16, 2)
-    for name, t in (("outlier_count", outlier_count), ("C_debug", C_debug)):
-        if t is not None:
-            _need(t, name, torch.int32)
+    _need_shape(Y, "Y", (M, N))
+    if outlier_count is not None:
+        _need_vec(outlier_count, "outlier_count", torch.int32, 1, exact=False)
+    if C_debug is not None:
+        _need(C_debug, "C_debug", torch.int32)
+        _need_shape(C_debug, "C_debug", (M, N), contiguous=True)
     for name, t, dt, n in (("bias", bias, torch.float16, N),
                            ("y_col_absmax", y_col_absmax, torch.float32, N),
                            ("x_col_absmax", x_col_absmax, torch.float32, K)):
@@ -239,7 +268,7 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
         opts = o
     args = (_ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
             _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
-            _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X))
+            _ptr(outlier_count), _ptr(C_debug), *_ws(workspace), _stream(X))
     if opts is None:
         _check(lib().llmint8_linear(*args))
     else:
@@ -261,7 +290,7 @@ def llmint8_quantize_tensorwise(W: torch.Tensor, workspace=None):
         workspace = torch.empty((max(llmint8_quantize_tensorwise_workspace_size(K, N), 1),),
                                 dtype=torch.uint8, device=W.device)
     _check(lib().llmint8_quantize_tensorwise(_ptr(W), K, N, _ld(W, "W"), _ptr(Wq), _ptr(sw),
-                                             _ptr(workspace), workspace.numel(), _stream(W)))
+                                             *_ws(workspace), _stream(W)))
     return Wq, sw
 
 
@@ -277,27 +306,28 @@ def llmint8_linear_tensorwise(X: torch.Tensor, Wq: torch.Tensor, w_absmax: torch
     from llmint8_quantize_tensorwise -> fp16 Y [M, N] (no outlier decomposition)."""
     _need(X, "X", torch.float16, 2)
     _need(Wq, "Wq", torch.int8, 2)
-    _need(w_absmax, "w_absmax", torch.float32, 1)
+    _need_vec(w_absmax, "w_absmax", torch.float32, 1, exact=False)
     M, K = X.shape
     N = Wq.shape[0]
     if Wq.shape[1] != K or not Wq.is_contiguous():
         raise ValueError("Wq must be contiguous [N, K]")
     if bias is not None:
-        _need(bias, "bias", torch.float16, 1)
-        if bias.numel() != N or not bias.is_contiguous():
-            raise ValueError(f"bias must be a contiguous vector of {N}")
-    for name, t in (("x_absmax", x_absmax), ("C_debug", C_debug)):
-        if t is not None:
-            _need(t, name, torch.float32 if name == "x_absmax" else torch.int32)
+        _need_vec(bias, "bias", torch.float16, N)
+    if x_absmax is not None:
+        _need_vec(x_absmax, "x_absmax", torch.float32, 1, exact=False)
+    if C_debug is not None:
+        _need(C_debug, "C_debug", torch.int32)
+        _need_shape(C_debug, "C_debug", (M, N), contiguous=True)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, "Y", torch.float16, 2)
+    _need_shape(Y, "Y", (M, N))
     if workspace is None:
         workspace = torch.empty((llmint8_linear_tensorwise_workspace_size(M, K, N),),
                                 dtype=torch.uint8, device=X.device)
     _check(lib().llmint8_linear_tensorwise(
         _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(w_absmax), N, _ptr(bias), _ptr(Y),
-        _ld(Y, "Y"), _ptr(x_absmax), _ptr(C_debug), _ptr(workspace), workspace.numel(),
+        _ld(Y, "Y"), _ptr(x_absmax), _ptr(C_debug), *_ws(workspace),
         _stream(X)))
     return Y
 
@@ -321,10 +351,10 @@ def llmint8_quantize_rowwise_fp8(X: torch.Tensor, idx: torch.Tensor | None = Non
     _need(X, "X", torch.float16, 2)
     if (idx is None) != (count is None):
         raise ValueError("idx and count go together")
-    if idx is not None:
-        _need(idx, "idx", torch.int32, 1)
-        _need(count, "count", torch.int32, 1)
     M, K = X.shape
+    if idx is not None:
+        _need_vec(idx, "idx", torch.int32, 1, exact=False)
+        _need_vec(count, "count", torch.int32, 1, exact=False)
     Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
     m = torch.empty((M,), dtype=torch.float32, device=X.device)
     _check(lib().llmint8_quantize_rowwise_fp8(_ptr(X), M, K, _ld(X, "X"), _ptr(idx), _ptr(count),
@@ -348,11 +378,11 @@ def llmint8_linear_fp8(X: torch.Tensor, Wq8: torch.Tensor, col_absmax: torch.Ten
     C_debug, if given, is an fp32 [M, N] tensor receiving the 8-bit product."""
     _need(X, "X", torch.float16, 2)
     _need(Wq8, "Wq8", torch.uint8, 2)
-    _need(col_absmax, "col_absmax", torch.float32, 1)
     M, K = X.shape
     N = Wq8.shape[0]
     if Wq8.shape[1] != K or not Wq8.is_contiguous():
         raise ValueError("Wq8 must be contiguous [N, K]")
+    _need_vec(col_absmax, "col_absmax", torch.float32, N)
     if W is not None:
         _need(W, "W", torch.float16, 2)
         if tuple(W.shape) != (K, N):
@@ -362,10 +392,12 @@ def llmint8_linear_fp8(X: torch.Tensor, Wq8: torch.Tensor, col_absmax: torch.Ten
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, "Y", torch.float16, 2)
+    _need_shape(Y, "Y", (M, N))
     if outlier_count is not None:
-        _need(outlier_count, "outlier_count", torch.int32)
+        _need_vec(outlier_count, "outlier_count", torch.int32, 1, exact=False)
     if C_debug is not None:
         _need(C_debug, "C_debug", torch.float32)
+        _need_shape(C_debug, "C_debug", (M, N), contiguous=True)
     for name, t, dt, n in (("bias", bias, torch.float16, N),
                            ("y_col_absmax", y_col_absmax, torch.float32, N),
                            ("x_col_absmax", x_col_absmax, torch.float32, K)):
@@ -385,6 +417,6 @@ def llmint8_linear_fp8(X: torch.Tensor, Wq8: torch.Tensor, col_absmax: torch.Ten
     _check(lib().llmint8_linear_fp8(
         _ptr(X), M, K, _ld(X, "X"), _ptr(Wq8), _ptr(col_absmax), _ptr(W),
         _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
-        _ptr(outlier_count), _ptr(C_debug), _ptr(workspace), workspace.numel(), _stream(X),
+        _ptr(outlier_count), _ptr(C_debug), *_ws(workspace), _stream(X),
         C.byref(o)))
     return Y
