@@ -16,7 +16,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "llmint8.h")
 LIB = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "libllmint8.so")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="HIP library not built")
+
+
+@pytest.fixture(autouse=True)
+def _library(built_library):
+    return built_library
 
 
 def declared_functions():

@@ -9,7 +9,11 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 RES = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "libllmint8.kernels.json")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(RES), reason="HIP library not built")
+
+
+@pytest.fixture(autouse=True)
+def _library(built_library):
+    return built_library
 
 
 def test_every_kernel_reported():
