@@ -6,14 +6,19 @@ X, K-compaction when the outlier share calls for it, the int8 GEMM with its
 fused fp16 outlier product, dequantization and merge. Weights are quantized
 once before timing (the method quantizes them at load), and that pass is
 reported on its own. Inputs are resident in HBM when the timed region starts.
-To keep the 256 MB Infinity Cache from serving the weights, consecutive steps
-cycle through distinct copies of the weight set (and of the activation).
+To keep the 256 MB Infinity Cache from serving the weights of the decode-sized
+workloads, consecutive steps cycle through distinct copies of the weight set
+(and of the activation).
 
-The timed region replays a HIP graph that holds one call per weight set and
-activation of that rotation, so the step rate is the GPU's, not that of the
-Python launch loop (the eager rate is reported beside it). The GEMM kernel's
-duration comes from event pairs that the kernel's own dispatch stamps, one pair
-per call, over a run of eager calls.
+The timed region replays HIP graphs holding exactly --steps layer calls, so
+the step rate is the GPU's, not that of the Python launch loop (the eager rate
+and a sustained rate over at least 1000 calls are reported beside it). The
+GEMM kernel's duration comes from event pairs that the kernel's own dispatch
+stamps, one pair per call, over a run of eager calls.
+
+By default the line also carries, for the prefill, 13b and 70b workloads (70b
+at thresholds 6, 4 and inf), the step time, TOPS, the GEMM kernel's time and
+roofline fraction, and the standalone bandwidth of the three quantize passes.
 
 Prints one JSON line. `value` is the whole-step rate in the workload's unit:
 GB/s of algorithmic bytes for the HBM-bound decode and tiny shapes, TOPS of
@@ -27,6 +32,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -44,10 +50,12 @@ METRIC = "LLM.int8() linear TOPS & GB/s at 7B/13B shapes; % of int8 MFMA / HBM p
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 FP16_PEAK_TFLOPS = 2500.0
+# dense int8 MFMA ops per CU per clock on gfx950: the 5.0 POPS figure is
+# 256 CUs x 2.4 GHz x 8192
+INT8_OPS_PER_CU_CLOCK = 8192
 HBM_BOUND = ("tiny", "decode")
 DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
 PROFILES = os.path.join(ROOT, "profiles")
-# the sources that define the GEMM kernels (small-M and large-M)
 # Sources of the GEMM kernels whose HBM counters are committed: the split-K
 # small-M kernels (up to 64 rows; the single-kernel path runs none of the
 # workloads with counters) and the large-M ones, digested separately so that a
@@ -59,6 +67,8 @@ KERNEL_SOURCES = {
                 ("common.hpp", "internal.hpp", "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")],
 }
 SMALL_M_MAX = 64  # rows up to which the layer runs the small-M kernels
+# the larger workloads measured by default next to the headline one
+SWEEP = (("prefill", (6.0,)), ("13b", (6.0,)), ("70b", (6.0, 4.0, math.inf)))
 
 
 def _code_only(text: str) -> str:
@@ -113,16 +123,17 @@ def uses_compaction(M, K, n_out, any_m=False):
 
 def step_work(M, K, N, n_out, compacted, int8w=False, large_m=False):
     """Algorithmic bytes and work of one layer call, and the algorithmic bytes of
-    its GEMM kernel. The small-M GEMM kernel quantizes fp16 X itself and writes
-    int32 sums, so its minimum traffic is Wq + X + C; the large-M kernel reads
-    Xq, Wq (or their compacted copies), the scales and the outlier operands and
-    writes Y. With int8 outlier weights the outlier rows come out of Wq, which
-    the call reads anyway, so the fp16 rows drop out of the call's bytes."""
+    its GEMM kernel. The small-M GEMM kernel must read Wq and the fp16 X (its
+    int32 split sums are the kernel's own intermediate, not algorithmic);
+    the large-M kernel reads Xq, Wq (or their compacted copies), the scales
+    and the outlier operands and writes Y. With int8 outlier weights the
+    outlier rows come out of Wq, which the call reads anyway, so the fp16 rows
+    drop out of the call's bytes."""
     k_int8 = K - n_out
     w_o = 0 if int8w else 2 * n_out * N
     call_bytes = 2 * M * K + K * N + 4 * N + w_o + 2 * M * N
     if M <= DECODE_MAX_M and not large_m:
-        gemm_bytes = N * K + 2 * M * K + 4 * M * N
+        gemm_bytes = N * K + 2 * M * K
     else:
         k_loop = k_int8 if compacted else K
         gemm_bytes = (N * k_loop + 4 * N + M * k_loop + 4 * M + 2 * M * n_out
@@ -130,6 +141,185 @@ def step_work(M, K, N, n_out, compacted, int8w=False, large_m=False):
     int8_ops = 2 * M * N * k_int8
     fp16_flops = 2 * M * N * n_out
     return call_bytes, gemm_bytes, int8_ops, fp16_flops
+
+
+def pass_bytes(M, K, N):
+    """Algorithmic bytes of the three quantize passes: each tensor read or
+    written once (find_outliers reads X; quantize_rowwise reads X, writes Xq
+    and m; quantize_colwise reads W, writes Wq and s)."""
+    return {"find_outliers": 2 * M * K, "quantize_rowwise": 3 * M * K + 4 * M,
+            "quantize_colwise": 3 * K * N + 4 * N}
+
+
+def host_facts():
+    """CPU model and thread counts of the host the benchmark runs on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
+def device_facts(torch, dev):
+    """The GPU as the runtime reports it, and the int8 MFMA peak derived from
+    its compute-unit count and the peak engine clock rocminfo lists."""
+    p = torch.cuda.get_device_properties(dev)
+    facts = {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+             "compute_units": p.multi_processor_count,
+             "hbm_bytes": int(p.total_memory)}
+    mhz = None
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        arch = facts["arch"].split(":")[0]
+        for block in out.split("*******"):
+            if arch and arch in block and "Compute Unit" in block:
+                m = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", block)
+                if m:
+                    mhz = int(m.group(1))
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    facts["max_clock_mhz"] = mhz
+    if mhz:
+        facts["int8_peak_derived_tops"] = round(
+            facts["compute_units"] * mhz * 1e6 * INT8_OPS_PER_CU_CLOCK / 1e12, 1)
+    return facts
+
+
+def copy_ceiling(torch, dev, mib=1024, reps=10):
+    """Plain device-to-device copy of a buffer far larger than the caches:
+    bytes read + bytes written per second, the practical HBM ceiling for a
+    stream that reads and writes once."""
+    n = mib << 20
+    a = torch.empty((n,), dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"what": f"device copy of {mib} MiB, read + write bytes", "ms": round(ms, 4),
+            "GB_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+def graph_time(torch, calls, steps, warmup_replays=1):
+    """Time exactly `steps` calls of `calls(i)` (i = 0 .. steps-1) replayed from
+    HIP graphs: one graph of min(steps, 1024) calls replayed, plus one graph of
+    the remainder. Returns (ms per call, description)."""
+    glen = min(steps, 1024)
+    reps, tail = divmod(steps, glen)
+
+    def capture(n, offset):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # allocations and lazy setup outside the capture
+            for i in range(n):
+                calls(offset + i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                calls(offset + i)
+        return g
+
+    g = capture(glen, 0)
+    gt = capture(tail, reps * glen) if tail else None
+    for _ in range(warmup_replays):
+        g.replay()
+        if gt is not None:
+            gt.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    if gt is not None:
+        gt.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    desc = f"{reps} replay(s) of a HIP graph of {glen} layer calls"
+    if tail:
+        desc += f" + 1 replay of a graph of {tail}"
+    del g, gt
+    return ms, desc
+
+
+def gemm_event_ms(torch, lm, step, n, eager_ms):
+    """Average GEMM kernel duration from event pairs its own dispatch stamps,
+    over n eager calls queued behind a spin kernel so that they run back to
+    back as in the timed region (an idle GPU between calls stretches each
+    kernel's events)."""
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev_b + ev_e:
+        e.record()  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    spin_ms = 1.5 * eager_ms * n + 1.0
+    torch.cuda._sleep(int(spin_ms * 1e-3 * 2.4e9))
+    for i in range(n):
+        step(i, lm.LinearOpts(gemm_begin_event=ev_b[i].cuda_event,
+                              gemm_end_event=ev_e[i].cuda_event))
+    torch.cuda.synchronize()
+    return sum(ev_b[i].elapsed_time(ev_e[i]) for i in range(n)) / n
+
+
+def eager_ms(torch, step, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def quantize_passes(torch, lm, Xs, Ws, threshold, calls=20):
+    """Standalone time and algorithmic bandwidth of the three public quantize
+    passes, each replayed from a HIP graph of `calls` calls cycling through the
+    given activations (weights), against the 8 TB/s peak."""
+    M, K = Xs[0].shape
+    N = Ws[0].shape[1]
+    nb = pass_bytes(M, K, N)
+    dev = Xs[0].device
+    ws = torch.empty((max(lm.llmint8_find_outliers_workspace_size(M, K), 1),),
+                     dtype=torch.uint8, device=dev)
+    found = [lm.llmint8_find_outliers(X, threshold, workspace=ws) for X in Xs]
+    torch.cuda.synchronize()
+    runs = {
+        "find_outliers": lambda i: lm.llmint8_find_outliers(Xs[i % len(Xs)], threshold,
+                                                            workspace=ws),
+        "quantize_rowwise": lambda i: lm.llmint8_quantize_rowwise(Xs[i % len(Xs)],
+                                                                  *found[i % len(Xs)]),
+        "quantize_colwise": lambda i: lm.llmint8_quantize_colwise(Ws[i % len(Ws)]),
+    }
+    out = {}
+    for name, fn in runs.items():
+        n = calls if name != "quantize_colwise" else max(2, min(calls, 8))
+        ms, _ = graph_time(torch, fn, n)
+        gbs = nb[name] / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "algorithmic_bytes": nb[name],
+                     "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        torch.cuda.empty_cache()
+    return out
 
 
 def accuracy(torch, lm, X_host, W_host, Xd, Wd, threshold, n_rows=16):
@@ -168,69 +358,175 @@ def accuracy(torch, lm, X_host, W_host, Xd, Wd, threshold, n_rows=16):
     return out
 
 
-def vendor_int8_gemm(torch, M, K, N, dev, reps=20):
-    """Reference point, not part of the layer: the plain int8 GEMM of the same
-    shape (Xq . Wq^T over all of K, int32 out, no outlier product, no
-    dequantization) through torch._int_mm, which ROCm runs on hipBLASLt."""
-    a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
-    b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev)
-    try:
-        for _ in range(3):
-            torch._int_mm(a, b.t())
-    except Exception as e:  # not every shape is supported by the library
-        return {"library": "torch._int_mm (hipBLASLt)", "error": repr(e)[:120]}
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        torch._int_mm(a, b.t())
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    tops = 2 * M * N * K / (ms * 1e-3) / 1e12
-    return {"library": "torch._int_mm (hipBLASLt)", "work": "2MNK int8 ops, int32 out",
-            "ms": round(ms, 6), "TOPS": round(tops, 2),
-            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-
-
 def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8=False):
-    """The oracle as it stands, single-threaded, on a bounded sample. Its weight
-    quantization (load time, like the GPU's) is done first and not timed."""
+    """The oracle as it stands, single-threaded, on a bounded sample, with each
+    step timed on its own: weight quantization (a0, load time), the outlier
+    scan (a1), row quantization (a2) and the int8 product with the merge
+    (a3-a5). The headline figure is the whole call's rate."""
     import numpy as np
     import oracle
 
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    rows = wl.M if hbm_bound else 4
+    Wsub = W if hbm_bound else W[:, :min(W.shape[1], 2048)]
     if fp8:
-        Wq8, s8 = oracle.quantize_colwise_fp8(W)
-
-        def layer(rows):
-            return oracle.linear_fp8(X, W, threshold, Wq8=Wq8, s=s8, rows=rows)
+        (Wq, s), t_a0 = timed(lambda: oracle.quantize_colwise_fp8(Wsub))
+        if Wsub is not W:
+            Wq, s = oracle.quantize_colwise_fp8(W)
     else:
-        Wq, s = oracle.quantize_colwise(W)
-
-        def layer(rows):
-            return oracle.linear_rows(X, W, threshold, rows, Wq=Wq, s=s)
-    rows = wl.M
-    if not hbm_bound:
-        rows = 4
-    sample_rows = np.arange(rows)
+        (Wq, s), t_a0 = timed(lambda: oracle.quantize_colwise(Wsub))
+        if Wsub is not W:
+            Wq, s = oracle.quantize_colwise(W)
+    Xs = np.ascontiguousarray(X[:rows])
+    steps = {"a1_find_outliers": [], "a2_quantize_rowwise": [], "a3_a5_gemm_and_merge": []}
     reps, elapsed = 0, 0.0
     while reps == 0 or (elapsed < budget_s and reps < 50):
-        t0 = time.perf_counter()
-        layer(sample_rows)
-        elapsed += time.perf_counter() - t0
+        idx, t1 = timed(lambda: oracle.find_outliers(X, threshold))
+        if fp8:
+            (Xq, m), t2 = timed(lambda: oracle.quantize_rowwise_fp8(Xs, idx))
+            _, t3 = timed(lambda: oracle.merge_fp8(oracle.gemm_fp8(Xq, Wq), m, s, Xs, W, idx))
+        else:
+            (Xq, m), t2 = timed(lambda: oracle.quantize_rowwise(Xs, idx))
+            _, t3 = timed(lambda: oracle.merge(oracle.gemm_i8(Xq, Wq), m, s, Xs, W, idx))
+        for k, t in zip(steps, (t1, t2, t3)):
+            steps[k].append(t)
+        elapsed += t1 + t2 + t3
         reps += 1
-    per = elapsed / reps
+    med = {k: sorted(v)[len(v) // 2] for k, v in steps.items()}
+    nb = pass_bytes(wl.M, wl.K, Wsub.shape[1])
+    per_step = {
+        "a0_quantize_colwise": {"s": round(t_a0, 4), "GB_per_s": round(
+            nb["quantize_colwise"] / t_a0 / 1e9, 4), "sample": f"W [{wl.K} x {Wsub.shape[1]}]"},
+        "a1_find_outliers": {"s": round(med["a1_find_outliers"], 5), "GB_per_s": round(
+            nb["find_outliers"] / med["a1_find_outliers"] / 1e9, 4)},
+        "a2_quantize_rowwise": {"s": round(med["a2_quantize_rowwise"], 5), "GB_per_s": round(
+            pass_bytes(rows, wl.K, 1)["quantize_rowwise"] / med["a2_quantize_rowwise"] / 1e9, 4),
+            "rows": rows},
+        "a3_a5_gemm_and_merge": {"s": round(med["a3_a5_gemm_and_merge"], 5), "TOPS": round(
+            2 * rows * wl.N * wl.K / med["a3_a5_gemm_and_merge"] / 1e12, 6), "rows": rows},
+    }
+    per_call = med["a1_find_outliers"] + med["a2_quantize_rowwise"] + med["a3_a5_gemm_and_merge"]
     if hbm_bound:
         call_bytes = step_work(wl.M, wl.K, wl.N, n_out, False, large_m=fp8)[0]
-        value, unit = call_bytes / per / 1e9, "GB/s"
-        sample = f"{reps} whole layer calls on the {wl.M}x{wl.K}x{wl.N} workload"
+        value, unit = call_bytes / per_call / 1e9, "GB/s"
+        sample = (f"{reps} whole layer calls on the {wl.M}x{wl.K}x{wl.N} workload "
+                  f"(median per step)")
     else:
         work = 2 * rows * wl.N * wl.K
-        value, unit = work / per / 1e12, "TOPS"
+        value, unit = work / per_call / 1e12, "TOPS"
         sample = (f"outlier scan over all {wl.M} rows + rows 0..{rows - 1} of the "
-                  f"{wl.M}x{wl.K}x{wl.N} workload, {reps} repetitions")
+                  f"{wl.M}x{wl.K}x{wl.N} workload, {reps} repetitions (median per step)")
+    facts = host_facts()
     return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 2)}
+            "sample": sample, "seconds": round(elapsed + t_a0, 2), "per_step": per_step,
+            "threads_used": 1, "cpu_model": facts["cpu_model"], "nproc": facts["nproc"]}
+
+
+class Layer:
+    """Device inputs of one workload and one call of the layer on them."""
+
+    def __init__(self, torch, lm, wl, threshold, dev, variant="int8", outlier_weights="fp16",
+                 rotate_weights=True, x_pool=4):
+        import workloads
+        self.torch, self.lm, self.wl, self.threshold = torch, lm, wl, threshold
+        self.fp8 = variant == "fp8"
+        self.int8w = outlier_weights == "int8"
+        self.outlier_weights = outlier_weights
+        self.W_host = workloads.make_w(wl)
+        W0 = torch.from_numpy(self.W_host).to(dev)
+        self.X_host = ([workloads.make_x(wl, c) for c in range(x_pool)] if wl.per_call
+                       else [workloads.make_x(wl)])
+        self.Xs = [torch.from_numpy(self.X_host[c % len(self.X_host)]).to(dev)
+                   for c in range(x_pool)]
+        quantize = lm.llmint8_quantize_colwise_fp8 if self.fp8 else lm.llmint8_quantize_colwise
+        Wq0, s0 = quantize(W0)
+        self.W0 = W0
+        self.n_sets = max(2, min(32, math.ceil(600e6 / (wl.N * wl.K)))) if rotate_weights else 1
+        self.sets = [(Wq0, s0, None if self.int8w else W0)] + [
+            (Wq0.clone(), s0.clone(), None if self.int8w else W0.clone())
+            for _ in range(self.n_sets - 1)]
+        self.Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+        ws_size = (lm.llmint8_linear_fp8_workspace_size if self.fp8
+                   else lm.llmint8_workspace_size)
+        self.ws = torch.empty((ws_size(wl.M, wl.K, wl.N),), dtype=torch.uint8, device=dev)
+        self.cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i, opts=None):
+        Wq, s, W = self.sets[i % self.n_sets]
+        X = self.Xs[i % len(self.Xs)]
+        if self.fp8:
+            self.lm.llmint8_linear_fp8(X, Wq, s, W, self.threshold, Y=self.Y, workspace=self.ws,
+                                       outlier_count=self.cnt, opts=opts)
+        else:
+            self.lm.llmint8_linear(X, Wq, s, W, self.threshold, Y=self.Y, workspace=self.ws,
+                                   outlier_count=self.cnt, opts=opts,
+                                   outlier_weights=self.outlier_weights)
+
+    def work(self):
+        wl = self.wl
+        n_out = int(self.cnt.item())
+        compacted = uses_compaction(wl.M, wl.K, n_out, any_m=self.fp8)
+        return (n_out, compacted) + step_work(wl.M, wl.K, wl.N, n_out, compacted, self.int8w,
+                                              large_m=self.fp8)
+
+
+def rooflines(hbm_bound, ms_per_step, gemm_ms, call_bytes, gemm_bytes, int8_ops, fp16_flops):
+    """The dominant kernel's roofline (the GEMM: HBM for small M, int8 MFMA for
+    large M; fp16 flops weigh double against the int8 peak) and the whole
+    call's: algorithmic bytes over the step time against 8 TB/s, or the ideal
+    time int8_ops / 5 POPS + fp16_flops / 2.5 PFLOPS over the step time."""
+    if hbm_bound:
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        kern = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        call_gbs = call_bytes / (ms_per_step * 1e-3) / 1e9
+        call = {"bound": "hbm", "achieved": round(call_gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(call_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = (int8_ops + 2 * fp16_flops) / (gemm_ms * 1e-3) / 1e12
+        kern = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+        t_ideal_ms = (int8_ops / (INT8_PEAK_TOPS * 1e12) + fp16_flops / (FP16_PEAK_TFLOPS * 1e12)) * 1e3
+        call = {"bound": "mfma", "ideal_ms": round(t_ideal_ms, 5),
+                "frac": round(t_ideal_ms / ms_per_step, 4)}
+    return kern, call
+
+
+def sweep_workload(torch, lm, name, thresholds, dev, steps=10):
+    """One larger workload at each of its thresholds: graph-timed steps, the
+    GEMM kernel's event time, rooflines and the standalone quantize passes."""
+    import workloads
+    wl = workloads.WORKLOADS[name]
+    L = Layer(torch, lm, wl, thresholds[0], dev, rotate_weights=False,
+              x_pool=2 if wl.per_call else 1)
+    outs = []
+    for threshold in thresholds:
+        print(f"# measuring {name} at threshold {threshold}", file=sys.stderr, flush=True)
+        L.threshold = threshold
+        for i in range(3):
+            L.step(i)
+        torch.cuda.synchronize()
+        ms, _ = graph_time(torch, L.step, steps)
+        e_ms = eager_ms(torch, L.step, steps)
+        g_ms = gemm_event_ms(torch, lm, L.step, steps, e_ms)
+        n_out, compacted, call_bytes, gemm_bytes, int8_ops, fp16_flops = L.work()
+        kern, call = rooflines(False, ms, g_ms, call_bytes, gemm_bytes, int8_ops, fp16_flops)
+        passes = quantize_passes(torch, lm, L.Xs, [L.W0], threshold, calls=10)
+        outs.append({"workload": wl.description, "M": wl.M, "K": wl.K, "N": wl.N,
+                     "threshold": threshold, "outlier_columns": n_out,
+                     "k_compacted": compacted, "steps": steps, "ms_per_step": round(ms, 5),
+                     "TOPS": round((int8_ops + fp16_flops) / (ms * 1e-3) / 1e12, 2),
+                     "gemm_kernel_ms": round(g_ms, 5), "roofline": kern, "call_roofline": call,
+                     "quantize_passes": passes})
+        torch.cuda.empty_cache()
+    del L
+    torch.cuda.empty_cache()
+    return outs
 
 
 def main():
@@ -246,6 +542,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true",
                     help="skip the output-error comparison of the layer's variants")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the prefill, 13b and 70b measurements next to the headline")
     ap.add_argument("--variant", default="int8", choices=("int8", "fp8"),
                     help="int8: the LLM.int8() layer; fp8: its E4M3 variant")
     ap.add_argument("--outlier-weights", default="fp16", choices=("fp16", "int8"),
@@ -261,7 +559,6 @@ def main():
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import bit_quantized_matmul_col_amd as lm
@@ -270,117 +567,30 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     threshold = wl.threshold if args.threshold is None else args.threshold
     hbm_bound = args.workload in HBM_BOUND
-    steps = args.steps if args.steps is not None else (2000 if hbm_bound else 100)
+    steps = args.steps if args.steps is not None else (1000 if hbm_bound else 20)
     warmup = args.warmup if args.warmup is not None else max(10, steps // 10)
+    if steps < 1 or warmup < 0:
+        sys.exit("--steps must be at least 1 and --warmup at least 0")
     dev = torch.device("cuda:0")
-
-    # inputs: weight sets and activations, resident before timing
-    W_host = workloads.make_w(wl)
-    W0 = torch.from_numpy(W_host).to(dev)
-    wq_bytes = wl.N * wl.K
-    n_sets = max(2, min(32, math.ceil(600e6 / wq_bytes)))
-    x_pool = 4
-    X_host = [workloads.make_x(wl, c) for c in range(x_pool)] if wl.per_call else \
-        [workloads.make_x(wl)]
-    Xs = [torch.from_numpy(X_host[c % len(X_host)]).to(dev) for c in range(x_pool)]
-
     fp8 = args.variant == "fp8"
     if fp8 and args.outlier_weights != "fp16":
         sys.exit("the FP8 layer takes its outlier rows from the fp16 weight")
-    quantize = lm.llmint8_quantize_colwise_fp8 if fp8 else lm.llmint8_quantize_colwise
-    # load-time weight quantization, timed on its own
-    Wq0, s0 = quantize(W0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 5
-    e0.record()
-    for _ in range(reps):
-        quantize(W0)
-    e1.record()
-    torch.cuda.synchronize()
-    colwise_ms = e0.elapsed_time(e1) / reps
-    colwise_bytes = 3 * wl.K * wl.N + 4 * wl.N
 
-    int8w = args.outlier_weights == "int8"
-    sets = [(Wq0, s0, None if int8w else W0)] + [
-        (Wq0.clone(), s0.clone(), None if int8w else W0.clone()) for _ in range(n_sets - 1)]
-    Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
-    ws_size = (lm.llmint8_linear_fp8_workspace_size if fp8 else lm.llmint8_workspace_size)
-    ws = torch.empty((ws_size(wl.M, wl.K, wl.N),), dtype=torch.uint8, device=dev)
-    cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
-
-    def step(i, opts=None):
-        Wq, s, W = sets[i % n_sets]
-        if fp8:
-            lm.llmint8_linear_fp8(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
-                                  outlier_count=cnt, opts=opts)
-        else:
-            lm.llmint8_linear(Xs[i % x_pool], Wq, s, W, threshold, Y=Y, workspace=ws,
-                              outlier_count=cnt, opts=opts, outlier_weights=args.outlier_weights)
-
+    L = Layer(torch, lm, wl, threshold, dev, variant=args.variant,
+              outlier_weights=args.outlier_weights, rotate_weights=True)
     for i in range(warmup):
-        step(i)
+        L.step(i)
     torch.cuda.synchronize()
 
-    # Timed region: replays of a HIP graph holding graph_len consecutive layer
-    # calls (every weight set and activation of the rotation), so the rate is the
-    # GPU's and not the Python launch loop's.
-    graph_len = n_sets * x_pool // math.gcd(n_sets, x_pool)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(graph_len):
-            step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(graph_len):
-            step(i)
-    replays = max(1, math.ceil(steps / graph_len))
-    steps = replays * graph_len
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for _ in range(replays):
-        graph.replay()
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_stop)
-    ms_per_step = total_ms / steps
-
-    # The same calls launched one by one from Python (no graph), for reference.
-    eager_steps = min(steps, 1000)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(eager_steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / eager_steps
-
-    # GEMM kernel duration: events stamped by the GEMM kernel's own dispatch on
-    # the library's stream, one pair per call, over eager calls.
-    kt_steps = min(steps, 500)
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(kt_steps)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(kt_steps)]
-    for e in ev_b + ev_e:
-        e.record()  # creates the underlying hipEvent
-    torch.cuda.synchronize()
-    # A spin kernel holds the queue while Python enqueues the calls, so they
-    # run back to back as in the timed region instead of one by one behind the
-    # Python loop (an idle GPU between calls stretches each kernel's events).
-    spin_ms = 1.5 * eager_ms * kt_steps
-    torch.cuda._sleep(int(spin_ms * 1e-3 * 2.4e9))
-    for i in range(kt_steps):
-        step(i, lm.LinearOpts(gemm_begin_event=ev_b[i].cuda_event,
-                              gemm_end_event=ev_e[i].cuda_event))
-    torch.cuda.synchronize()
-    gemm_ms = sum(ev_b[i].elapsed_time(ev_e[i]) for i in range(kt_steps)) / kt_steps
+    # Timed region: exactly `steps` layer calls, replayed from HIP graphs.
+    ms_per_step, timed_desc = graph_time(torch, L.step, steps)
+    # Sustained rate over at least 1000 calls (more weight sets than the cache holds).
+    sus_calls = max(1000, steps)
+    sus_ms, sus_desc = graph_time(torch, L.step, sus_calls)
+    e_steps = min(max(steps, 100), 1000)
+    e_ms = eager_ms(torch, L.step, e_steps)
+    kt_steps = min(max(steps, 100), 500)
+    gemm_ms = gemm_event_ms(torch, lm, L.step, kt_steps, e_ms)
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -390,24 +600,19 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
-    n_out = int(cnt.item())
-    compacted = uses_compaction(wl.M, wl.K, n_out, any_m=fp8)
-    call_bytes, gemm_bytes, int8_ops, fp16_flops = step_work(wl.M, wl.K, wl.N, n_out, compacted,
-                                                             int8w, large_m=fp8)
+    n_out, compacted, call_bytes, gemm_bytes, int8_ops, fp16_flops = L.work()
+    kern, call = rooflines(hbm_bound, ms_per_step, gemm_ms, call_bytes, gemm_bytes, int8_ops,
+                           fp16_flops)
+    kern["traffic"] = read_traffic(args.workload, args.variant)
     if hbm_bound:
         value, unit = call_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
-        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
         value, unit = (int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, "TOPS"
-        # fp16 flops weigh double: the fp16 MFMA peak is half the int8 one
-        achieved = (int8_ops + 2 * fp16_flops) / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof["traffic"] = read_traffic(args.workload, args.variant)
 
+    facts = device_facts(torch, dev)
+    ceiling = copy_ceiling(torch, dev)
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
@@ -418,30 +623,46 @@ def main():
                    "threshold": threshold, "outlier_columns": n_out,
                    "variant": "fp8 (E4M3) decomposition" if fp8 else "LLM.int8()",
                    "outlier_weights": args.outlier_weights,
-                   "k_compacted": compacted, "weight_sets_cycled": n_sets,
-                   "activation_pool": x_pool, "parallelism": "single GPU"},
-        "roofline": roof,
+                   "k_compacted": compacted, "weight_sets_cycled": L.n_sets,
+                   "activation_pool": len(L.Xs), "parallelism": "single GPU"},
+        "roofline": kern,
+        "call_roofline": call,
         "gemm_kernel_ms": round(gemm_ms, 6),
-        "timing": {"timed_region": f"{replays} replays of a HIP graph of {graph_len} layer calls",
-                   "eager_ms_per_step": round(eager_ms, 6),
+        "timing": {"timed_region": timed_desc, "timed_region_ms": round(ms_per_step * steps, 4),
+                   "sustained": {"calls": sus_calls, "region": sus_desc,
+                                 "ms_per_step": round(sus_ms, 6),
+                                 "value": round(call_bytes / (sus_ms * 1e-3) / 1e9 if hbm_bound
+                                                else (int8_ops + fp16_flops) / (sus_ms * 1e-3)
+                                                / 1e12, 3)},
+                   "eager_ms_per_step": round(e_ms, 6),
                    "gemm_kernel_timing": f"dispatch-stamped events around the GEMM kernel "
                                          f"of {kt_steps} eager calls queued behind a spin "
                                          f"kernel (run back to back)"},
-        "whole_step": {"algorithmic_bytes": call_bytes, "int8_ops": int8_ops,
-                       "fp16_flops": fp16_flops,
+        "whole_step": {"algorithmic_bytes": call_bytes, "gemm_algorithmic_bytes": gemm_bytes,
+                       "int8_ops": int8_ops, "fp16_flops": fp16_flops,
                        "GB_per_s": round(call_bytes / (ms_per_step * 1e-3) / 1e9, 2),
-                       "TOPS": round((int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, 3),
-                       "wall_s": round(wall, 4)},
-        "quantize_colwise": {"ms": round(colwise_ms, 5), "algorithmic_bytes": colwise_bytes,
-                             "GB_per_s": round(colwise_bytes / (colwise_ms * 1e-3) / 1e9, 2)},
+                       "TOPS": round((int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, 3)},
+        "peaks": {"hbm_published_GB_per_s": HBM_PEAK_GBS,
+                  "int8_published_TOPS": INT8_PEAK_TOPS,
+                  "fp16_published_TFLOPS": FP16_PEAK_TFLOPS, "device": facts,
+                  "measured_copy_ceiling": ceiling},
+        "quantize_passes": quantize_passes(
+            torch, lm, L.Xs, [st[2] if st[2] is not None else L.W0 for st in L.sets],
+            threshold),
     }
-    if not hbm_bound:
-        out["vendor_int8_gemm"] = vendor_int8_gemm(torch, wl.M, wl.K, wl.N, dev)
     if not args.no_accuracy:
-        del graph
-        out["accuracy"] = accuracy(torch, lm, X_host[0], W_host, Xs[0], W0, threshold)
+        out["accuracy"] = accuracy(torch, lm, L.X_host[0], L.W_host, L.Xs[0], L.W0, threshold)
+    X0_host, W_host = L.X_host[0], L.W_host
+    del L
+    torch.cuda.empty_cache()
+    if not args.no_sweep and args.variant == "int8" and args.outlier_weights == "fp16":
+        out["workloads"] = []
+        for name, thrs in SWEEP:
+            thrs = [t for t in thrs if not (name == args.workload and t == threshold)]
+            if thrs:
+                out["workloads"] += sweep_workload(torch, lm, name, thrs, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, X_host[0], W_host, threshold, args.cpu_seconds,
+        out["cpu_baseline"] = cpu_baseline(wl, X0_host, W_host, threshold, args.cpu_seconds,
                                            hbm_bound, n_out, fp8)
     print(json.dumps(out), flush=True)
 

@@ -1,6 +1,7 @@
 """The benchmark's host-side bookkeeping (no GPU): the algorithmic byte and op
 counts it reports, its copy of the library's compaction rule, and its refusal
 of a multi-GPU run."""
+import math
 import os
 import subprocess
 import sys
@@ -15,8 +16,9 @@ def test_decode_call_bytes():
     call, gemm, ops, flops = bench.step_work(32, 4096, 4096, 4, False)
     assert call == 2 * 32 * 4096 + 4096 * 4096 + 4 * 4096 + 2 * 4 * 4096 + 2 * 32 * 4096
     assert call == 17350656
-    # the small-M GEMM kernel reads Wq and X and writes the int32 split sums
-    assert gemm == 4096 * 4096 + 2 * 32 * 4096 + 4 * 32 * 4096
+    # the small-M GEMM kernel must read Wq and the fp16 X; its int32 split sums
+    # are its own intermediate and are not counted
+    assert gemm == 4096 * 4096 + 2 * 32 * 4096 == 17039360
     assert ops == 2 * 32 * 4096 * (4096 - 4) and flops == 2 * 32 * 4096 * 4
     # int8-only weights: the outlier rows come out of Wq, already counted
     assert bench.step_work(32, 4096, 4096, 4, False, int8w=True)[0] == call - 2 * 4 * 4096
@@ -77,3 +79,29 @@ def test_committed_counters_match_the_sources():
     for w in ("decode", "prefill", "13b", "70b"):
         for v in ("int8", "fp8"):
             assert bench.read_traffic(w, v) is not None, (w, v)
+
+
+def test_quantize_pass_bytes():
+    # each tensor read or written once
+    b = bench.pass_bytes(8192, 8192, 28672)
+    assert b["find_outliers"] == 2 * 8192 * 8192
+    assert b["quantize_rowwise"] == 3 * 8192 * 8192 + 4 * 8192
+    assert b["quantize_colwise"] == 3 * 8192 * 28672 + 4 * 28672
+
+
+def test_rooflines():
+    # decode: the GEMM kernel's bytes over its time, the call's over the step
+    k, c = bench.rooflines(True, 0.010, 0.005, 16e6, 8e6, 0, 0)
+    assert k["bound"] == "hbm" and math.isclose(k["achieved"], 1600.0)
+    assert math.isclose(k["frac"], 0.2) and math.isclose(c["frac"], 0.2)
+    # large M: fp16 flops weigh double against the int8 peak; the call's
+    # fraction is the ideal time over the step time
+    k, c = bench.rooflines(False, 0.2, 0.1, 0, 0, 250e9, 50e9)
+    assert k["bound"] == "mfma" and math.isclose(k["achieved"], 3500.0)
+    assert math.isclose(c["ideal_ms"], (250e9 / 5e15 + 50e9 / 2.5e15) * 1e3)
+    assert math.isclose(c["frac"], c["ideal_ms"] / 0.2, rel_tol=1e-3)
+
+
+def test_host_facts():
+    f = bench.host_facts()
+    assert f["nproc"] >= 1 and isinstance(f["cpu_model"], str)
