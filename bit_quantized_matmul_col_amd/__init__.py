@@ -25,6 +25,7 @@ LLMINT8_ERR_OVERFLOW = 3
 LLMINT8_ERR_WORKSPACE = 4
 LLMINT8_ERR_HIP = 5
 LLMINT8_MAX_K = 133144
+LLMINT8_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -70,6 +71,8 @@ def lib() -> C.CDLL:
         L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p,
                                      sz, p]
         L.llmint8_linear_ex.argtypes = L.llmint8_linear.argtypes + [p]
+        L.llmint8_linear_noalloc.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64,
+                                             p, p, p]
         L.llmint8_quantize_tensorwise_workspace_size.argtypes = [i64, i64]
         L.llmint8_quantize_tensorwise_workspace_size.restype = sz
         L.llmint8_quantize_tensorwise.argtypes = [p, i64, i64, i64, p, p, p, sz, p]
@@ -86,6 +89,7 @@ def lib() -> C.CDLL:
         L.llmint8_status_string.restype = C.c_char_p
         for name in ("llmint8_quantize_colwise", "llmint8_find_outliers",
                      "llmint8_quantize_rowwise", "llmint8_linear", "llmint8_linear_ex",
+                     "llmint8_linear_noalloc",
                      "llmint8_quantize_tensorwise", "llmint8_linear_tensorwise",
                      "llmint8_quantize_colwise_fp8", "llmint8_quantize_rowwise_fp8",
                      "llmint8_linear_fp8"):
@@ -273,6 +277,44 @@ def llmint8_linear(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
         _check(lib().llmint8_linear(*args))
     else:
         _check(lib().llmint8_linear_ex(*args, C.byref(opts)))
+    return Y
+
+
+def llmint8_linear_noalloc(X: torch.Tensor, Wq: torch.Tensor, col_absmax: torch.Tensor,
+                           W: torch.Tensor | None, threshold: float = 6.0, *, Y=None,
+                           outlier_count: torch.Tensor | None = None,
+                           C_debug: torch.Tensor | None = None) -> torch.Tensor:
+    """llmint8_linear without a workspace: the library's per-GPU scratch array
+    (LLMINT8_NOALLOC_SCRATCH_BYTES) takes its place, so the C call allocates
+    nothing (pass Y to allocate nothing here either). Shapes whose workspace
+    would exceed the scratch raise Llmint8Error (LLMINT8_ERR_WORKSPACE); calls
+    that may overlap on one GPU race on the shared scratch."""
+    _need(X, "X", torch.float16, 2)
+    _need(Wq, "Wq", torch.int8, 2)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or not Wq.is_contiguous():
+        raise ValueError("Wq must be contiguous [N, K]")
+    _need_vec(col_absmax, "col_absmax", torch.float32, N)
+    if W is not None:
+        _need(W, "W", torch.float16, 2)
+        if tuple(W.shape) != (K, N):
+            raise ValueError("W must be [K, N]")
+    elif not (math.isinf(threshold) and threshold > 0):
+        raise ValueError("W may be omitted only with threshold=+inf")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    _need_shape(Y, "Y", (M, N))
+    if outlier_count is not None:
+        _need_vec(outlier_count, "outlier_count", torch.int32, 1, exact=False)
+    if C_debug is not None:
+        _need(C_debug, "C_debug", torch.int32)
+        _need_shape(C_debug, "C_debug", (M, N), contiguous=True)
+    _check(lib().llmint8_linear_noalloc(
+        _ptr(X), M, K, _ld(X, "X"), _ptr(Wq), _ptr(col_absmax), _ptr(W),
+        _ld(W, "W") if W is not None else N, N, float(threshold), _ptr(Y), _ld(Y, "Y"),
+        _ptr(outlier_count), _ptr(C_debug), _stream(X)))
     return Y
 
 

@@ -3,6 +3,7 @@
 // rejected call enqueues nothing.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.hpp"
 #include "llmint8.h"
@@ -224,14 +225,13 @@ LLMINT8_EXPORT size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N) {
   return make_layout(M, K, N, true).total;
 }
 
-LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
-                                     const int8_t *Wq, const float *col_absmax, const uint16_t *W,
-                                     int64_t ldw, int64_t N, float threshold, uint16_t *Y,
-                                     int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
-                                     void *workspace, size_t workspace_bytes, void *stream,
-                                     const llmint8_linear_opts *opts) {
-  if (opts && opts->struct_size != sizeof(llmint8_linear_opts)) return LLMINT8_ERR_INVALID_ARG;
-  const llmint8_linear_opts o = opts ? *opts : llmint8_linear_opts{};
+namespace {
+
+// Every check of llmint8_linear_ex except the workspace one; makes no HIP call.
+int check_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, const int8_t *Wq,
+                 const float *col_absmax, const uint16_t *W, int64_t ldw, int64_t N,
+                 float threshold, uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
+                 int32_t *C_debug, const llmint8_linear_opts &o) {
   if (o.outlier_weights != LLMINT8_OUTLIER_W_FP16 && o.outlier_weights != LLMINT8_OUTLIER_W_INT8)
     return LLMINT8_ERR_INVALID_ARG;
   const bool int8w = o.outlier_weights == LLMINT8_OUTLIER_W_INT8;
@@ -250,11 +250,20 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
     return LLMINT8_ERR_UNSUPPORTED;
   // the GEMM addresses a 256-row output tile with 32-bit byte offsets
   if (ldy >= kMaxTileLd || N >= kMaxTileLd) return LLMINT8_ERR_UNSUPPORTED;
+  return LLMINT8_OK;
+}
+
+// The layer after check_linear: the workspace check, then the launches.
+int run_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, const int8_t *Wq,
+               const float *col_absmax, const uint16_t *W, int64_t ldw, int64_t N,
+               float threshold, uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
+               int32_t *C_debug, void *workspace, size_t workspace_bytes, hipStream_t s,
+               const llmint8_linear_opts &o) {
   const Layout L = make_layout(M, K, N, true);
   if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
 
-  hipStream_t s = (hipStream_t)stream;
+  const bool int8w = o.outlier_weights == LLMINT8_OUTLIER_W_INT8;
   uint8_t *ws = (uint8_t *)workspace;
   const GemmEvents ev{o.gemm_begin_event, o.gemm_end_event};
   // with int8 outlier weights the fp16 weight is not read at all
@@ -282,6 +291,73 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
 
   return hip_status(prefill_layer(X, M, K, ldx, Wq, col_absmax, Wf, ldw, N, threshold, Y, ldy,
                                   outlier_count_out, C_debug, ws, L, o, ev, ep, false, s));
+}
+
+// Scratch of llmint8_linear_noalloc: one copy per GPU the library runs on,
+// held until the process ends. Host code never uses the array's name as an
+// address (on the host it is only a handle); it uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = LLMINT8_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch, looked up once per device with that
+// device current.
+int scratch_of(hipStream_t s, void **out) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return LLMINT8_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return LLMINT8_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return LLMINT8_ERR_HIP;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return LLMINT8_ERR_HIP;
+    if (e != hipSuccess || !p) return LLMINT8_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return LLMINT8_OK;
+}
+
+}  // namespace
+
+LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                     const int8_t *Wq, const float *col_absmax, const uint16_t *W,
+                                     int64_t ldw, int64_t N, float threshold, uint16_t *Y,
+                                     int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
+                                     void *workspace, size_t workspace_bytes, void *stream,
+                                     const llmint8_linear_opts *opts) {
+  if (opts && opts->struct_size != sizeof(llmint8_linear_opts)) return LLMINT8_ERR_INVALID_ARG;
+  const llmint8_linear_opts o = opts ? *opts : llmint8_linear_opts{};
+  const int st = check_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
+                              outlier_count_out, C_debug, o);
+  if (st) return st;
+  return run_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
+                    outlier_count_out, C_debug, workspace, workspace_bytes, (hipStream_t)stream,
+                    o);
+}
+
+LLMINT8_EXPORT int llmint8_linear_noalloc(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                                          const int8_t *Wq, const float *col_absmax,
+                                          const uint16_t *W, int64_t ldw, int64_t N,
+                                          float threshold, uint16_t *Y, int64_t ldy,
+                                          int32_t *outlier_count_out, int32_t *C_debug,
+                                          void *stream) {
+  const llmint8_linear_opts o{};
+  int st = check_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
+                        outlier_count_out, C_debug, o);
+  if (st) return st;
+  if (make_layout(M, K, N, true).total > kScratchBytes) return LLMINT8_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if ((st = scratch_of((hipStream_t)stream, &ws))) return st;
+  return run_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
+                    outlier_count_out, C_debug, ws, kScratchBytes, (hipStream_t)stream, o);
 }
 
 LLMINT8_EXPORT size_t llmint8_quantize_tensorwise_workspace_size(int64_t K, int64_t N) {

@@ -24,6 +24,8 @@
  *   - The caller owns and allocates every buffer, including the workspace. The
  *     library never allocates device memory, keeps no state between calls and
  *     is re-entrant; calls that share a workspace must be ordered on one stream.
+ *     The one exception is llmint8_linear_noalloc, whose workspace is a fixed
+ *     scratch array the library holds on each GPU (see there).
  *   - Calls are asynchronous: they enqueue kernels on `stream` and return.
  *     Results are valid once the caller synchronizes with the stream. Inputs
  *     and outputs must not overlap.
@@ -123,6 +125,29 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
                    const uint16_t *W, int64_t ldw, int64_t N, float threshold,
                    uint16_t *Y, int64_t ldy, int32_t *outlier_count_out, int32_t *C_debug,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * llmint8_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, results and checks
+ * as llmint8_linear otherwise; the call itself allocates nothing.
+ * Its workspace is a static device array of LLMINT8_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) inside the library, one per GPU, held until the process ends; its
+ * address is looked up on the first call on each device (the only HIP call
+ * besides the launches). A call whose llmint8_workspace_size(M, K, N) exceeds
+ * that size returns LLMINT8_ERR_WORKSPACE before any HIP call: in practice
+ * this covers the small-M (decode) shapes, M <= 64. Every call on one GPU
+ * shares its scratch, so calls that may overlap on one GPU (different
+ * streams, or host threads without ordering) race; order them on one stream.
+ * Nothing in the scratch needs to start at zero: every call writes what it
+ * reads.
+ */
+#define LLMINT8_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int llmint8_linear_noalloc(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                           const int8_t *Wq, const float *col_absmax,
+                           const uint16_t *W, int64_t ldw, int64_t N, float threshold,
+                           uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
+                           int32_t *C_debug, void *stream);
 
 /* Where the 16-bit outlier product takes its weight rows from. */
 #define LLMINT8_OUTLIER_W_FP16 0 /* rows k in O of the fp16 weight W */

@@ -90,6 +90,17 @@ int main(void)
     expect("linear_ex int8 weights small ws",
            llmint8_linear_ex(A, 4, 64, 64, B, A, NULL, 32, 32, 6.f, B, 32, NULL, NULL, A, 0,
                              NULL, &o), 4);
+    /* the allocation-free layer: every check first, then the scratch size */
+    expect("noalloc null X", llmint8_linear_noalloc(NULL, 4, 64, 64, B, A, A, 32, 32, 6.f, B, 32,
+                                                    NULL, NULL, NULL), 1);
+    expect("noalloc nan", llmint8_linear_noalloc(A, 4, 64, 64, B, A, A, 32, 32, nan, B, 32, NULL,
+                                                 NULL, NULL), 1);
+    expect("noalloc beyond scratch",
+           llmint8_linear_noalloc(A, 2048, 4096, 4096, B, A, A, 11008, 11008, 6.f, B, 11008,
+                                  NULL, NULL, NULL), 4);
+    expect("noalloc huge", llmint8_linear_noalloc(A, ((int64_t)1 << 31) - 1, 133136, 133136, B,
+                                                  A, A, 65536, 65536, 6.f, B, 65536, NULL, NULL,
+                                                  NULL), 4);
     /* per-tensor and FP8 */
     expect("qtw small ws", llmint8_quantize_tensorwise(A, 64, 32, 32, B, A, A, 16, NULL), 4);
     expect("ltw ldy short", llmint8_linear_tensorwise(A, 4, 64, 64, B, A, 32, NULL, B, 16, NULL,

@@ -56,6 +56,7 @@ L.llmint8_find_outliers.argtypes = [p, i64, i64, i64, f32, p, p, p, sz, p]
 L.llmint8_quantize_rowwise.argtypes = [p, i64, i64, i64, p, p, p, p, p]
 L.llmint8_linear.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p, sz, p]
 L.llmint8_linear_ex.argtypes = L.llmint8_linear.argtypes + [p]
+L.llmint8_linear_noalloc.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, f32, p, i64, p, p, p]
 class Opts(C.Structure):
     _fields_ = [("struct_size", sz), ("b", p), ("e", p), ("outlier_weights", C.c_int),
                 ("bias", p), ("y_col_absmax", p), ("x_col_absmax", p)]
@@ -101,6 +102,17 @@ def lfp8(name, size=C.sizeof(Opts), ow=0, W=A, t=6.0, M=4, cdbg=N0, wsb=0, opts=
     o = Opts(size, None, None, ow, None, None, None)
     res[name] = L.llmint8_linear_fp8(A, M, 64, 64, B, A, W, 32, 32, t, B, 32, None, cdbg, A, wsb,
                                      None, C.byref(o) if opts else None)
+def noalloc(name, X=A, M=4, K=64, ldx=64, W=A, N=32, t=6.0, Y=B, ldy=32, cdbg=N0):
+    res[name] = L.llmint8_linear_noalloc(X, M, K, ldx, B, A, W, 32 if N == 32 else N, N, t, Y,
+                                         ldy, None, cdbg, None)
+noalloc("noalloc_null_X", X=N0)
+noalloc("noalloc_nan_threshold", t=math.nan)
+noalloc("noalloc_null_W_finite_threshold", W=N0)
+noalloc("noalloc_ldy_short", ldy=16)
+noalloc("noalloc_misaligned_cdbg", cdbg=MIS)
+noalloc("noalloc_K_too_big", K=133152, ldx=133152)
+# a workspace beyond the 32 MiB scratch is refused before any HIP call
+noalloc("noalloc_beyond_scratch", M=2048, K=4096, ldx=4096, N=11008, ldy=11008)
 colwise("colwise_null_W", W=N0)
 colwise("colwise_K0", K=0)
 colwise("colwise_ld_short", ldw=16)
@@ -173,6 +185,9 @@ print(json.dumps(res))
 """
 
 EXPECTED = {
+    "noalloc_null_X": 1, "noalloc_nan_threshold": 1, "noalloc_null_W_finite_threshold": 1,
+    "noalloc_ldy_short": 1, "noalloc_misaligned_cdbg": 2, "noalloc_K_too_big": 3,
+    "noalloc_beyond_scratch": 4,
     "colwise_null_W": 1, "colwise_K0": 1, "colwise_ld_short": 1, "colwise_ld_not_mult8": 2,
     "colwise_misaligned_W": 2, "colwise_K_not_mult16": 2, "colwise_N_not_mult8": 2,
     "colwise_K_too_big": 3, "colwise_null_Wq": 1,
