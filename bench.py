@@ -529,8 +529,49 @@ def sweep_workload(torch, lm, name, thresholds, dev, steps=10):
     return outs
 
 
+def summarize_profile(path: str, min_calls: int = 1) -> str:
+    """Text summary of a rocprofv3 CSV output directory: per kernel, the call
+    count and durations (kernel_stats.csv), or per kernel and counter the
+    average value per dispatch (counter_collection.csv)."""
+    import csv
+    import glob
+
+    lines = []
+    stats = sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True))
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+        lines.append("# columns: calls, total ns, average ns, min ns, max ns, share of GPU "
+                     "time, kernel")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            if int(r["Calls"]) < min_calls:
+                continue
+            lines.append(f"{int(r['Calls']):6d} {float(r['TotalDurationNs']):12.0f} "
+                         f"{float(r['AverageNs']):12.1f} {float(r['MinNs']):10.0f} "
+                         f"{float(r['MaxNs']):10.0f} "
+                         f"{100 * float(r['TotalDurationNs']) / total:6.2f}%  {r['Name'][:160]}")
+    counters = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                recursive=True))
+    for f in counters:
+        acc = {}
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            d = acc.setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        lines.append("# columns: dispatches, average value per dispatch, counter, kernel")
+        for (kern, ctr), d in sorted(acc.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+            if len(d) < min_calls:
+                continue
+            lines.append(f"{len(d):6d} {sum(d.values()) / len(d):18.1f}  {ctr:32s} {kern[:160]}")
+    return "\n".join(lines)
+
+
 def main():
     import workloads
+
+    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-profile":
+        print(summarize_profile(sys.argv[2], int(sys.argv[3]) if len(sys.argv) > 3 else 1))
+        return
 
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -548,6 +589,10 @@ def main():
                     help="int8: the LLM.int8() layer; fp8: its E4M3 variant")
     ap.add_argument("--outlier-weights", default="fp16", choices=("fp16", "int8"),
                     help="fp16: outlier rows of the fp16 weight; int8: from Wq (no fp16 W kept)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed region and the GEMM-event calls (for profiler runs): "
+                         "no sustained rate, quantize passes, ceiling, accuracy, sweep or "
+                         "CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
     args = ap.parse_args()
@@ -585,11 +630,12 @@ def main():
     # Timed region: exactly `steps` layer calls, replayed from HIP graphs.
     ms_per_step, timed_desc = graph_time(torch, L.step, steps)
     # Sustained rate over at least 1000 calls (more weight sets than the cache holds).
-    sus_calls = max(1000, steps)
-    sus_ms, sus_desc = graph_time(torch, L.step, sus_calls)
-    e_steps = min(max(steps, 100), 1000)
+    sus_calls = max(1000, steps) if not args.no_extras else steps
+    sus_ms, sus_desc = ((ms_per_step, timed_desc) if args.no_extras
+                        else graph_time(torch, L.step, sus_calls))
+    e_steps = min(max(steps, 100), 1000) if not args.no_extras else steps
     e_ms = eager_ms(torch, L.step, e_steps)
-    kt_steps = min(max(steps, 100), 500)
+    kt_steps = min(max(steps, 100), 500) if not args.no_extras else steps
     gemm_ms = gemm_event_ms(torch, lm, L.step, kt_steps, e_ms)
 
     if args.copy_calibration_mib:
@@ -611,8 +657,8 @@ def main():
     else:
         value, unit = (int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, "TOPS"
 
-    facts = device_facts(torch, dev)
-    ceiling = copy_ceiling(torch, dev)
+    facts = device_facts(torch, dev) if not args.no_extras else {}
+    ceiling = copy_ceiling(torch, dev) if not args.no_extras else {}
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 6),
@@ -646,10 +692,12 @@ def main():
                   "int8_published_TOPS": INT8_PEAK_TOPS,
                   "fp16_published_TFLOPS": FP16_PEAK_TFLOPS, "device": facts,
                   "measured_copy_ceiling": ceiling},
-        "quantize_passes": quantize_passes(
-            torch, lm, L.Xs, [st[2] if st[2] is not None else L.W0 for st in L.sets],
-            threshold),
     }
+    if not args.no_extras:
+        out["quantize_passes"] = quantize_passes(
+            torch, lm, L.Xs, [st[2] if st[2] is not None else L.W0 for st in L.sets], threshold)
+    if args.no_extras:
+        args.no_accuracy = args.no_sweep = args.no_cpu_baseline = True
     if not args.no_accuracy:
         out["accuracy"] = accuracy(torch, lm, L.X_host[0], L.W_host, L.Xs[0], L.W0, threshold)
     X0_host, W_host = L.X_host[0], L.W_host
