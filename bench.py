@@ -688,6 +688,9 @@ def main():
                        "int8_ops": int8_ops, "fp16_flops": fp16_flops,
                        "GB_per_s": round(call_bytes / (ms_per_step * 1e-3) / 1e9, 2),
                        "TOPS": round((int8_ops + fp16_flops) / (ms_per_step * 1e-3) / 1e12, 3)},
+        "build": {"source_digest": lm.build_record.get("source_digest", "")[:16],
+                  "compiler": lm.build_record.get("compiler", ""),
+                  "built_at": lm.build_record.get("built_at", "")},
         "peaks": {"hbm_published_GB_per_s": HBM_PEAK_GBS,
                   "int8_published_TOPS": INT8_PEAK_TOPS,
                   "fp16_published_TFLOPS": FP16_PEAK_TFLOPS, "device": facts,

@@ -17,6 +17,9 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libllmint8.so")
+_DEFAULT_LIB = LIB_PATH
+# filled when the library is loaded: source digest, compiler and flags it was built with
+build_record: dict = {}
 
 LLMINT8_OK = 0
 LLMINT8_ERR_INVALID_ARG = 1
@@ -59,6 +62,10 @@ def lib() -> C.CDLL:
             raise ImportError(
                 f"{LIB_PATH} is missing: build the HIP library first "
                 "(python -c 'import __graft_entry__ as g; g.build()')")
+        if LIB_PATH == _DEFAULT_LIB:
+            # the in-tree library must be the recorded build of the current sources
+            from . import build as _build
+            build_record.update(_build.check_record())
         L = C.CDLL(LIB_PATH)
         p, i64, f32, sz = C.c_void_p, C.c_int64, C.c_float, C.c_size_t
         L.llmint8_quantize_colwise.argtypes = [p, i64, i64, i64, p, p, p]

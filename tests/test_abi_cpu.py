@@ -251,3 +251,17 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "_lib", None)
     with pytest.raises(ImportError):
         b.lib()
+
+
+def test_library_matches_its_build_record(monkeypatch):
+    # the binding loads the in-tree library only if it is the recorded build of
+    # the sources as they are now
+    import bit_quantized_matmul_col_amd as b
+    from bit_quantized_matmul_col_amd import build
+    rec = build.check_record()
+    assert rec["source_digest"] == build.source_digest()
+    assert "--offload-arch=gfx950" in rec["flags"] and "-packed-fp32-ops" in rec["flags"]
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(build, "source_digest", lambda: "0" * 64)
+    with pytest.raises(ImportError, match="different sources"):
+        b.lib()
