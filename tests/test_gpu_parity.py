@@ -11,6 +11,7 @@ the outlier set is known, so the oracle runs on chunks of rows in parallel
 (tests/oracle_rows.py).
 """
 import math
+import os
 import sys
 
 import numpy as np
@@ -332,6 +333,22 @@ def test_workload_70b(dev, w70, threshold, call):
     W, ref_w = w70
     X = workloads.make_x(wl, call)
     run_all(torch, lm, X, W, threshold, rows=rows, check_colwise=(call == 0), ref_w=ref_w)
+    torch.cuda.empty_cache()
+
+
+# Every row of the 70b workload at all three thresholds: the full report run,
+# left out of routine runs for its time (about a minute of oracle work per
+# threshold on 16 threads). Enable with LLMINT8_FULL_70B=1.
+@pytest.mark.skipif(os.environ.get("LLMINT8_FULL_70B") != "1",
+                    reason="full 70b report run: set LLMINT8_FULL_70B=1")
+@pytest.mark.parametrize("threshold,call", [(6.0, 0), (math.inf, 1), (4.0, 2)])
+def test_workload_70b_every_row(dev, w70, threshold, call):
+    torch, lm = dev
+    wl = workloads.WORKLOADS["70b"]
+    say(f"case workload 70b threshold={threshold} call={call} (every row against the oracle)")
+    W, ref_w = w70
+    X = workloads.make_x(wl, call)
+    run_all(torch, lm, X, W, threshold, check_colwise=(call == 0), ref_w=ref_w)
     torch.cuda.empty_cache()
 
 
