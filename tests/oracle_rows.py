@@ -16,7 +16,9 @@ GEMM, the first and the last row.
 from __future__ import annotations
 
 import os
-from concurrent.futures import ThreadPoolExecutor
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor, as_completed
 
 import numpy as np
 
@@ -45,6 +47,23 @@ def tile_rows(M: int, n: int = 256, tile: int = TILE_ROWS, seed: int | None = No
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def _run(fn, chunks):
+    """fn over the row chunks in a thread pool, results in chunk order. Long
+    runs (the full 70b workload) report their progress on stderr every 20 s."""
+    t0 = last = time.monotonic()
+    out = [None] * len(chunks)
+    with ThreadPoolExecutor(workers()) as ex:
+        futs = {ex.submit(fn, c): i for i, c in enumerate(chunks)}
+        for done, f in enumerate(as_completed(futs), 1):
+            out[futs[f]] = f.result()
+            now = time.monotonic()
+            if now - last > 20:
+                print(f"oracle rows: {done}/{len(chunks)} chunks, {now - t0:.0f} s",
+                      file=sys.stderr, flush=True)
+                last = now
+    return out
+
+
 def _chunks(rows: np.ndarray, nw: int):
     per = max(1, -(-rows.size // (4 * nw)))
     return [rows[i:i + per] for i in range(0, rows.size, per)]
@@ -69,9 +88,7 @@ def linear_rows(X, W, threshold, rows, Wq, s, *, outlier_weights="fp16", bias=No
             Y = oracle.add_bias(Y, bias)
         return Xq, m, C, Y
 
-    nw = workers()
-    with ThreadPoolExecutor(nw) as ex:
-        parts = list(ex.map(part, _chunks(rows, nw)))
+    parts = _run(part, _chunks(rows, workers()))
     return dict(rows=rows, idx=idx, Xq=np.concatenate([p[0] for p in parts]),
                 m=np.concatenate([p[1] for p in parts]),
                 C=np.concatenate([p[2] for p in parts]),
@@ -90,9 +107,7 @@ def linear_fp8_rows(X, W, threshold, rows, Wq8, s):
         C = oracle.gemm_fp8(Xq, Wq8)
         return Xq, m, C, oracle.merge_fp8(C, m, s, Xs, W, idx)
 
-    nw = workers()
-    with ThreadPoolExecutor(nw) as ex:
-        parts = list(ex.map(part, _chunks(rows, nw)))
+    parts = _run(part, _chunks(rows, workers()))
     return dict(rows=rows, idx=idx, Wq=Wq8, s=s, Xq=np.concatenate([p[0] for p in parts]),
                 m=np.concatenate([p[1] for p in parts]),
                 C=np.concatenate([p[2] for p in parts]),
