@@ -267,25 +267,29 @@ __device__ void compact_block(int64_t b, int64_t nb, const WeightSideArgs &a, ui
   }
 }
 
-// The preparation of a large-M call after detection, in one launch: blocks
-// [0, M) quantize the rows of X, the next gather_blocks gather W_O^T, the rest
-// compact Wq (their counts are fixed by the host; the work they find depends on
-// the outlier count on the device).
+// The preparation of a large-M call after detection, in one launch: the first
+// blocks compact Wq, the next gather_blocks gather W_O^T, the last M quantize
+// the rows of X (the block counts are fixed by the host; the work the
+// compaction blocks find depends on the outlier count on the device). Blocks
+// start roughly in index order, so the compaction blocks, each of which walks
+// several rows of Wq one after another, and the gathers, each a chain of
+// dependent loads, begin first and overlap the row blocks instead of running
+// after them.
 template <class Codec>
 __global__ __launch_bounds__(256) void k_layer_prep(RowQuantArgs r, WeightSideArgs w) {
   extern __shared__ u32x4 srow_v[];
   uint8_t *srow = (uint8_t *)srow_v;
   const int64_t b = blockIdx.x;
-  if (b < r.M) {
-    rowquant_row<Codec>(b, r, srow);
-  } else if (b < r.M + w.gather_blocks) {
+  const int64_t nc = (int64_t)gridDim.x - r.M - w.gather_blocks;  // compaction blocks
+  if (b < nc) {
+    compact_block(b, nc, w, srow);
+  } else if (b < nc + w.gather_blocks) {
     if (w.W)
-      gather_wot_block(b - r.M, w);
+      gather_wot_block(b - nc, w);
     else
-      gather_codes_block(b - r.M, w);
+      gather_codes_block(b - nc, w);
   } else {
-    const int64_t c0 = r.M + w.gather_blocks;
-    compact_block(b - c0, gridDim.x - c0, w, srow);
+    rowquant_row<Codec>(b - nc - w.gather_blocks, r, srow);
   }
 }
 
