@@ -1,6 +1,7 @@
 """The benchmark's host-side bookkeeping (no GPU): the algorithmic byte and op
 counts it reports, its copy of the library's compaction rule, and its refusal
 of a multi-GPU run."""
+import glob
 import math
 import os
 import subprocess
@@ -79,6 +80,20 @@ def test_committed_counters_match_the_sources():
     for w in ("decode", "prefill", "13b", "70b"):
         for v in ("int8", "fp8"):
             assert bench.read_traffic(w, v) is not None, (w, v)
+
+
+def test_every_counter_summary_names_the_current_gemm_sources():
+    # the MFMA, LDS and memory-pipeline summaries of the large-M GEMM carry the
+    # digest of the sources they were taken on; a kernel change marks them stale
+    files = sorted(glob.glob(os.path.join(bench.PROFILES, "gemm_*_counters.txt")))
+    assert len(files) >= 12
+    for f in files:
+        digests = [line.split(":", 1)[1].strip() for line in open(f)
+                   if "kernel_source_digest:" in line and not line.startswith("#")]
+        assert len(digests) == 1, f
+        fam = "small_m" if os.path.basename(f) in ("gemm_decode_hbm_counters.txt",
+                                                    "gemm_fp8_decode_hbm_counters.txt") else "large_m"
+        assert digests[0] == bench.kernel_source_digest(fam), f
 
 
 def test_quantize_pass_bytes():
