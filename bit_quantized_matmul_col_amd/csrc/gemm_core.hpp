@@ -272,6 +272,37 @@ struct SpreadLoads {
   }
 };
 
+// The loads of the next stage in a two-stage ring: the first half of the row
+// groups before this stage's MFMAs, the second half after its first k-step.
+// Each direct-to-LDS load moves 1 KB through the texture path, and a wave that
+// issues all of its loads at once stalls its MFMA issue until they are
+// accepted; issued in two halves, they still land well before the next
+// stage's wait.
+template <int BM, int BN, int NW, int SK>
+struct SplitLoads {
+  static constexpr int G = OperandTile<BM, NW, SK>::G;
+  static_assert(G == OperandTile<BN, NW, SK>::G && G % 2 == 0, "equal, even row groups");
+  const OperandTile<BM, NW, SK> &A;
+  const OperandTile<BN, NW, SK> &B;
+  uint8_t *buf;
+  int kb;
+  bool on;
+  __device__ void groups(int j0, int j1) const {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (j >= j0 && j < j1) {
+        A.load_group(buf, kb, j);
+        B.load_group(buf + BM * SK, kb, j);
+      }
+  }
+  __device__ void first_half() const {
+    if (on) groups(0, G / 2);
+  }
+  __device__ void operator()(int ks, int) const {
+    if (on && ks == 0) groups(G / 2, G);
+  }
+};
+
 // What a k-loop multiplies: int8 codes (int32 sums), fp16 (the outlier
 // product) or E4M3 codes (fp32 sums).
 enum class Op { I8, F16, F8 };
@@ -308,24 +339,37 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
     ring_barrier();
     // The loads of stage it + NST - 1. With three or more buffers they are
     // spread over the k-steps of this stage's MFMAs (they have at least one
-    // further stage to land), so that no wave stalls on a burst of address
-    // work; with two they must all be in flight from the start of the stage.
+    // further stage to land); with two, half go out before the MFMAs and half
+    // after the first of the stage's four k-steps, so that the second half
+    // still has three quarters of the stage to land. An E4M3 stage has two
+    // k-steps, and its second half would have only half a stage (measured
+    // slower), so it issues the whole stage up front.
     const int64_t nx = it + NST - 1;
     const bool more = nx < nstages;
     uint8_t *buf = smem + (nx % NST) * STAGE;
     const int kb = (int)(nx * SK);
-    if (NST == 2 && more) {
-      A.load(buf, kb);
-      B.load(buf + BM * SK, kb);
-    }
-    const SpreadLoads<BM, BN, NW, SK> issue{A, B, buf, kb, NST > 2 && more};
     const uint8_t *cur = smem + (it % NST) * STAGE;
-    if constexpr (OP == Op::F16)
-      stage_mfma<BM, WM, WN, MI, NI, SK, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
-    else if constexpr (OP == Op::F8)
-      stage_mfma<BM, WM, WN, MI, NI, SK, i32x8>(cur, wm, wn, li, lg, acc, MfmaF8(), issue);
-    else
-      stage_mfma<BM, WM, WN, MI, NI, SK, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
+    auto run = [&](const auto &issue) {
+      if constexpr (OP == Op::F16)
+        stage_mfma<BM, WM, WN, MI, NI, SK, f16x8>(cur, wm, wn, li, lg, acc, MfmaF16(), issue);
+      else if constexpr (OP == Op::F8)
+        stage_mfma<BM, WM, WN, MI, NI, SK, i32x8>(cur, wm, wn, li, lg, acc, MfmaF8(), issue);
+      else
+        stage_mfma<BM, WM, WN, MI, NI, SK, i32x4>(cur, wm, wn, li, lg, acc, MfmaI8(), issue);
+    };
+    if constexpr (NST == 2 && OP != Op::F8) {
+      const SplitLoads<BM, BN, NW, SK> issue{A, B, buf, kb, more};
+      issue.first_half();
+      run(issue);
+    } else if constexpr (NST == 2) {
+      if (more) {
+        A.load(buf, kb);
+        B.load(buf + BM * SK, kb);
+      }
+      run(SpreadLoads<BM, BN, NW, SK>{A, B, buf, kb, false});
+    } else {
+      run(SpreadLoads<BM, BN, NW, SK>{A, B, buf, kb, more});
+    }
   }
   __syncthreads();  // every wave is done with the ring before it is reused
 }
