@@ -131,6 +131,9 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
         raise ValueError(f"{name} must be on a GPU device")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if ndim == 2 and t.numel() == 0:
+        # the C calls take M, K, N >= 1 (LLMINT8_ERR_INVALID_ARG otherwise)
+        raise ValueError(f"{name} is empty ({tuple(t.shape)}); every dimension must be >= 1")
 
 
 def _need_shape(t: torch.Tensor, name: str, shape: tuple, contiguous: bool = False):

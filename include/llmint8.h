@@ -31,7 +31,8 @@
  *     and outputs must not overlap.
  *   - Shape/alignment rules (else LLMINT8_ERR_UNSUPPORTED): every pointer is
  *     16-byte aligned; K is a multiple of 16; N is a multiple of 8; ldx, ldw and
- *     ldy are multiples of 8. M >= 1 is unrestricted.
+ *     ldy are multiples of 8. M >= 1 is otherwise unrestricted. An empty input
+ *     (M, K or N below 1) is LLMINT8_ERR_INVALID_ARG.
  *   - Arguments are validated before any HIP call is made. A failed check
  *     enqueues nothing and leaves every output untouched. Device faults surface
  *     at the caller's next synchronization.

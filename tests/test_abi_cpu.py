@@ -140,6 +140,12 @@ linear("linear_misaligned_cdbg", cdbg=MIS, wsb=1 << 40)
 linear("linear_workspace_small", wsb=100)
 linear("linear_K_not_mult16", K=40, ldx=48)
 linear("linear_N0", N=0)
+linear("linear_M0", M=0)
+rowq("rowq_M0", M=0)
+find("find_M0", M=0)
+ltw("ltw_M0", M=0)
+lfp8("lfp8_M0", M=0, wsb=1 << 40)
+noalloc("noalloc_M0", M=0)
 linear_ex("ex_struct_size_old", size=24)
 linear_ex("ex_bad_outlier_weights", ow=2)
 linear_ex("ex_misaligned_bias", bias=MIS)
@@ -197,7 +203,8 @@ EXPECTED = {
     "linear_null_W_finite_threshold": 1, "linear_null_W_inf_threshold_small_ws": 4,
     "linear_null_Y": 1, "linear_ldy_short": 1, "linear_nan_threshold": 1,
     "linear_misaligned_cdbg": 2, "linear_workspace_small": 4, "linear_K_not_mult16": 2,
-    "linear_N0": 1,
+    "linear_N0": 1, "linear_M0": 1, "rowq_M0": 1, "find_M0": 1, "ltw_M0": 1, "lfp8_M0": 1,
+    "noalloc_M0": 1,
     "ex_struct_size_old": 1, "ex_bad_outlier_weights": 1, "ex_misaligned_bias": 2,
     "ex_misaligned_y_col_absmax": 2, "ex_misaligned_x_col_absmax": 2,
     # int8 outlier weights need no fp16 W at any threshold: the call reaches the

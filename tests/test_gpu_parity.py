@@ -801,6 +801,39 @@ def test_binding_rejects_undersized_buffers(dev):
     assert_y_close(Y.cpu().numpy(), oracle.linear(X, W, 6.0)["Y"], "Y")
 
 
+def test_empty_inputs_are_refused_before_any_launch(dev):
+    # a zero dimension is an argument error on every entry point (the C calls
+    # return LLMINT8_ERR_INVALID_ARG for it): the binding raises ValueError and
+    # enqueues nothing
+    torch, lm = dev
+    say("case empty inputs refused on every entry point")
+    K, N = 256, 64
+    X, W, _ = workloads.random_case(4, K, N, seed=5, n_out=1)
+    Wd = to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    Wq8, s8 = lm.llmint8_quantize_colwise_fp8(Wd)
+    Wqt, sw = lm.llmint8_quantize_tensorwise(Wd)
+    torch.cuda.synchronize()
+    X0 = torch.zeros((0, K), dtype=torch.float16, device="cuda")
+    W0 = torch.zeros((0, N), dtype=torch.float16, device="cuda")
+    empty = [
+        ("find_outliers", lambda: lm.llmint8_find_outliers(X0, 6.0)),
+        ("quantize_rowwise", lambda: lm.llmint8_quantize_rowwise(X0)),
+        ("quantize_rowwise_fp8", lambda: lm.llmint8_quantize_rowwise_fp8(X0)),
+        ("quantize_colwise, K = 0", lambda: lm.llmint8_quantize_colwise(W0)),
+        ("quantize_colwise_fp8, K = 0", lambda: lm.llmint8_quantize_colwise_fp8(W0)),
+        ("quantize_tensorwise, K = 0", lambda: lm.llmint8_quantize_tensorwise(W0)),
+        ("linear", lambda: lm.llmint8_linear(X0, Wq, s, Wd, 6.0)),
+        ("linear_noalloc", lambda: lm.llmint8_linear_noalloc(X0, Wq, s, Wd, 6.0)),
+        ("linear_fp8", lambda: lm.llmint8_linear_fp8(X0, Wq8, s8, Wd, 6.0)),
+        ("linear_tensorwise", lambda: lm.llmint8_linear_tensorwise(X0, Wqt, sw)),
+    ]
+    for what, call in empty:
+        with pytest.raises(ValueError, match="empty"):
+            call()
+    torch.cuda.synchronize()
+
+
 # --- NaN entries: never an outlier, never a row scale, on every path -----------------------
 
 @pytest.mark.parametrize("M,K,N", [(8, 1024, 136), (32, 1024, 520), (300, 1024, 264)])
