@@ -207,7 +207,7 @@ def llmint8_quantize_rowwise(X: torch.Tensor, idx: torch.Tensor | None = None,
         raise ValueError("idx and count go together")
     M, K = X.shape
     if idx is not None:
-        _need_vec(idx, "idx", torch.int32, 1, exact=False)
+        _need_vec(idx, "idx", torch.int32, K, exact=False)
         _need_vec(count, "count", torch.int32, 1, exact=False)
     Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
     m = torch.empty((M,), dtype=torch.float32, device=X.device)
@@ -405,7 +405,7 @@ def llmint8_quantize_rowwise_fp8(X: torch.Tensor, idx: torch.Tensor | None = Non
         raise ValueError("idx and count go together")
     M, K = X.shape
     if idx is not None:
-        _need_vec(idx, "idx", torch.int32, 1, exact=False)
+        _need_vec(idx, "idx", torch.int32, K, exact=False)
         _need_vec(count, "count", torch.int32, 1, exact=False)
     Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
     m = torch.empty((M,), dtype=torch.float32, device=X.device)

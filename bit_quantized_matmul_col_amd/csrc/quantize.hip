@@ -93,6 +93,109 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
   }
 }
 
+// Public row quantization for K <= 256 * 8 * CPT (CPT 16-byte chunks of a row
+// per thread): block b takes rows R b .. R b + R - 1. A wave's loads complete
+// in issue order, so the outlier count and the first kIdxAhead entries of the
+// list (read whatever the count, from inside the K-entry list) go out first,
+// then the row chunks of all R rows (rows past M re-read row M - 1, chunks
+// past K read chunk 0; both are dropped): the LDS bitmask is built while the
+// rows are in flight, and only list entries past kIdxAhead wait for them. The
+// rows stay in registers between their absmax and their codes; R > 1 builds
+// the bitmask once for R rows.
+constexpr int kRowChunksMax = 4;
+constexpr int kIdxAhead = 2;  // list entries per thread loaded ahead of the rows
+template <class Codec, int R, int CPT>
+__global__ __launch_bounds__(256) void k_rowquant_rows(const uint16_t *__restrict__ X, int64_t M,
+                                                       int64_t K, int64_t ldx,
+                                                       const int32_t *__restrict__ idx,
+                                                       const int32_t *__restrict__ count_ptr,
+                                                       uint8_t *__restrict__ Xq,
+                                                       float *__restrict__ m) {
+  extern __shared__ uint32_t smask[];
+  __shared__ float red[R][4];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * R;
+  const int64_t nch = K / 8;
+  // every load goes out unconditionally from a valid address (a load under a
+  // branch is waited for at once): without a list, X's first bytes stand in
+  const bool has_list = idx != nullptr && count_ptr != nullptr;
+  const int32_t *cp = has_list ? count_ptr : (const int32_t *)X;
+  const int32_t *ip = has_list ? idx : (const int32_t *)X;
+  const int count_word = *cp;
+  int ahead[kIdxAhead];
+#pragma unroll
+  for (int u = 0; u < kIdxAhead; ++u) {
+    const int64_t p = t + 256 * u;
+    ahead[u] = ip[(has_list && p < K) ? p : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 v[R][CPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = (row0 + r < M) ? row0 + r : M - 1;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t ch = t + 256 * j;
+      v[r][j] = *(const u32x4 *)(X + row * ldx + (ch < nch ? ch : 0) * 8);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t kw = (K + 31) / 32;
+  for (int64_t w = t; w < kw; w += 256) smask[w] = 0u;
+  __syncthreads();
+  const int count_raw = has_list ? count_word : 0;
+  const int count = count_raw > K ? (int)K : count_raw;
+#pragma unroll
+  for (int u = 0; u < kIdxAhead; ++u) {
+    const int p = t + 256 * u, k = ahead[u];
+    if (p < count && k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
+  }
+  for (int p = t + 256 * kIdxAhead; p < count; p += 256) {
+    const int k = idx[p];
+    if (k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
+  }
+  __syncthreads();
+
+  unsigned ob[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t ch = t + 256 * j;
+    ob[j] = ch < nch ? chunk_bits(smask, ch) : 0xffu;  // absent chunks count as all outliers
+  }
+  float mx[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    mx[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      float c8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      absmax8(v[r][j], c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((ob[j] >> e) & 1u)) mx[r] = __builtin_fmaxf(mx[r], c8[e]);
+    }
+    mx[r] = wave_max(mx[r]);
+    if (lane == 0) red[r][wv] = mx[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= M) break;
+    const float rm = __builtin_fmaxf(__builtin_fmaxf(red[r][0], red[r][1]),
+                                     __builtin_fmaxf(red[r][2], red[r][3]));
+    if (t == 0) m[row] = rm;
+    const bool zero_row = !(rm > 0.f);
+    const float inv = zero_row ? 0.f : inv_scale_of<Codec>(rm);
+    uint8_t *qrow = Xq + row * K;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t ch = t + 256 * j;
+      if (ch < nch) *(u32x2 *)(qrow + ch * 8) = quant_chunk<Codec>(v[r][j], ob[j], inv, zero_row);
+    }
+  }
+}
+
 // Row quantization inside the layer, row i (one block). Besides Xq and m it
 // gathers the row's outlier entries into xo (position = rank of the column in
 // the ascending outlier list) and, in compaction mode, writes the kept codes
@@ -394,8 +497,30 @@ hipError_t launch_rowquant_idx(const uint16_t *X, int64_t M, int64_t K, int64_t 
                                const int32_t *idx, const int32_t *count, uint8_t *Xq, float *m,
                                hipStream_t stream) {
   const size_t lds = (size_t)((K + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_rowquant_idx<Codec>, dim3((unsigned)M), dim3(256), lds, stream, X, K, ldx,
-                     idx, count, Xq, m);
+  // 16-byte chunks of a row per thread. The register kernel takes rows that
+  // split evenly over the 256 threads: with a ragged split (K = 5120) the
+  // threads past the row's end issue a duplicate load each, and the kernel
+  // measured slower than reading the row twice.
+  const int64_t cpt = (K / 8 + 255) / 256;
+  if (cpt <= kRowChunksMax && (K / 8) % 256 == 0) {
+    // four rows per block at M >= 8192: the bitmask, built once per block from
+    // the outlier list, is then shared by four rows
+    const bool four = M >= 8192;
+    const dim3 grid((unsigned)(four ? (M + 3) / 4 : M));
+    switch ((int)cpt * 2 + (four ? 1 : 0)) {
+#define LLMINT8_ROWS(C, F)                                                                      \
+  case C * 2 + F:                                                                               \
+    hipLaunchKernelGGL((k_rowquant_rows<Codec, F ? 4 : 1, C>), grid, dim3(256), lds, stream, X, \
+                       M, K, ldx, idx, count, Xq, m);                                           \
+    break;
+      LLMINT8_ROWS(1, 0) LLMINT8_ROWS(1, 1) LLMINT8_ROWS(2, 0) LLMINT8_ROWS(2, 1)
+      LLMINT8_ROWS(3, 0) LLMINT8_ROWS(3, 1) LLMINT8_ROWS(4, 0) LLMINT8_ROWS(4, 1)
+#undef LLMINT8_ROWS
+    }
+  } else {
+    hipLaunchKernelGGL(k_rowquant_idx<Codec>, dim3((unsigned)M), dim3(256), lds, stream, X, K,
+                       ldx, idx, count, Xq, m);
+  }
   return hipGetLastError();
 }
 template hipError_t launch_rowquant_idx<CodecI8>(const uint16_t *, int64_t, int64_t, int64_t,

@@ -93,8 +93,9 @@ int llmint8_find_outliers(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, 
  * Row-wise (per-token) quantization of X without its outlier columns
  * (walkthrough page, sections 2.1 and 2.3; codearts page, section 1).
  *   X          [M x K] fp16, leading dimension ldx >= K.
- *   idx, count outlier columns as produced by llmint8_find_outliers (device).
- *              Both NULL means no outlier columns.
+ *   idx, count outlier columns as produced by llmint8_find_outliers (device):
+ *              idx holds K entries (the first *count are used; the call may
+ *              read all K). Both NULL means no outlier columns.
  *   Xq         [M x K] int8 output, leading dimension K; outlier columns are 0.
  *   row_absmax [M] fp32 output: m[i] = max over non-outlier k of |X[i, k]|.
  */

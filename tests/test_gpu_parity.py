@@ -801,6 +801,36 @@ def test_binding_rejects_undersized_buffers(dev):
     assert_y_close(Y.cpu().numpy(), oracle.linear(X, W, 6.0)["Y"], "Y")
 
 
+# the public row quantization's register kernel: rows that split evenly over
+# 256 threads (K a multiple of 2048), one row per block below M = 8192 and four
+# at and above it (a ragged last block included); outlier lists of a few
+# entries, of more than the 512 loaded ahead of the rows (threshold 2), of all
+# K columns (threshold 0), and no list at all
+@pytest.mark.parametrize("M,K", [(1, 2048), (5, 4096), (33, 6144), (64, 8192), (8195, 2048)])
+@pytest.mark.parametrize("threshold", [6.0, 2.0, 0.0, None])
+@pytest.mark.parametrize("codec", ["int8", "fp8"])
+def test_rowwise_register_kernel(dev, M, K, threshold, codec):
+    torch, lm = dev
+    say(f"case rowwise register kernel {codec} M={M} K={K} threshold={threshold}")
+    X, _, _ = workloads.random_case(M, K, 8, seed=M + K, n_out=3)
+    X[M // 2, :] = 0.0  # a zero row
+    Xd = to_gpu(torch, X)
+    quant = lm.llmint8_quantize_rowwise if codec == "int8" else lm.llmint8_quantize_rowwise_fp8
+    if threshold is None:
+        Xq, m = quant(Xd)
+        idx = np.zeros(0, dtype=np.int64)
+    else:
+        idx_d, cnt_d = lm.llmint8_find_outliers(Xd, threshold)
+        Xq, m = quant(Xd, idx_d, cnt_d)
+        idx = oracle.find_outliers(X, threshold)
+        assert int(cnt_d.item()) == idx.size
+    ref_q, ref_m = (oracle.quantize_rowwise(X, idx) if codec == "int8"
+                    else oracle.quantize_rowwise_fp8(X, idx))
+    torch.cuda.synchronize()
+    assert np.array_equal(m.cpu().numpy().view(np.uint32), ref_m.view(np.uint32)), "m differs"
+    assert np.array_equal(Xq.cpu().numpy(), ref_q), "Xq differs"
+
+
 def test_empty_inputs_are_refused_before_any_launch(dev):
     # a zero dimension is an argument error on every entry point (the C calls
     # return LLMINT8_ERR_INVALID_ARG for it): the binding raises ValueError and
