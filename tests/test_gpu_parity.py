@@ -630,6 +630,38 @@ def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None
     return int(cnt.item())
 
 
+@pytest.mark.parametrize("M", [5, 48, 300])
+def test_fp8_product_exact_on_unit_codes(dev, M):
+    # Every X and W code is 0 or +-1 except each row's (column's) absmax 448,
+    # which sits where the other operand is zero: X column b is zero where W
+    # carries its 448s, W row a is zero where X carries its 448s. All products
+    # the MFMA sums are then 0 or +-1, so C is a small integer in any
+    # accumulation order and must equal the oracle's exactly; this pins the
+    # operand layout and k mapping of the E4M3 MFMAs independently of the
+    # rounding bound the general FP8 check allows.
+    torch, lm = dev
+    K, N, a, b = 320, 72, 7, 300
+    say(f"case fp8 product exact on unit codes M={M} K={K} N={N}")
+    rng = np.random.default_rng(M)
+    X = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    W = rng.integers(-1, 2, size=(K, N)).astype(np.float16)
+    X[:, a] = np.float16(448.0) * rng.choice([-1, 1], size=M).astype(np.float16)
+    X[:, b] = 0
+    W[b, :] = np.float16(448.0) * rng.choice([-1, 1], size=N).astype(np.float16)
+    W[a, :] = 0
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq8, s8 = lm.llmint8_quantize_colwise_fp8(Wd)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    lm.llmint8_linear_fp8(Xd, Wq8, s8, Wd, math.inf, C_debug=C)
+    ref = oracle.linear_fp8(X, W, math.inf)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy().astype(np.float64)
+    # the oracle's exact sum is the integer count of matching signs
+    assert np.array_equal(ref["C"], np.rint(ref["C"]))
+    assert np.abs(ref["C"]).max() <= K
+    assert np.array_equal(c, ref["C"]), f"max |C - exact| = {np.abs(c - ref['C']).max()}"
+
+
 # small M (split-K decode kernels, ragged K and N included) and large M
 FP8_CASES = [(1, 256, 136), (5, 4096, 520), (17, 272, 8), (48, 2048, 1032), (64, 1008, 200),
              (65, 784, 136), (257, 784, 520), (300, 1024, 264), (700, 1008, 200)]
