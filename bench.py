@@ -371,6 +371,24 @@ def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8=False):
         r = fn()
         return r, time.perf_counter() - t0
 
+    # one core: the oracle is single-threaded; pin this thread to the first core
+    # it may run on for the timing (restored below)
+    allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    pinned = min(allowed) if allowed else None
+    if pinned is not None:
+        os.sched_setaffinity(0, {pinned})
+    try:
+        return _cpu_baseline_pinned(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8, timed,
+                                    pinned)
+    finally:
+        if allowed:
+            os.sched_setaffinity(0, allowed)
+
+
+def _cpu_baseline_pinned(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8, timed, pinned):
+    import numpy as np
+    import oracle
+
     rows = wl.M if hbm_bound else 4
     Wsub = W if hbm_bound else W[:, :min(W.shape[1], 2048)]
     if fp8:
@@ -423,7 +441,8 @@ def cpu_baseline(wl, X, W, threshold, budget_s, hbm_bound, n_out, fp8=False):
     facts = host_facts()
     return {"value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
             "sample": sample, "seconds": round(elapsed + t_a0, 2), "per_step": per_step,
-            "threads_used": 1, "cpu_model": facts["cpu_model"], "nproc": facts["nproc"]}
+            "threads_used": 1, "pinned_cpu": pinned, "cpu_model": facts["cpu_model"],
+            "nproc": facts["nproc"]}
 
 
 class Layer:
