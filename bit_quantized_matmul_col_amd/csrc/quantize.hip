@@ -490,6 +490,117 @@ __global__ __launch_bounds__(256) void k_colquant(const uint16_t *__restrict__ W
   }
 }
 
+// Column absmax and codes of W [K x N] with one read of W, for K <= 512 * RPT.
+// A block owns a stripe of SC columns (8 or 16: 16 or 32 bytes of every row)
+// and holds all of it in registers: thread (rp, c) keeps rows
+// RPT*rp .. RPT*rp + RPT - 1 of the stripe's 8-column chunk c. The block
+// reduces the stripe's column maxima, codes the values it holds, stages them
+// as the stripe's SC rows of Wq [N x K] in LDS and writes those rows whole.
+// Two blocks fit on a CU (at most 128 registers per thread and 66 KB of LDS
+// each), so one block's loads run while the other codes and writes. Stripes
+// are dealt to the XCDs in contiguous runs (blocks go to the 8 XCDs in turn),
+// so the stripes that share a 128-byte line of W run on one XCD close together
+// in time and the line is fetched from HBM once. Column maxima are the same
+// fmax reduction as the two-pass kernels, so the results are bit-identical.
+constexpr int kStripeRowPhases = 512;
+constexpr int kStripeMaxK = 8192;
+
+template <class Codec, int SC, int RPT>
+__global__ __launch_bounds__(kStripeRowPhases * SC / 8) void k_colwise_stripe(
+    const uint16_t *__restrict__ W, int64_t K, int64_t N, int64_t ldw, float *__restrict__ s,
+    uint8_t *__restrict__ Wq, int64_t stripes, int64_t kp) {
+  constexpr int H = SC / 8;                         // 16-byte chunks per row
+  constexpr int T = kStripeRowPhases * H;           // threads
+  extern __shared__ __attribute__((aligned(16))) uint8_t scode[];  // [SC][kp] codes
+  __shared__ float sred[T / 64][SC];
+  __shared__ float sinv[SC];
+  __shared__ uint8_t szero[SC];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int c = t % H, rp = t / H;
+
+  // stripe of this block: XCD x = blockIdx.x % 8 takes a contiguous run
+  const int64_t bid = blockIdx.x;
+  const int64_t x = bid % 8, q = stripes / 8, rem = stripes % 8;
+  const int64_t n0 = (x * q + (x < rem ? x : rem) + bid / 8) * SC;
+  const int64_t nc = n0 + 8 * c;
+  // K is a multiple of 16, so a thread's RPT rows are all inside K or all past it
+  const bool ok = nc < N && (int64_t)RPT * rp < K;
+
+  // every row load issued up front; a thread past K or N reads rows 0.. of
+  // column 0 instead (a valid address) and its values are dropped
+  u32x4 v[RPT];
+  {
+    const uint16_t *p = W + (ok ? (int64_t)RPT * rp * ldw + nc : 0);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) v[j] = *(const u32x4 *)(p + j * ldw);
+  }
+  float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) absmax8(v[j], mx);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx[e] = ok ? mx[e] : 0.f;
+  // lanes with the same chunk c hold the same 8 columns
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int off = H; off < 64; off <<= 1)
+      mx[e] = __builtin_fmaxf(mx[e], __shfl_xor(mx[e], off, 64));
+  }
+  if (lane < H) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sred[wv][8 * lane + e] = mx[e];
+  }
+  __syncthreads();
+  if (t < SC) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < T / 64; ++w) a = __builtin_fmaxf(a, sred[w][t]);
+    if (n0 + t < N) s[n0 + t] = a;
+    szero[t] = !(a > 0.f);
+    sinv[t] = (a > 0.f) ? inv_scale_of<Codec>(a) : 0.f;
+  }
+  __syncthreads();
+
+  // codes, column by column: the RPT codes of one column are consecutive k
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int nl = 8 * c + e;
+    const float si = sinv[nl];
+    // a zero column codes to 0 whatever it holds (NaN included)
+    const uint32_t keep = szero[nl] ? 0u : 0xffu;
+    uint32_t wd[(RPT + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (RPT + 3) / 4; ++i) wd[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const uint32_t w = v[j][e >> 1];
+      const float xv = (e & 1) ? fp16_hi(w) : fp16_lo(w);
+      wd[j >> 2] |= (Codec::code(xv * si) & keep) << (8 * (j & 3));
+    }
+    uint8_t *dst = scode + (int64_t)nl * kp + (int64_t)RPT * rp;
+    if (ok) {
+      if constexpr (RPT == 16)
+        *(u32x4 *)dst = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      else if constexpr (RPT == 8)
+        *(uint2 *)dst = make_uint2(wd[0], wd[1]);
+      else if constexpr (RPT == 4)
+        *(uint32_t *)dst = wd[0];
+      else
+        *(uint16_t *)dst = (uint16_t)wd[0];
+    }
+  }
+  __syncthreads();
+
+  // the stripe's rows of Wq, 16 bytes per thread and step
+  const int cpr = (int)(K / 16);  // at most 512
+  const int rows = (N - n0 < SC) ? (int)(N - n0) : SC;
+  uint8_t *dst = Wq + n0 * K;
+  for (int qc = t; qc < rows * cpr; qc += T) {
+    const int nl = qc / cpr, kc = qc - nl * cpr;
+    *(u32x4 *)(dst + (int64_t)nl * K + 16 * kc) = *(const u32x4 *)(scode + nl * (int)kp + 16 * kc);
+  }
+}
+
 }  // namespace
 
 template <class Codec>
@@ -577,9 +688,42 @@ template hipError_t launch_colwise_quant<CodecI8>(const uint16_t *, int64_t, int
 template hipError_t launch_colwise_quant<CodecE4M3>(const uint16_t *, int64_t, int64_t, int64_t,
                                                     const float *, uint8_t *, hipStream_t);
 
+template <class Codec, int SC, int RPT>
+hipError_t launch_colwise_stripe(const uint16_t *W, int64_t K, int64_t N, int64_t ldw,
+                                 uint8_t *Wq, float *s, hipStream_t stream) {
+  const int64_t stripes = (N + SC - 1) / SC;
+  const int64_t kp = K + 16;  // row pitch of the staged codes (bank spread)
+  const size_t lds = (size_t)(SC * kp);
+  auto *kern = k_colwise_stripe<Codec, SC, RPT>;
+  hipError_t e =
+      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)stripes), dim3(kStripeRowPhases * SC / 8), lds, stream,
+                     W, K, N, ldw, s, Wq, stripes, kp);
+  return hipGetLastError();
+}
+
+// The memory-side Infinity Cache of the MI355X. A W that fits in it is read
+// by the one-read kernel at 16 or 32 bytes per row without penalty; a larger W
+// comes from HBM, where the two-pass kernels' 1 KB row segments use the DRAM
+// pages better (measured level or faster at 470 MB, slower at <= 141 MB).
+constexpr int64_t kMallBytes = (int64_t)256 << 20;
+
 template <class Codec>
 hipError_t launch_colwise(const uint16_t *W, int64_t K, int64_t N, int64_t ldw, uint8_t *Wq,
                           float *s, hipStream_t stream) {
+  // one read of W while a stripe of K rows fits in the block's registers and
+  // W fits in the Infinity Cache
+  if (K <= kStripeMaxK && 2 * K * N <= kMallBytes) {
+    if (K <= kStripeMaxK / 8)
+      return launch_colwise_stripe<Codec, 16, 2>(W, K, N, ldw, Wq, s, stream);
+    if (K <= kStripeMaxK / 4)
+      return launch_colwise_stripe<Codec, 16, 4>(W, K, N, ldw, Wq, s, stream);
+    if (K <= kStripeMaxK / 2)
+      return launch_colwise_stripe<Codec, 16, 8>(W, K, N, ldw, Wq, s, stream);
+    // 16 rows per thread: 8-column stripes keep two blocks per CU
+    return launch_colwise_stripe<Codec, 8, 16>(W, K, N, ldw, Wq, s, stream);
+  }
   const hipError_t e = launch_colwise_absmax(W, K, N, ldw, s, stream);
   if (e != hipSuccess) return e;
   return launch_colwise_quant<Codec>(W, K, N, ldw, s, Wq, stream);

@@ -587,6 +587,39 @@ def test_fp8_colwise_codes(dev, K, N):
     assert np.array_equal(Wq.cpu().numpy(), ref_q)
 
 
+# Column quantization with one read of W (K <= 8192 and W within the 256 MB
+# Infinity Cache): row counts for 2, 4, 8 and 16 rows per thread, K just past a
+# thread's share, a last 16-column stripe that is half empty (N % 16 == 8),
+# strided W, and above 8192 rows the two-pass kernels (the 70b workload covers
+# them for a W above 256 MB). Each column's maximum sits in its first row, its
+# last row, in the middle, or on a negative entry; one column is zero.
+@pytest.mark.parametrize("K,N,pad", [(16, 8, 0), (1008, 24, 8), (1024, 520, 0),
+                                     (1040, 136, 16), (2064, 264, 0), (4096, 4104, 8),
+                                     (5120, 520, 0), (8192, 1032, 0), (8208, 520, 8)])
+@pytest.mark.parametrize("codec", ["int8", "fp8"])
+def test_colwise_one_read(dev, K, N, pad, codec):
+    torch, lm = dev
+    say(f"case colwise one read {codec} K={K} N={N} pad={pad}")
+    _, W, _ = workloads.random_case(4, K, N, seed=K + N)
+    W[:, 0] = 0.0
+    W[0, 1] = 3.0
+    W[K - 1, 2] = -5.0
+    W[K // 2, N - 1] = 7.0
+    W[K - 1, N - 2] = 9.0
+    Wd_big = torch.zeros((K, N + pad), dtype=torch.float16, device="cuda")
+    Wd_big[:, :N] = to_gpu(torch, W)
+    Wv = Wd_big[:, :N]
+    if codec == "int8":
+        Wq, s = lm.llmint8_quantize_colwise(Wv)
+        ref_q, ref_s = oracle.quantize_colwise(W)
+    else:
+        Wq, s = lm.llmint8_quantize_colwise_fp8(Wv)
+        ref_q, ref_s = oracle.quantize_colwise_fp8(W)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(Wq.cpu().numpy().view(np.uint8), ref_q.view(np.uint8))
+
+
 def check_fp8_layer(torch, lm, X, W, threshold, rows=None, ref_w=None, bias=None, ycmax=False):
     M, K = X.shape
     N = W.shape[1]
