@@ -29,6 +29,30 @@ __device__ inline unsigned chunk_bits(const uint32_t *mask, int64_t ch) {
   return (mask[ch >> 2] >> ((ch & 3) * 8)) & 0xffu;
 }
 
+// Bits of the outlier list entries p0 + t, p0 + t + 256, ... below count set
+// in the LDS bitmask (256 threads). Four entries per thread are loaded before
+// any is used, so a long list costs few round trips. The loads go through a
+// buffer resource over the K-entry list (32-bit offsets, fewer registers;
+// entries past K read as 0 and are not used).
+__device__ inline void list_to_mask(const int32_t *__restrict__ idx, int count, int64_t K,
+                                    int p0, uint32_t *smask) {
+  constexpr int kBatch = 4;
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)idx, (short)0, (int)(K * 4), 0x00020000);
+  for (int b = p0; b < count; b += 256 * kBatch) {
+    int k[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      k[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (b + t + 256 * u), 0, 0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = b + t + 256 * u;
+      if (p < count && k[u] >= 0 && k[u] < K) atomicOr(&smask[k[u] >> 5], 1u << (k[u] & 31));
+    }
+  }
+}
+
 // Codes of the 8 fp16 of a chunk, outlier columns (and a zero row) zeroed,
 // packed little-endian.
 template <class Codec>
@@ -64,10 +88,7 @@ __global__ __launch_bounds__(256) void k_rowquant_idx(const uint16_t *__restrict
   __syncthreads();
   int count = count_ptr ? *count_ptr : 0;
   if (count > K) count = (int)K;
-  for (int p = t; p < count; p += 256) {
-    const int k = idx[p];
-    if (k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
-  }
+  list_to_mask(idx, count, K, 0, smask);
   __syncthreads();
 
   const uint16_t *row = X + i * ldx;
@@ -150,10 +171,7 @@ __global__ __launch_bounds__(256) void k_rowquant_rows(const uint16_t *__restric
     const int p = t + 256 * u, k = ahead[u];
     if (p < count && k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
   }
-  for (int p = t + 256 * kIdxAhead; p < count; p += 256) {
-    const int k = idx[p];
-    if (k >= 0 && k < K) atomicOr(&smask[k >> 5], 1u << (k & 31));
-  }
+  list_to_mask(idx, count, K, 256 * kIdxAhead, smask);
   __syncthreads();
 
   unsigned ob[CPT];
