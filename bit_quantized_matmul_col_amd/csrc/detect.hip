@@ -71,6 +71,7 @@ __global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restri
   }
 }
 
+template <int KB>
 __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restrict__ pmask,
                                                         int row_chunks, int64_t K, int64_t kw,
                                                         DetectOut out) {
@@ -95,20 +96,20 @@ __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restri
   } else {
     for (int64_t w = t; w < kw; w += 1024) smask[w] = 0u;
     __syncthreads();
-    // OR the row-chunk masks: every thread issues a batch of independent loads,
-    // then merges the non-zero words (rare) into LDS.
-    constexpr int kBatch = 8;
+    // OR the row-chunk masks: every thread issues a batch of KB independent
+    // loads (the launch sizes KB so that one batch covers all the words), then
+    // merges the non-zero words (rare) into LDS. Words past the end read as
+    // zero through the buffer resource.
     const int64_t total_words = (int64_t)row_chunks * kw;
-    for (int64_t base = 0; base < total_words; base += 1024 * kBatch) {
-      uint32_t v[kBatch];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)pmask, (short)0, (int)(total_words * 4), 0x00020000);
+    for (int64_t base = 0; base < total_words; base += 1024 * KB) {
+      uint32_t v[KB];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int64_t q = base + t + 1024 * u;
-        const uint32_t x = pmask[q < total_words ? q : 0];
-        v[u] = q < total_words ? x : 0u;
-      }
+      for (int u = 0; u < KB; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(4 * (base + t + 1024 * u)), 0, 0);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < KB; ++u)
         if (v[u]) atomicOr(&smask[(base + t + 1024 * u) % kw], v[u]);
     }
     __syncthreads();
@@ -166,9 +167,12 @@ DetectPlan detect_plan(int64_t M, int64_t K) {
   DetectPlan p;
   p.kw = (K + 31) / 32;
   p.col_tiles = (int)((K + kTileCols - 1) / kTileCols);
-  // Aim for >= 8 rows per block phase and at most kMaxRowChunks partial masks.
+  // Aim for >= 8 rows per block phase and at most kMaxRowChunks partial masks
+  // (twice that from M = 8192: more blocks in flight on the long scans, for
+  // the price of a larger merge).
   int64_t chunks = (M + 31) / 32;
-  if (chunks > kMaxRowChunks) chunks = kMaxRowChunks;
+  const int64_t max_chunks = M >= 8192 ? 2 * kMaxRowChunks : kMaxRowChunks;
+  if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
   p.rows_per_chunk = (int)((M + chunks - 1) / chunks);
   p.row_chunks = (int)((M + p.rows_per_chunk - 1) / p.rows_per_chunk);
@@ -184,9 +188,19 @@ hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, f
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_detect_finish, dim3(1), dim3(1024), (size_t)plan.kw * 4, stream,
-                     (const uint32_t *)out.pmask,
-                     plan.row_chunks, K, plan.kw, out);
+  // one batch of partial-mask loads per thread covers all the words
+  const int64_t words = out.xcmax ? 0 : (int64_t)plan.row_chunks * plan.kw;
+  const size_t lds = (size_t)plan.kw * 4;
+  const uint32_t *pm = (const uint32_t *)out.pmask;
+  if (words <= 1024 * 8)
+    hipLaunchKernelGGL(k_detect_finish<8>, dim3(1), dim3(1024), lds, stream, pm, plan.row_chunks,
+                       K, plan.kw, out);
+  else if (words <= 1024 * 16)
+    hipLaunchKernelGGL(k_detect_finish<16>, dim3(1), dim3(1024), lds, stream, pm,
+                       plan.row_chunks, K, plan.kw, out);
+  else
+    hipLaunchKernelGGL(k_detect_finish<32>, dim3(1), dim3(1024), lds, stream, pm,
+                       plan.row_chunks, K, plan.kw, out);
   return hipGetLastError();
 }
 
