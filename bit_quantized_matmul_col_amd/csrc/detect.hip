@@ -5,7 +5,7 @@
 // sections 2.3 and 4.2). HBM-bound: X is read once, 2MK bytes.
 //
 // Pass 1 (k_detect_partial): a block owns 512 columns (64 lanes x one 16-byte
-// chunk of 8 fp16) of one row chunk; its 4 waves stride over the chunk's rows,
+// chunk of 8 fp16) of one row chunk; its 8 waves stride over the chunk's rows,
 // so every wave load is a fully coalesced 1 KB row segment. The running column
 // maxima are compared with the threshold once at the end (max >= t is the same
 // test as "some entry >= t") and stored as 16 mask words per row chunk.
@@ -22,33 +22,34 @@ namespace {
 
 constexpr int kTileCols = 512;
 constexpr int kMaxRowChunks = 64;
+constexpr int kRowPhases = 8;  // waves per detection block, each on every 8th row
 
-__global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restrict__ X, int64_t M,
-                                                        int64_t K, int64_t ldx, float threshold,
-                                                        int rows_per_chunk, int64_t kw,
-                                                        uint32_t *__restrict__ pmask) {
+__global__ __launch_bounds__(64 * kRowPhases) void k_detect_partial(
+    const uint16_t *__restrict__ X, int64_t M, int64_t K, int64_t ldx, float threshold,
+    int rows_per_chunk, int64_t kw, uint32_t *__restrict__ pmask) {
   const int t = threadIdx.x;
   const int c = t & 63;   // 16-byte chunk within the tile
-  const int rp = t >> 6;  // row phase 0..3
+  const int rp = t >> 6;  // row phase 0 .. kRowPhases - 1
   const int64_t col = (int64_t)blockIdx.x * kTileCols + (int64_t)c * 8;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
   const int64_t r1 = (r0 + rows_per_chunk < M) ? r0 + rows_per_chunk : M;
+  constexpr int P = kRowPhases;
 
   float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (col < K) {
     const uint16_t *p = X + col;
     int64_t r = r0 + rp;
-    for (; r + 12 < r1; r += 16) {
+    for (; r + 3 * P < r1; r += 4 * P) {
       u32x4 v0 = *(const u32x4 *)(p + r * ldx);
-      u32x4 v1 = *(const u32x4 *)(p + (r + 4) * ldx);
-      u32x4 v2 = *(const u32x4 *)(p + (r + 8) * ldx);
-      u32x4 v3 = *(const u32x4 *)(p + (r + 12) * ldx);
+      u32x4 v1 = *(const u32x4 *)(p + (r + P) * ldx);
+      u32x4 v2 = *(const u32x4 *)(p + (r + 2 * P) * ldx);
+      u32x4 v3 = *(const u32x4 *)(p + (r + 3 * P) * ldx);
       absmax8(v0, mx);
       absmax8(v1, mx);
       absmax8(v2, mx);
       absmax8(v3, mx);
     }
-    for (; r < r1; r += 4) absmax8(*(const u32x4 *)(p + r * ldx), mx);
+    for (; r < r1; r += P) absmax8(*(const u32x4 *)(p + r * ldx), mx);
   }
   unsigned bits = 0;
   if (col < K && rp < r1 - r0) {
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restri
     for (int e = 0; e < 8; ++e)
       if (mx[e] >= threshold) bits |= 1u << e;
   }
-  __shared__ uint8_t sb[4][64];
+  __shared__ uint8_t sb[P][64];
   sb[rp][c] = (uint8_t)bits;
   __syncthreads();
   if (t < kTileCols / 32) {
@@ -64,7 +65,10 @@ __global__ __launch_bounds__(256) void k_detect_partial(const uint16_t *__restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ch = 4 * t + j;
-      word |= (uint32_t)(sb[0][ch] | sb[1][ch] | sb[2][ch] | sb[3][ch]) << (8 * j);
+      uint32_t b = 0;
+#pragma unroll
+      for (int q = 0; q < P; ++q) b |= sb[q][ch];
+      word |= b << (8 * j);
     }
     const int64_t w = (int64_t)blockIdx.x * (kTileCols / 32) + t;
     if (w < kw) pmask[(int64_t)blockIdx.y * kw + w] = word;
@@ -167,12 +171,9 @@ DetectPlan detect_plan(int64_t M, int64_t K) {
   DetectPlan p;
   p.kw = (K + 31) / 32;
   p.col_tiles = (int)((K + kTileCols - 1) / kTileCols);
-  // Aim for >= 8 rows per block phase and at most kMaxRowChunks partial masks
-  // (twice that from M = 8192: more blocks in flight on the long scans, for
-  // the price of a larger merge).
+  // Aim for >= 4 rows per block phase and at most kMaxRowChunks partial masks.
   int64_t chunks = (M + 31) / 32;
-  const int64_t max_chunks = M >= 8192 ? 2 * kMaxRowChunks : kMaxRowChunks;
-  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks > kMaxRowChunks) chunks = kMaxRowChunks;
   if (chunks < 1) chunks = 1;
   p.rows_per_chunk = (int)((M + chunks - 1) / chunks);
   p.row_chunks = (int)((M + p.rows_per_chunk - 1) / p.rows_per_chunk);
@@ -183,7 +184,8 @@ hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, f
                          const DetectPlan &plan, const DetectOut &out, hipStream_t stream) {
   // a caller-supplied column absmax replaces the scan of X
   if (!out.xcmax) {
-    hipLaunchKernelGGL(k_detect_partial, dim3(plan.col_tiles, plan.row_chunks), dim3(256), 0,
+    hipLaunchKernelGGL(k_detect_partial, dim3(plan.col_tiles, plan.row_chunks),
+                       dim3(64 * kRowPhases), 0,
                        stream, X, M, K, ldx, threshold, plan.rows_per_chunk, plan.kw, out.pmask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
