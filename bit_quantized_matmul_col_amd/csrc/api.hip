@@ -26,7 +26,8 @@ int64_t pitch_o(int64_t K) { return (K + 63) / 64 * 64; }
 
 // Offsets (bytes) of the regions a call carves out of its workspace.
 struct Layout {
-  size_t pmask, omask, wprefix, idx, count, xq, m, xo, wqc, wot, part, total;
+  size_t pmask, omask, wprefix, idx, count, xq, m, xo, wqc, wot, part, sem, kpart, kpart_bytes,
+      total;
 };
 
 // Small-M layer calls: preparation outputs, split-K partial sums, counters.
@@ -46,7 +47,10 @@ Layout make_decode_layout(int64_t M, int64_t K, int64_t N) {
   return L;
 }
 
-Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefill = false) {
+// split: room for the large-M GEMM's split-K tiles (int8 layer calls that may
+// allocate; the FP8 layer and the allocation-free call run without them).
+Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefill = false,
+                   bool split = false) {
   if (layer && M <= kDecodeMaxM && !any_m_prefill) return make_decode_layout(M, K, N);
   const DetectPlan p = detect_plan(M, K);
   Layout L{};
@@ -73,6 +77,14 @@ Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefi
     o += up((size_t)N * ldq);
     L.wot = o;
     o += up((size_t)N * ldo * 2);
+    const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1};
+    if (sp.ksplit > 1) {
+      L.sem = o;
+      o += up((size_t)sp.tiles * 4);
+      L.kpart = o;
+      L.kpart_bytes = (size_t)sp.tiles * (size_t)sp.ksplit * (size_t)kSplitSlotBytes;
+      o += up(L.kpart_bytes);
+    }
   }
   L.total = o;
   return L;
@@ -137,8 +149,13 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
   int8_t *wqc = (int8_t *)(ws + L.wqc);
   const bool int8w = ep.int8w != 0;
 
+  // split-K tiles only on int8 calls whose layout has room for them
+  const bool split = L.kpart_bytes > 0 && !fp8;
+  uint32_t *sem = split ? (uint32_t *)(ws + L.sem) : nullptr;
+  int32_t *kpart = split ? (int32_t *)(ws + L.kpart) : nullptr;
+  const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1};
   DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
-              wprefix, idx, count, outlier_count_out};
+              wprefix, idx, count, outlier_count_out, sem, sp.tiles};
   const int64_t ldq = pitch_q(K), ldo = pitch_o(K);
   uint16_t *wot = (uint16_t *)(ws + L.wot);
   hipError_t e = launch_detect(X, M, K, ldx, threshold, plan, d, s);
@@ -152,7 +169,8 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
     // the GEMM's outlier product runs when it has weight rows (gathered above)
     const uint16_t *wo_src = (Wf || int8w) ? wot : nullptr;
     GemmArgs g{xq, Wq, wqc, m, col_absmax, xo, wot, wo_src ? (const uint16_t *)wot : nullptr,
-               count, Y, C_debug, M, N, K, ldq, ldo, ldw, ldy, ep, fp8 ? 1 : 0};
+               count, Y, C_debug, M, N, K, ldq, ldo, ldw, ldy, ep, fp8 ? 1 : 0, 0,
+               kpart, sem, split ? (int64_t)L.kpart_bytes : 0, 1};
     e = launch_gemm(g, ev, s);
   }
   return e;
@@ -222,7 +240,7 @@ LLMINT8_EXPORT int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_
 
 LLMINT8_EXPORT size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || K > LLMINT8_MAX_K) return 0;
-  return make_layout(M, K, N, true).total;
+  return make_layout(M, K, N, true, false, true).total;
 }
 
 namespace {
@@ -258,8 +276,8 @@ int run_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, const int8_
                const float *col_absmax, const uint16_t *W, int64_t ldw, int64_t N,
                float threshold, uint16_t *Y, int64_t ldy, int32_t *outlier_count_out,
                int32_t *C_debug, void *workspace, size_t workspace_bytes, hipStream_t s,
-               const llmint8_linear_opts &o) {
-  const Layout L = make_layout(M, K, N, true);
+               const llmint8_linear_opts &o, bool split) {
+  const Layout L = make_layout(M, K, N, true, false, split);
   if (!workspace || workspace_bytes < L.total) return LLMINT8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LLMINT8_ERR_UNSUPPORTED;
 
@@ -340,7 +358,7 @@ LLMINT8_EXPORT int llmint8_linear_ex(const uint16_t *X, int64_t M, int64_t K, in
   if (st) return st;
   return run_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
                     outlier_count_out, C_debug, workspace, workspace_bytes, (hipStream_t)stream,
-                    o);
+                    o, true);
 }
 
 LLMINT8_EXPORT int llmint8_linear_noalloc(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
@@ -357,7 +375,8 @@ LLMINT8_EXPORT int llmint8_linear_noalloc(const uint16_t *X, int64_t M, int64_t 
   void *ws = nullptr;
   if ((st = scratch_of((hipStream_t)stream, &ws))) return st;
   return run_linear(X, M, K, ldx, Wq, col_absmax, W, ldw, N, threshold, Y, ldy,
-                    outlier_count_out, C_debug, ws, kScratchBytes, (hipStream_t)stream, o);
+                    outlier_count_out, C_debug, ws, kScratchBytes, (hipStream_t)stream, o,
+                    false);
 }
 
 LLMINT8_EXPORT size_t llmint8_quantize_tensorwise_workspace_size(int64_t K, int64_t N) {

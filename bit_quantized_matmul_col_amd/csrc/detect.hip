@@ -83,6 +83,8 @@ __global__ __launch_bounds__(1024) void k_detect_finish(const uint32_t *__restri
   const int t = threadIdx.x;
   if (out.ycmax)  // the epilogue's column maxima start from zero
     for (int64_t n = t; n < out.N; n += 1024) out.ycmax[n] = 0.f;
+  if (out.sem)  // so do the split-K GEMM's arrival counters
+    for (int64_t i = t; i < out.nsem; i += 1024) out.sem[i] = 0u;
   if (out.xcmax) {
     // outlier bits straight from the caller's column absmax of X
     for (int64_t w = t; w < kw; w += 1024) {

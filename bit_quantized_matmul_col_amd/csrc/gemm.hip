@@ -53,6 +53,40 @@ int64_t wide_columns(int64_t M, int64_t N, int cus) {
   return tail_blocks <= cus ? n1 : 0;
 }
 
+// Fewest 128-byte stages of k that a split-K part runs, and most parts. A part
+// hands its int32 sums over through memory (256 KB per part, stored and read
+// back by the last part); with fewer than 16 stages per part that costs about
+// what the split saves.
+constexpr int64_t kSplitMinStages = 16;
+constexpr int kSplitMax = 8;
+
+}  // namespace
+
+// The tiles a split-K launch cuts. When a launch has fewer 256x256 tiles than
+// CUs (M up to a few hundred rows), most of the chip would idle: every tile
+// then cuts its k range into as many parts as the CUs take (at most kSplitMax,
+// each at least kSplitMinStages stages). A partial last wave of a larger
+// launch is left to the paired launch (its 128x256 tail tiles measured faster
+// than 256x256 tiles split in two: 115 against 124 us at 2048x4096x11008,
+// 298 against 314 us at 4096x5120x13824). The plan is a function of the shape
+// alone (the MI355X's 256 CUs, not a device query), so the workspace size
+// query and the launch agree.
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t K, int64_t N) {
+  GemmSplitPlan p{0, 1};
+  constexpr int64_t cus = 256;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= cus) return p;
+  int64_t S = cus / tiles;
+  if (S > kSplitMax) S = kSplitMax;
+  while (S > 1 && (K + 127) / 128 < S * kSplitMinStages) --S;
+  if (S < 2) return p;
+  p.tiles = tiles;
+  p.ksplit = (int)S;
+  return p;
+}
+
+namespace {
+
 // The same GEMM restricted to output columns [n0, n0 + ncols).
 GemmArgs column_slice(const GemmArgs &a, int64_t n0, int64_t ncols) {
   GemmArgs b = a;
@@ -84,6 +118,13 @@ hipError_t launch_gemm_wide(const GemmArgs &a, const GemmEvents &ev, hipStream_t
 hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream) {
   GemmArgs a = args;
   if (a.ldc == 0) a.ldc = a.N;
+  if (a.part && a.sem && !a.fp8) {
+    const GemmSplitPlan p = gemm_split_plan(a.M, a.K, a.N);
+    if (p.ksplit > 1 && p.tiles * p.ksplit * kSplitSlotBytes <= a.part_bytes) {
+      a.ksplit = p.ksplit;
+      return launch_gemm_split(a, ev, stream);
+    }
+  }
   const int cus = cu_count();
   if (narrow_tiles(a.M, a.N, cus)) return launch_gemm_narrow(a, ev, stream);
   const int64_t n1 = wide_columns(a.M, a.N, cus);

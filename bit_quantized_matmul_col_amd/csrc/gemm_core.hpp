@@ -100,11 +100,15 @@ struct OperandTile {
   int bytes;            // bytes from base to the end of the matrix rows in the tile
   int voff[G];
 
-  __device__ void init(const void *mat, int64_t ld_bytes, int64_t row0, int64_t nrows) {
+  // k0: the first byte of k the tile reads (the start of a split-K range, a
+  // multiple of the stage size); the resource still ends at the end of the
+  // last row, so whatever lies past it reads as zero as before.
+  __device__ void init(const void *mat, int64_t ld_bytes, int64_t row0, int64_t nrows,
+                       int64_t k0 = 0) {
     int64_t rows = nrows - row0;
     rows = rows < ROWS ? rows : ROWS;
-    base = (const uint8_t *)mat + row0 * ld_bytes;
-    bytes = (int)(rows * ld_bytes);
+    base = (const uint8_t *)mat + row0 * ld_bytes + k0;
+    bytes = (int)(rows * ld_bytes - k0);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -374,11 +378,71 @@ __device__ inline void kloop(uint8_t *smem, const OperandTile<BM, NW, SK> &A,
   __syncthreads();  // every wave is done with the ring before it is reused
 }
 
+// Split-K handoff of one 256 x 256 tile. Every split stores its int32 sums in
+// its own slot of a.part (register r of thread t at word r * TH + t, so each
+// store instruction of a wave writes 256 contiguous bytes) and counts itself
+// in a.sem[tile]. The split that arrives last adds the other slots to its own
+// sums (exact integers, so the order does not matter) and returns true: it
+// finishes the tile. The others return false. Nothing waits for another block.
+// The slots are written and read with agent-scope atomic stores and loads
+// (coherent across the XCDs' L2 caches), and every wave waits for its stores
+// to complete before the block counts itself, so no fence is needed: an
+// agent-scope fence would write back and invalidate the whole L2 of the XCD,
+// costing the other blocks there their staged operand lines.
+template <int TH, int NACC>
+__device__ inline bool split_merge(const GemmArgs &a, int64_t tile, int split, i32x16 *acc) {
+  constexpr int R = NACC * 16;  // int32 sums per thread
+  const int t = threadIdx.x;
+  const int S = a.ksplit;
+  int32_t *slots = a.part + tile * (int64_t)S * R * TH;
+  int32_t *mine = slots + (int64_t)split * R * TH;
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __hip_atomic_store(mine + (i * 16 + r) * TH + t, acc[i][r], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's sums are stored
+  __shared__ int s_last;
+  __syncthreads();
+  if (t == 0)
+    s_last = __hip_atomic_fetch_add(a.sem + tile, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+  __syncthreads();
+  if (!s_last) return false;
+  for (int sp = 0; sp < S; ++sp) {
+    if (sp == split) continue;
+    const int32_t *other = slots + (int64_t)sp * R * TH;
+    // four accumulator blocks (64 loads) in flight at a time
+#pragma unroll
+    for (int i0 = 0; i0 < NACC; i0 += 4) {
+      i32x16 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          v[i][r] = (i0 + i < NACC) ? __hip_atomic_load(other + ((i0 + i) * 16 + r) * TH + t,
+                                                        __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i0 + i < NACC) acc[i0 + i] += v[i];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  return true;
+}
+
 // One output tile: block bid of the launch's tiles for a. F8: the operands are
 // E4M3 codes (fp32 sums, dequantized by 1 / 448^2) instead of int8 codes
 // (int32 sums, 1 / 127^2).
-template <int BM, int BN, int NWN, int SK, bool DBG, bool F8>
+// SPLIT: the launch holds a.ksplit blocks per tile, block bid taking k range
+// bid / tiles of the tile bid % tiles (so each split's blocks keep the
+// XCD-aware tile order); the last split to finish runs the epilogue.
+template <int BM, int BN, int NWN, int SK, bool DBG, bool F8, bool SPLIT = false>
 __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uint8_t *smem) {
+  static_assert(!SPLIT || (BM == 256 && BN == 256 && !F8), "split-K: int8 256 x 256 tiles");
   using T = TileCfg<BM, BN, NWN, SK>;
   constexpr int NW = T::NW, TH = T::THREADS;
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
@@ -390,7 +454,10 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uin
   const int wm = wv / NWN, wn = wv % NWN;
   const int li = lane & 31, lg = lane >> 5;
   int64_t tm, tn;
-  tile_of_block(bid, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, tm, tn);
+  const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  const int64_t tile = SPLIT ? bid % (tiles_m * tiles_n) : bid;
+  const int split = SPLIT ? (int)(bid / (tiles_m * tiles_n)) : 0;
+  tile_of_block(tile, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int count = *a.count;
@@ -419,15 +486,22 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uin
     for (int ni = 0; ni < NI; ++ni) acc[mi * NI + ni] = (i32x16){};
 
   {
+    // stages [st0, st1) of the k range: all of them, or this split's share
+    const int64_t nst = (Kl + SK - 1) / SK;
+    const int64_t st0 = SPLIT ? nst * split / a.ksplit : 0;
+    const int64_t st1 = SPLIT ? nst * (split + 1) / a.ksplit : nst;
     OperandTile<BM, NW, SK> A;
     OperandTile<BN, NW, SK> B;
-    A.init(a.xq, a.ldq, m0, a.M);
+    A.init(a.xq, a.ldq, m0, a.M, st0 * SK);
     if (compact)
-      B.init(a.wqc, a.ldq, n0, a.N);
+      B.init(a.wqc, a.ldq, n0, a.N, st0 * SK);
     else
-      B.init(a.wq, a.K, n0, a.N);
+      B.init(a.wq, a.K, n0, a.N, st0 * SK);
     kloop<BM, BN, WM, WN, MI, NI, T::NST, NW, SK, F8 ? Op::F8 : Op::I8>(
-        smem, A, B, (Kl + SK - 1) / SK, wm, wn, li, lg, acc);
+        smem, A, B, st1 - st0, wm, wn, li, lg, acc);
+  }
+  if constexpr (SPLIT) {
+    if (!split_merge<TH, MI * NI>(a, tile, split, acc)) return;
   }
 
   // dequantize in place: C * m[i] * s[n] / 127^2 (or / 448^2)
@@ -534,6 +608,26 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_pair(GemmArgs a1, GemmArg
     prefill_tile<BM1, BN1, NWN, SK, DBG, F8>(a1, b, (uint8_t *)smem_v);
   else
     prefill_tile<BM2, BN2, NWN, SK, DBG, F8>(a2, b - blocks1, (uint8_t *)smem_v);
+}
+
+// Split-K 256 x 256 int8 tiles: a.ksplit blocks per tile.
+template <int NWN, int SK, bool DBG>
+__global__ __launch_bounds__(128 * NWN, 1) void k_gemm_split(GemmArgs a) {
+  extern __shared__ u32x4 smem_v[];
+  prefill_tile<256, 256, NWN, SK, DBG, false, true>(a, blockIdx.x, (uint8_t *)smem_v);
+}
+
+template <int NWN, int SK, bool DBG>
+hipError_t launch_split(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
+  using T = TileCfg<256, 256, NWN, SK>;
+  auto *kern = k_gemm_split<NWN, SK, DBG>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.ksplit;
+  hipExtLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::THREADS), T::LDS, stream,
+                        (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
+  return hipGetLastError();
 }
 
 template <int BM1, int BN1, int BM2, int BN2, int NWN, int SK, bool DBG, bool F8>

@@ -44,6 +44,8 @@ struct DetectOut {
   int32_t *idx;      // [K] ascending outlier columns
   int32_t *count;    // [1]
   int32_t *count_copy;  // optional second copy of the count
+  uint32_t *sem;        // optional [nsem] arrival counters of the split-K GEMM, zeroed here
+  int64_t nsem;
 };
 
 hipError_t launch_detect(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
@@ -129,7 +131,26 @@ struct GemmArgs {
   EpilogueOpts ep;
   int fp8;               // xq and wq hold E4M3 codes instead of int8 ones
   int64_t ldc;           // row pitch of cdbg (0: N)
+  // Split-K tiles (int8 only; null part: never split). Each part of a tile
+  // stores its int32 sums in one slot of part and counts itself in sem[tile];
+  // the last to arrive adds the other slots and runs the epilogue. sem must be
+  // zero when the GEMM starts.
+  int32_t *part;         // [tiles x ksplit slots of kSplitSlotBytes each]
+  uint32_t *sem;         // [tiles] arrival counters
+  int64_t part_bytes;    // bytes available at part
+  int ksplit;            // set by the launcher on the split-K tiles
 };
+
+// Bytes of one split's int32 partial sums of a 256 x 256 tile.
+constexpr int64_t kSplitSlotBytes = (int64_t)256 * 256 * 4;
+
+// Split-K plan of the large-M GEMM: each of its `tiles` 256 x 256 tiles cuts
+// its k range into ksplit parts (ksplit = 1: whole tiles, no split).
+struct GemmSplitPlan {
+  int64_t tiles;
+  int ksplit;
+};
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t K, int64_t N);
 
 // Caller-supplied events (may be null) that the GEMM kernel's own dispatch
 // stamps when the kernel starts and when it ends.
@@ -146,6 +167,7 @@ hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStrea
 hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_pair(const GemmArgs &a1, const GemmArgs &a2, const GemmEvents &ev,
                             hipStream_t stream);
+hipError_t launch_gemm_split(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream);
 
 // Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
 // its slice of X itself.

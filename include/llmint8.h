@@ -119,7 +119,10 @@ int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ld
  *              int32 accumulators of step 4.
  *   workspace  device scratch of at least llmint8_workspace_size(M, K, N) bytes.
  * When the outlier share is large, the int8 GEMM runs over the K - |O| kept
- * columns only (compacted operands); the result is identical either way.
+ * columns only (compacted operands); when M > 64 and the 256 x 256 output
+ * tiles number fewer than the GPU's 256 CUs, each tile's k range is split
+ * into parts whose int32 sums meet in the workspace. The result is identical
+ * either way.
  */
 size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N);
 int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
@@ -136,9 +139,11 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
  * Its workspace is a static device array of LLMINT8_NOALLOC_SCRATCH_BYTES
  * (32 MiB) inside the library, one per GPU, held until the process ends; its
  * address is looked up on the first call on each device (the only HIP call
- * besides the launches). A call whose llmint8_workspace_size(M, K, N) exceeds
- * that size returns LLMINT8_ERR_WORKSPACE before any HIP call: in practice
- * this covers the small-M (decode) shapes, M <= 64. Every call on one GPU
+ * besides the launches). It never splits the k range of its GEMM tiles, so
+ * it needs llmint8_workspace_size(M, K, N) less the split-K area; a call
+ * whose need exceeds the scratch returns LLMINT8_ERR_WORKSPACE before any HIP
+ * call: in practice this covers the small-M (decode) shapes, M <= 64, and
+ * small large-M ones. Every call on one GPU
  * shares its scratch, so calls that may overlap on one GPU (different
  * streams, or host threads without ordering) race; order them on one stream.
  * Nothing in the scratch needs to start at zero: every call writes what it

@@ -23,6 +23,7 @@ CASES = [
     ("int8", 32, 1024, 520, True),   # split-K small M
     ("int8", 8, 1024, 264, False),   # single kernel
     ("int8", 300, 1024, 520, True),  # large M
+    ("int8", 300, 4096, 520, True),  # large M, split-K tiles (arrival counters reset per call)
     ("fp8", 32, 1024, 520, False),
     ("fp8", 300, 512, 264, True),
 ]

@@ -772,6 +772,81 @@ def test_gemm_split_into_wide_and_narrow_launches(dev, variant):
     assert np.array_equal(ycm.cpu().numpy(), np.abs(y.astype(np.float32)).max(axis=0))
 
 
+# --- split-K tiles of the large-M GEMM -------------------------------------------------
+# With fewer 256 x 256 tiles than CUs, every tile cuts its k range into parts
+# (at least 16 stages of 128 bytes each, at most 8 parts) that run on the idle
+# CUs; each part stores its int32 sums and the last to finish adds them and runs
+# the epilogue. C must stay bit-exact and Y within tolerance.
+SPLIT_CASES = [
+    # M, K, N, threshold, planted outliers: what the case covers
+    (300, 8192, 520, 6.0, 3),     # 6 tiles in 4 parts of 16 stages; ragged M and N
+    (520, 4112, 264, 6.0, 2),     # 6 tiles in 2 parts of 16 and 17 stages; K not a multiple of 128
+    (1100, 4096, 1032, 3.0, 4),   # compacted k (about 30 % outliers): 25 tiles, 2 parts of ~12 stages
+    (300, 4096, 264, 0.0, 0),     # every column an outlier: no int8 stage in any part
+    (300, 4096, 264, math.inf, 0),  # no outlier: no fp16 product
+    (100, 16384, 264, 6.0, 2),    # 2 tiles in 8 parts
+]
+
+
+@pytest.mark.parametrize("M,K,N,threshold,n_out", SPLIT_CASES)
+def test_split_k_tiles(dev, M, K, N, threshold, n_out):
+    torch, lm = dev
+    say(f"case split-K tiles M={M} K={K} N={N} threshold={threshold} n_out={n_out}")
+    X, W, _ = workloads.random_case(M, K, N, seed=M + K + N, n_out=n_out)
+    run_all(torch, lm, X, W, threshold)
+
+
+@pytest.mark.parametrize("mode", ["int8_weights", "bias_ycmax"])
+def test_split_k_tiles_options(dev, mode):
+    torch, lm = dev
+    M, K, N = 600, 4096, 776  # 3 x 4 tiles in 2 parts of 16 stages
+    say(f"case split-K tiles with options {mode} M={M} K={K} N={N}")
+    X, W, _ = workloads.random_case(M, K, N, seed=23, n_out=3)
+    Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    if mode == "int8_weights":
+        Y = lm.llmint8_linear(Xd, Wq, s, None, 6.0, C_debug=C, outlier_weights="int8")
+        ref = oracle.linear(X, W, 6.0, outlier_weights="int8")
+        ycm = None
+    else:
+        b = (np.random.default_rng(5).standard_normal(N) * 0.5).astype(np.float16)
+        ycm = torch.full((N,), 1e30, dtype=torch.float32, device="cuda")
+        Y = lm.llmint8_linear(Xd, Wq, s, Wd, 6.0, C_debug=C, bias=to_gpu(torch, b),
+                              y_col_absmax=ycm)
+        ref = oracle.linear(X, W, 6.0, bias=b)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref["C"]), "C differs"
+    y = Y.cpu().numpy()
+    assert_y_close(y, ref["Y"], "Y")
+    if ycm is not None:
+        assert np.array_equal(ycm.cpu().numpy(), np.abs(y.astype(np.float32)).max(axis=0))
+
+
+def test_split_k_tiles_repeat_bit_identical(dev):
+    """The arrival counters are reset by every call: back-to-back calls on one
+    workspace give the same bits, and a call of another shape in between does
+    not disturb them."""
+    torch, lm = dev
+    X, W, _ = workloads.random_case(300, 8192, 520, seed=41, n_out=3)
+    X2, W2, _ = workloads.random_case(520, 4112, 264, seed=42, n_out=2)
+    Xd, Wd, X2d, W2d = (to_gpu(torch, a) for a in (X, W, X2, W2))
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    Wq2, s2 = lm.llmint8_quantize_colwise(W2d)
+    ws = torch.empty(max(lm.llmint8_workspace_size(300, 8192, 520),
+                         lm.llmint8_workspace_size(520, 4112, 264)), dtype=torch.uint8,
+                     device="cuda")
+    ys = []
+    for _ in range(3):
+        ys.append(lm.llmint8_linear(Xd, Wq, s, Wd, 6.0, workspace=ws).clone())
+        lm.llmint8_linear(X2d, Wq2, s2, W2d, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    ref = oracle.linear(X, W, 6.0)
+    assert_y_close(ys[0].cpu().numpy(), ref["Y"], "Y")
+
+
 # --- seeded random shapes ----------------------------------------------------------
 
 def _random_shapes(n, seed):

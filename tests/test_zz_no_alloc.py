@@ -48,10 +48,12 @@ def both(torch, lm, M, K, N, seed, threshold=6.0):
 
 # pairs of consecutive calls, the second smaller: split-K small M (two K
 # splits and more), the single kernel (M <= 16, K in {1024, 2048, 4096}), and
-# a large-M call whose workspace fits in the scratch
+# a large-M call whose workspace fits in the scratch (the last pair: one that
+# the workspace call runs with split-K tiles and the scratch call without)
 PAIRS = [((64, 4096, 4096), (20, 1024, 520)),
          ((16, 4096, 11008), (3, 1024, 136)),
          ((300, 1024, 520), (70, 256, 64)),
+         ((300, 4096, 520), (70, 256, 64)),
          ((48, 8192, 4096), (1, 16, 8))]
 
 
