@@ -19,8 +19,8 @@ def _library(built_library):
 def test_every_kernel_reported():
     res = json.load(open(RES))
     names = " ".join(res)
-    for k in ("k_gemm_prefill", "k_decode_gemm", "k_decode_fused", "k_detect_partial",
-              "k_layer_prep", "k_colquant", "k_quant_tensor"):
+    for k in ("k_gemm_prefill", "k_gemm_pair", "k_gemm_split", "k_decode_gemm", "k_decode_fused",
+              "k_detect_partial", "k_layer_prep", "k_colquant", "k_quant_tensor"):
         assert k in names, k
 
 
