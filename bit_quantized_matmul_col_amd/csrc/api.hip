@@ -77,12 +77,12 @@ Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefi
     o += up((size_t)N * ldq);
     L.wot = o;
     o += up((size_t)N * ldo * 2);
-    const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1};
+    const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1, 256};
     if (sp.ksplit > 1) {
       L.sem = o;
       o += up((size_t)sp.tiles * 4);
       L.kpart = o;
-      L.kpart_bytes = (size_t)sp.tiles * (size_t)sp.ksplit * (size_t)kSplitSlotBytes;
+      L.kpart_bytes = (size_t)sp.tiles * (size_t)sp.ksplit * (size_t)split_slot_bytes(sp.bm);
       o += up(L.kpart_bytes);
     }
   }
@@ -153,7 +153,7 @@ hipError_t prefill_layer(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, c
   const bool split = L.kpart_bytes > 0 && !fp8;
   uint32_t *sem = split ? (uint32_t *)(ws + L.sem) : nullptr;
   int32_t *kpart = split ? (int32_t *)(ws + L.kpart) : nullptr;
-  const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1};
+  const GemmSplitPlan sp = split ? gemm_split_plan(M, K, N) : GemmSplitPlan{0, 1, 256};
   DetectOut d{o.x_col_absmax, threshold, o.y_col_absmax, N, (uint32_t *)(ws + L.pmask), omask,
               wprefix, idx, count, outlier_count_out, sem, sp.tiles};
   const int64_t ldq = pitch_q(K), ldo = pitch_o(K);

@@ -62,27 +62,33 @@ constexpr int kSplitMax = 8;
 
 }  // namespace
 
-// The tiles a split-K launch cuts. When a launch has fewer 256x256 tiles than
-// CUs (M up to a few hundred rows), most of the chip would idle: every tile
-// then cuts its k range into as many parts as the CUs take (at most kSplitMax,
-// each at least kSplitMinStages stages). A partial last wave of a larger
-// launch is left to the paired launch (its 128x256 tail tiles measured faster
-// than 256x256 tiles split in two: 115 against 124 us at 2048x4096x11008,
-// 298 against 314 us at 4096x5120x13824). The plan is a function of the shape
-// alone (the MI355X's 256 CUs, not a device query), so the workspace size
-// query and the launch agree.
+// The tiles a split-K launch cuts. When a launch has fewer tiles than CUs (M
+// up to several hundred rows at these widths), most of the chip would idle:
+// every tile then cuts its k range into as many parts as the CUs take (at most
+// kSplitMax, each at least kSplitMinStages stages). The tiles are 128 x 256
+// when that gives a split (a three-stage ring, and no zero rows below M = 128),
+// else 256 x 256. Measured on whole calls (best of six interleaved rounds),
+// 256 x 256 split tiles against whole ones: 128 x 8192 x 8192 78.4 -> 56.8 us,
+// 512 x 8192 x 8192 86.0 -> 72.6 us; 128 x 256 against 256 x 256 split tiles:
+// 65 x 4096 x 4096 45.6 -> 33.9 us, 256 x 4096 x 4096 47.2 -> 34.9 us,
+// 512 x 8192 x 8192 71.2 -> 62.1 us, 1024 x 4096 x 4096 53.8 -> 44.8 us. A
+// partial last wave of a larger launch is left to the paired launch (its
+// 128 x 256 tail tiles measured faster than 256 x 256 tiles split in two: 115
+// against 124 us at 2048 x 4096 x 11008, 298 against 314 us at
+// 4096 x 5120 x 13824). The plan is a function of the shape alone (the
+// MI355X's 256 CUs, not a device query), so the workspace size query and the
+// launch agree.
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t K, int64_t N) {
-  GemmSplitPlan p{0, 1};
   constexpr int64_t cus = 256;
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles >= cus) return p;
-  int64_t S = cus / tiles;
-  if (S > kSplitMax) S = kSplitMax;
-  while (S > 1 && (K + 127) / 128 < S * kSplitMinStages) --S;
-  if (S < 2) return p;
-  p.tiles = tiles;
-  p.ksplit = (int)S;
-  return p;
+  for (const int bm : {128, 256}) {
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
+    if (tiles >= cus) continue;
+    int64_t S = cus / tiles;
+    if (S > kSplitMax) S = kSplitMax;
+    while (S > 1 && (K + 127) / 128 < S * kSplitMinStages) --S;
+    if (S >= 2) return GemmSplitPlan{tiles, (int)S, bm};
+  }
+  return GemmSplitPlan{0, 1, 256};
 }
 
 namespace {
@@ -120,9 +126,9 @@ hipError_t launch_gemm(const GemmArgs &args, const GemmEvents &ev, hipStream_t s
   if (a.ldc == 0) a.ldc = a.N;
   if (a.part && a.sem && !a.fp8) {
     const GemmSplitPlan p = gemm_split_plan(a.M, a.K, a.N);
-    if (p.ksplit > 1 && p.tiles * p.ksplit * kSplitSlotBytes <= a.part_bytes) {
+    if (p.ksplit > 1 && p.tiles * p.ksplit * split_slot_bytes(p.bm) <= a.part_bytes) {
       a.ksplit = p.ksplit;
-      return launch_gemm_split(a, ev, stream);
+      return launch_gemm_split(a, p.bm, ev, stream);
     }
   }
   const int cus = cu_count();

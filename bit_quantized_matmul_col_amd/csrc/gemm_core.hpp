@@ -442,7 +442,8 @@ __device__ inline bool split_merge(const GemmArgs &a, int64_t tile, int split, i
 // XCD-aware tile order); the last split to finish runs the epilogue.
 template <int BM, int BN, int NWN, int SK, bool DBG, bool F8, bool SPLIT = false>
 __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uint8_t *smem) {
-  static_assert(!SPLIT || (BM == 256 && BN == 256 && !F8), "split-K: int8 256 x 256 tiles");
+  static_assert(!SPLIT || ((BM == 256 || BM == 128) && BN == 256 && !F8),
+                "split-K: int8 256 x 256 or 128 x 256 tiles");
   using T = TileCfg<BM, BN, NWN, SK>;
   constexpr int NW = T::NW, TH = T::THREADS;
   constexpr int MI = T::MI, NI = T::NI, WM = T::WM, WN = T::WN;
@@ -610,21 +611,21 @@ __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_pair(GemmArgs a1, GemmArg
     prefill_tile<BM2, BN2, NWN, SK, DBG, F8>(a2, b - blocks1, (uint8_t *)smem_v);
 }
 
-// Split-K 256 x 256 int8 tiles: a.ksplit blocks per tile.
-template <int NWN, int SK, bool DBG>
+// Split-K BM x 256 int8 tiles: a.ksplit blocks per tile.
+template <int BM, int NWN, int SK, bool DBG>
 __global__ __launch_bounds__(128 * NWN, 1) void k_gemm_split(GemmArgs a) {
   extern __shared__ u32x4 smem_v[];
-  prefill_tile<256, 256, NWN, SK, DBG, false, true>(a, blockIdx.x, (uint8_t *)smem_v);
+  prefill_tile<BM, 256, NWN, SK, DBG, false, true>(a, blockIdx.x, (uint8_t *)smem_v);
 }
 
-template <int NWN, int SK, bool DBG>
+template <int BM, int NWN, int SK, bool DBG>
 hipError_t launch_split(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream) {
-  using T = TileCfg<256, 256, NWN, SK>;
-  auto *kern = k_gemm_split<NWN, SK, DBG>;
+  using T = TileCfg<BM, 256, NWN, SK>;
+  auto *kern = k_gemm_split<BM, NWN, SK, DBG>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
-  const int64_t blocks = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.ksplit;
+  const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + 255) / 256) * a.ksplit;
   hipExtLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::THREADS), T::LDS, stream,
                         (hipEvent_t)ev.begin, (hipEvent_t)ev.end, 0u, a);
   return hipGetLastError();

@@ -135,20 +135,21 @@ struct GemmArgs {
   // stores its int32 sums in one slot of part and counts itself in sem[tile];
   // the last to arrive adds the other slots and runs the epilogue. sem must be
   // zero when the GEMM starts.
-  int32_t *part;         // [tiles x ksplit slots of kSplitSlotBytes each]
+  int32_t *part;         // [tiles x ksplit slots of split_slot_bytes(bm) each]
   uint32_t *sem;         // [tiles] arrival counters
   int64_t part_bytes;    // bytes available at part
   int ksplit;            // set by the launcher on the split-K tiles
 };
 
-// Bytes of one split's int32 partial sums of a 256 x 256 tile.
-constexpr int64_t kSplitSlotBytes = (int64_t)256 * 256 * 4;
+// Bytes of one part's int32 sums of a bm x 256 tile.
+inline int64_t split_slot_bytes(int bm) { return (int64_t)bm * 256 * 4; }
 
-// Split-K plan of the large-M GEMM: each of its `tiles` 256 x 256 tiles cuts
+// Split-K plan of the large-M GEMM: each of its `tiles` bm x 256 tiles cuts
 // its k range into ksplit parts (ksplit = 1: whole tiles, no split).
 struct GemmSplitPlan {
   int64_t tiles;
   int ksplit;
+  int bm;
 };
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t K, int64_t N);
 
@@ -167,7 +168,7 @@ hipError_t launch_gemm_wide(const GemmArgs &args, const GemmEvents &ev, hipStrea
 hipError_t launch_gemm_narrow(const GemmArgs &args, const GemmEvents &ev, hipStream_t stream);
 hipError_t launch_gemm_pair(const GemmArgs &a1, const GemmArgs &a2, const GemmEvents &ev,
                             hipStream_t stream);
-hipError_t launch_gemm_split(const GemmArgs &a, const GemmEvents &ev, hipStream_t stream);
+hipError_t launch_gemm_split(const GemmArgs &a, int bm, const GemmEvents &ev, hipStream_t stream);
 
 // Small-M (decode) path: a detection kernel and a split-K GEMM that quantizes
 // its slice of X itself.

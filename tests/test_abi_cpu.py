@@ -191,6 +191,8 @@ res["ws_size_70b"] = L.llmint8_workspace_size(8192, 8192, 28672)
 res["ws_fp8_70b"] = L.llmint8_linear_fp8_workspace_size(8192, 8192, 28672)
 res["ws_size_6tiles"] = L.llmint8_workspace_size(300, 8192, 520)
 res["ws_fp8_6tiles"] = L.llmint8_linear_fp8_workspace_size(300, 8192, 520)
+res["ws_size_768"] = L.llmint8_workspace_size(768, 8192, 8192)
+res["ws_fp8_768"] = L.llmint8_linear_fp8_workspace_size(768, 8192, 8192)
 res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
 res["find_ws_ok"] = L.llmint8_find_outliers_workspace_size(8192, 8192)
 res["find_ws_bad"] = L.llmint8_find_outliers_workspace_size(8, 133160)
@@ -249,17 +251,19 @@ def test_invalid_arguments_are_rejected_before_any_hip_call():
     assert res["ltw_ws"] >= 2048 * 4096 + 2048 * 4 + 11008 * 4 and res["ltw_ws_bad"] == 0
     # FP8 layer: the same layouts as the int8 layer
     assert res["ws_fp8_small_m"] == res["ws_int8_small_m"] > 0
-    # Large M: when a launch has fewer 256 x 256 tiles than the 256 CUs, the
-    # int8 layer also holds the split-K GEMM's arrival counters (256-byte
-    # aligned) and one 256 KB slot of int32 sums per part of each tile.
-    # 300 x 8192 x 520: 6 tiles in 4 parts of 16 stages of 128 bytes of k. The
-    # 7B prefill (344 tiles), 13b and 70b shapes have no split.
-    def split_room(tiles, parts):
-        return (tiles * 4 + 255) // 256 * 256 + tiles * parts * 256 * 256 * 4
+    # Large M: when a launch has fewer tiles than the 256 CUs, the int8 layer
+    # also holds the split-K GEMM's arrival counters (256-byte aligned) and one
+    # slot of int32 sums per part of each tile (bm x 256 x 4 bytes).
+    # 300 x 8192 x 520: 3 x 3 tiles of 128 x 256 in 4 parts of 16 stages of 128
+    # bytes of k. The 7B prefill, 13b and 70b shapes have no split.
+    def split_room(tiles, parts, bm=128):
+        return (tiles * 4 + 255) // 256 * 256 + tiles * parts * bm * 256 * 4
     assert res["ws_size_prefill"] == res["ws_fp8_prefill"]
     assert res["ws_size_13b"] == res["ws_fp8_13b"]
     assert res["ws_size_70b"] == res["ws_fp8_70b"]
-    assert res["ws_size_6tiles"] - res["ws_fp8_6tiles"] == split_room(6, 4)
+    assert res["ws_size_6tiles"] - res["ws_fp8_6tiles"] == split_room(9, 4)
+    # 768 x 8192 x 8192: 192 tiles of 128 x 256 do not split, 96 of 256 x 256 do (2 parts)
+    assert res["ws_size_768"] - res["ws_fp8_768"] == split_room(96, 2, 256)
 
 
 def test_status_strings():

@@ -97,7 +97,7 @@ def test_outliers_and_row_pass(dev, M, K, fp8):
 # tiles, and large M with K-compaction (threshold 0: every column an outlier)
 LAYER = [(8, 1024, 136, 6.0), (33, 1024, 264, 6.0), (300, 1040, 520, 6.0),
          (400, 1024, 264, 0.0), (48, 2048, 72, math.inf),
-         # split-K tiles of the large-M GEMM (int8): 6 and 4 tiles in 2 parts
+         # split-K tiles of the large-M GEMM (int8): 9 and 8 tiles of 128 rows in 2 parts
          (300, 4096, 520, 6.0), (400, 4096, 264, 0.0)]
 
 

@@ -773,18 +773,22 @@ def test_gemm_split_into_wide_and_narrow_launches(dev, variant):
 
 
 # --- split-K tiles of the large-M GEMM -------------------------------------------------
-# With fewer 256 x 256 tiles than CUs, every tile cuts its k range into parts
-# (at least 16 stages of 128 bytes each, at most 8 parts) that run on the idle
-# CUs; each part stores its int32 sums and the last to finish adds them and runs
-# the epilogue. C must stay bit-exact and Y within tolerance.
+# With fewer tiles than CUs, every tile cuts its k range into parts (at least
+# 16 stages of 128 bytes each, at most 8 parts) that run on the idle CUs; each
+# part stores its int32 sums and the last to finish adds them and runs the
+# epilogue. The tiles are 128 x 256 when that gives a split, else 256 x 256.
+# C must stay bit-exact and Y within tolerance.
 SPLIT_CASES = [
     # M, K, N, threshold, planted outliers: what the case covers
-    (300, 8192, 520, 6.0, 3),     # 6 tiles in 4 parts of 16 stages; ragged M and N
-    (520, 4112, 264, 6.0, 2),     # 6 tiles in 2 parts of 16 and 17 stages; K not a multiple of 128
-    (1100, 4096, 1032, 3.0, 4),   # compacted k (about 30 % outliers): 25 tiles, 2 parts of ~12 stages
+    (300, 8192, 520, 6.0, 3),     # 3 x 3 tiles of 128 rows in 4 parts of 16 stages; ragged M and N
+    (520, 4112, 264, 6.0, 2),     # 5 x 2 tiles in 2 parts of 16 and 17 stages; K not a multiple of 128
+    (1100, 4096, 1032, 3.0, 4),   # compacted k (about 30 % outliers): 45 tiles, 2 parts of ~12 stages
     (300, 4096, 264, 0.0, 0),     # every column an outlier: no int8 stage in any part
     (300, 4096, 264, math.inf, 0),  # no outlier: no fp16 product
     (100, 16384, 264, 6.0, 2),    # 2 tiles in 8 parts
+    (65, 4096, 520, 6.0, 2),      # one row past the small-M path: 3 tiles of 128 rows
+    (768, 4096, 2056, 6.0, 3),    # 6 x 9 = 54 tiles of 128 rows in 2 parts (4 would leave 8 stages each)
+    (768, 8192, 8192, 6.0, 3),    # 192 tiles of 128 rows do not split: 96 of 256 rows in 2 parts
 ]
 
 
@@ -799,7 +803,7 @@ def test_split_k_tiles(dev, M, K, N, threshold, n_out):
 @pytest.mark.parametrize("mode", ["int8_weights", "bias_ycmax"])
 def test_split_k_tiles_options(dev, mode):
     torch, lm = dev
-    M, K, N = 600, 4096, 776  # 3 x 4 tiles in 2 parts of 16 stages
+    M, K, N = 600, 4096, 776  # 5 x 4 tiles of 128 rows in 2 parts of 16 stages
     say(f"case split-K tiles with options {mode} M={M} K={K} N={N}")
     X, W, _ = workloads.random_case(M, K, N, seed=23, n_out=3)
     Xd, Wd = to_gpu(torch, X), to_gpu(torch, W)
