@@ -33,6 +33,8 @@ constexpr int kSubK = 512;         // k bytes staged per GEMM stage
 constexpr int kXPitch = kSubK + 16;
 constexpr int kPmaxUnroll = 8;     // detection partials per thread loaded up front
 constexpr int kTargetBlocks = 256; // GEMM blocks aimed for (one per CU)
+constexpr int kOnePassBlocks = 768;  // most blocks for K ranges of at most two stages
+constexpr int kWideBlocks = 512;     // blocks aimed for when that does not fit
 constexpr int kMaxSplits = 16;
 constexpr int kListWords = 256;    // mask words scanned per epilogue window
 constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
@@ -595,16 +597,35 @@ hipError_t launch_decode_kernels(const DecodeGemmArgs &gemm, const DecodePlan &p
 }  // namespace
 
 DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
-  (void)M;
   DecodePlan p;
   p.tiles = (int)((N + kTileN - 1) / kTileN);
   p.det_blocks = (int)((K + kDetCols - 1) / kDetCols);
   // K splits: a power of two, about kTargetBlocks blocks in all, and at least
   // one full stage of K per split
-  int kb = 1;
-  while (kb < kMaxSplits && (int64_t)p.tiles * (kb * 2) <= kTargetBlocks &&
-         K / (kb * 2) >= kSubK)
-    kb *= 2;
+  auto splits_for = [&](int64_t target) {
+    int b = 1;
+    while (b < kMaxSplits && (int64_t)p.tiles * (b * 2) <= target && K / (b * 2) >= kSubK)
+      b *= 2;
+    return b;
+  };
+  int kb = splits_for(kTargetBlocks);
+  // A K range of at most two stages issues all of its loads before its first
+  // wait; a longer one streams through two register stages, one ahead. With
+  // more than 16 rows, when the ranges are longer than that, split further if
+  // it takes at most kOnePassBlocks blocks, else aim for kWideBlocks blocks.
+  // Measured under graph replay (same weights each call): 64x4096x11008
+  // 35.7 -> 25.8 us, 32x4096x11008 22.7 -> 20.0 us (one-pass ranges);
+  // 32x5120x13824 28.2 -> 25.7 us, 48x8192x4096 22.1 -> 21.1 us (more
+  // blocks); splitting 32x11008x4096 into one-pass ranges (1024 blocks) took
+  // 31.7 us against 24.7, and with one or two rows the extra splits cost
+  // more than they gain (1x12288x1032 13.8 -> 15.5 us).
+  if (M > 16 && (K + kb - 1) / kb > 2 * kSubK) {
+    int b = kb;
+    while (b < kMaxSplits && (K + b - 1) / b > 2 * kSubK) b *= 2;
+    kb = ((K + b - 1) / b <= 2 * kSubK && (int64_t)p.tiles * b <= kOnePassBlocks)
+             ? b
+             : splits_for(kWideBlocks);
+  }
   int64_t kc = (K + kb - 1) / kb;
   kc = (kc + 63) / 64 * 64;
   p.kc = kc;
