@@ -54,7 +54,7 @@ FP16_PEAK_TFLOPS = 2500.0
 # 256 CUs x 2.4 GHz x 8192
 INT8_OPS_PER_CU_CLOCK = 8192
 HBM_BOUND = ("tiny", "decode")
-DECODE_MAX_M = 64  # row count up to which the library takes its small-M path
+DECODE_MAX_M = 128  # rows up to which the library may take its small-M path (65-128: shape-dependent)
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources of the GEMM kernels whose HBM counters are committed: the split-K
 # small-M kernels (up to 64 rows; the single-kernel path runs none of the
@@ -66,7 +66,7 @@ KERNEL_SOURCES = {
     "large_m": [os.path.join(_CSRC, f) for f in
                 ("common.hpp", "internal.hpp", "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")],
 }
-SMALL_M_MAX = 64  # rows up to which the layer runs the small-M kernels
+SMALL_M_MAX = 128  # rows up to which the layer runs the small-M kernels
 # the larger workloads measured by default next to the headline one
 SWEEP = (("prefill", (6.0,)), ("13b", (6.0,)), ("70b", (6.0, 4.0, math.inf)))
 

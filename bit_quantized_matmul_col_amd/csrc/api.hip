@@ -51,7 +51,7 @@ Layout make_decode_layout(int64_t M, int64_t K, int64_t N) {
 // allocate; the FP8 layer and the allocation-free call run without them).
 Layout make_layout(int64_t M, int64_t K, int64_t N, bool layer, bool any_m_prefill = false,
                    bool split = false) {
-  if (layer && M <= kDecodeMaxM && !any_m_prefill) return make_decode_layout(M, K, N);
+  if (layer && !any_m_prefill && use_decode_path(M, K, N)) return make_decode_layout(M, K, N);
   const DetectPlan p = detect_plan(M, K);
   Layout L{};
   size_t o = 0;
@@ -294,7 +294,7 @@ int run_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, const int8_
                       threshold, o.x_col_absmax, ep};
     return hip_status(launch_decode_fused(f, ev, s));
   }
-  if (M <= kDecodeMaxM) {
+  if (use_decode_path(M, K, N)) {
     const DecodePlan dp = decode_plan(M, K, N);
     const int64_t kw = (K + 31) / 32;
     uint32_t *omask = (uint32_t *)(ws + L.omask);
@@ -529,7 +529,7 @@ LLMINT8_EXPORT int llmint8_linear_fp8(const uint16_t *X, int64_t M, int64_t K, i
   const EpilogueOpts ep{0, o.bias, o.y_col_absmax};
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  if (M <= kDecodeMaxM) {
+  if (use_decode_path(M, K, N)) {
     const DecodePlan dp = decode_plan(M, K, N);
     const int64_t kw = (K + 31) / 32;
     uint32_t *omask = (uint32_t *)(ws + L.omask);

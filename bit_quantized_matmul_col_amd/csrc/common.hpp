@@ -33,8 +33,10 @@ __host__ __device__ inline bool use_compaction(int count, int64_t K, int64_t M) 
   return count > 0 && K <= kCompactMaxK && M * (int64_t)count * 16 > 5000 * (2 * K - count);
 }
 
-// Row count up to which the layer takes the small-M (decode) path.
-constexpr int kDecodeMaxM = 64;
+// Row count up to which the layer takes the small-M (decode) path, and the
+// rows of one of its row groups (a GEMM block covers one group).
+constexpr int kDecodeMaxM = 128;
+constexpr int kDecodeGroupRows = 64;
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }

@@ -1,6 +1,6 @@
 // Small-M (decode-shaped) path of the LLM.int8() linear layer on gfx950.
 //
-// With M <= 64 rows the layer is bound by streaming the int8 weight Wq from
+// With M <= 128 rows the layer is bound by streaming the int8 weight Wq from
 // HBM (the decode regime of the INT8-vs-FP8 page, section one: every step
 // re-reads all weights). The path is three kernels. None communicates across
 // blocks inside a kernel (on gfx950 each XCD has its own L2, so an agent-scope
@@ -150,16 +150,17 @@ struct DecodeStage {
   bool kok;              // column k0 + 8 lane lies inside the K range
 };
 
+// r0: the first row of the block's row group (rows past M read row 0).
 template <int MB>
 __device__ inline void decode_load_x(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
-                                     int64_t k_end, int wv, int lane) {
+                                     int64_t k_end, int r0, int wv, int lane) {
   const int64_t kx = k0 + 8 * lane;
   st.kok = kx < k_end;
   const int64_t kxc = st.kok ? kx : 0;
   st.mw = a.omask[kxc >> 5];
 #pragma unroll
   for (int u = 0; u < 4 * MB; ++u) {
-    const int row = wv + 4 * u;
+    const int row = r0 + wv + 4 * u;
     st.x[u] = *(const u32x4 *)(a.X + (int64_t)(row < a.M ? row : 0) * a.ldx + kxc);
   }
 }
@@ -176,8 +177,9 @@ __device__ inline void decode_load_b(DecodeStage<MB> &st, int64_t k0, int64_t k_
 
 template <int MB>
 __device__ inline void decode_load(const DecodeGemmArgs &a, DecodeStage<MB> &st, int64_t k0,
-                                   int64_t k_end, const int8_t *brow, int wv, int lane, int g) {
-  decode_load_x<MB>(a, st, k0, k_end, wv, lane);
+                                   int64_t k_end, const int8_t *brow, int r0, int wv, int lane,
+                                   int g) {
+  decode_load_x<MB>(a, st, k0, k_end, r0, wv, lane);
   decode_load_b<MB>(st, k0, k_end, brow, g);
 }
 
@@ -271,7 +273,9 @@ __device__ inline void decode_step(const DecodeStage<MB> &st, uint8_t *sx, const
 // any count, two register stages alternate so that the next stage's loads are
 // in flight while the current one is quantized and contracted. No load is
 // issued under a branch that the following waits would have to merge.
-template <int MB, int NST, bool F8>
+// RG: the launch has row groups (M > 64); without them the block covers rows
+// 0 .. M - 1 and the group arithmetic folds away.
+template <int MB, int NST, bool F8, bool RG>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   constexpr int kStageBytes = MB * 16 * kXPitch;
   __shared__ __attribute__((aligned(16))) uint8_t sx[(NST == 2 ? 2 : 1) * kStageBytes];
@@ -286,9 +290,15 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   const int64_t k_end = (k_begin + a.kc < K) ? k_begin + a.kc : K;
   const int64_t ncol = n0 + wv * 16 + c16;
   const int8_t *brow = a.wq + ((ncol < a.N) ? ncol : a.N - 1) * K;
+  // row group: rows r0 .. r0 + 63 (the blocks of the groups of one tile and
+  // K split are 256 or more block ids apart, a multiple of the 8 XCDs, so they
+  // run on one XCD and its L2 serves the second read of their Wq bytes)
+  const int r0 = RG ? kDecodeGroupRows * (int)blockIdx.z : 0;
+  const int mg = !RG ? (int)a.M
+                     : (a.M - r0 < kDecodeGroupRows) ? (int)(a.M - r0) : kDecodeGroupRows;
 
-  // detection partials of row `lane`, blocks wv + 4 i (first kPmaxUnroll up front)
-  const int prow = lane < a.M ? lane : 0;
+  // detection partials of row r0 + `lane`, blocks wv + 4 i (first kPmaxUnroll up front)
+  const int prow = lane < mg ? r0 + lane : 0;
   float pv[kPmaxUnroll];
 #pragma unroll
   for (int i = 0; i < kPmaxUnroll; ++i) {
@@ -301,12 +311,12 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   if constexpr (NST == 2) {
     // both X stages ahead of the Wq bytes: loads complete in issue order, so
     // the X codes of both stages can be formed while Wq is still streaming
-    decode_load_x<MB>(a, s0, k_begin, k_end, wv, lane);
-    decode_load_x<MB>(a, s1, k_begin + kSubK, k_end, wv, lane);
+    decode_load_x<MB>(a, s0, k_begin, k_end, r0, wv, lane);
+    decode_load_x<MB>(a, s1, k_begin + kSubK, k_end, r0, wv, lane);
     decode_load_b<MB>(s0, k_begin, k_end, brow, g);
     decode_load_b<MB>(s1, k_begin + kSubK, k_end, brow, g);
   } else {
-    decode_load<MB>(a, s0, k_begin, k_end, brow, wv, lane, g);
+    decode_load<MB>(a, s0, k_begin, k_end, brow, r0, wv, lane, g);
   }
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first wait
 
@@ -320,8 +330,8 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   if (t < 64) {
     const float mx = __builtin_fmaxf(__builtin_fmaxf(spart[0][t], spart[1][t]),
                                      __builtin_fmaxf(spart[2][t], spart[3][t]));
-    sinv[t] = (t < a.M && mx > 0.f) ? (F8 ? inv_scale_of<CodecE4M3>(mx) : inv_scale(mx)) : 0.f;
-    if (kb == 0 && blockIdx.x == 0 && t < a.M) a.m[t] = mx;
+    sinv[t] = (t < mg && mx > 0.f) ? (F8 ? inv_scale_of<CodecE4M3>(mx) : inv_scale(mx)) : 0.f;
+    if (kb == 0 && blockIdx.x == 0 && t < mg) a.m[r0 + t] = mx;
   }
 
   i32x4 acc[MB];
@@ -342,13 +352,13 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
     int64_t k0 = k_begin;
     int i = 0;
     for (; i + 2 < nst; i += 2, k0 += 2 * kSubK) {  // stages i + 1 and i + 2 exist
-      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
+      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, r0, wv, lane, g);
       decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
-      decode_load<MB>(a, s0, k0 + 2 * kSubK, k_end, brow, wv, lane, g);
+      decode_load<MB>(a, s0, k0 + 2 * kSubK, k_end, brow, r0, wv, lane, g);
       decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
     }
     if (nst - i == 2) {
-      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, wv, lane, g);
+      decode_load<MB>(a, s1, k0 + kSubK, k_end, brow, r0, wv, lane, g);
       decode_step<MB, F8>(s0, sx, sinv, acc, wv, lane, c16, g);
       decode_step<MB, F8>(s1, sx, sinv, acc, wv, lane, c16, g);
     } else {
@@ -366,8 +376,9 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = mb * 16 + 4 * g + r;
-        if (row < a.M)
-          __builtin_nontemporal_store(acc[mb][r], &a.part[((int64_t)kb * a.M + row) * a.N + ncol]);
+        if (row < mg)
+          __builtin_nontemporal_store(acc[mb][r],
+                                      &a.part[((int64_t)kb * a.M + r0 + row) * a.N + ncol]);
       }
   }
 }
@@ -550,21 +561,28 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   }
 }
 
+template <int MB, bool F8, bool RG>
+hipError_t launch_decode_gemm_rg(const DecodeGemmArgs &a, int tiles, int kb, const GemmEvents &ev,
+                                 hipStream_t stream) {
+  const int64_t nst = (a.kc + kSubK - 1) / kSubK;
+  const hipEvent_t b = (hipEvent_t)ev.begin, e = (hipEvent_t)ev.end;
+  const dim3 grid(tiles, kb, (unsigned)((a.M + kDecodeGroupRows - 1) / kDecodeGroupRows));
+  if (nst == 1)
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 1, F8, RG>), grid, dim3(256), 0, stream, b, e, 0u, a);
+  else if (nst == 2)
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 2, F8, RG>), grid, dim3(256), 0, stream, b, e, 0u, a);
+  else
+    hipExtLaunchKernelGGL((k_decode_gemm<MB, 0, F8, RG>), grid, dim3(256), 0, stream, b, e, 0u, a);
+  return hipGetLastError();
+}
+
 template <int MB, bool F8>
 hipError_t launch_decode_gemm(const DecodeGemmArgs &a, int tiles, int kb, const GemmEvents &ev,
                               hipStream_t stream) {
-  const int64_t nst = (a.kc + kSubK - 1) / kSubK;
-  const hipEvent_t b = (hipEvent_t)ev.begin, e = (hipEvent_t)ev.end;
-  if (nst == 1)
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 1, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
-                          0u, a);
-  else if (nst == 2)
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 2, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
-                          0u, a);
-  else
-    hipExtLaunchKernelGGL((k_decode_gemm<MB, 0, F8>), dim3(tiles, kb), dim3(256), 0, stream, b, e,
-                          0u, a);
-  return hipGetLastError();
+  if constexpr (MB == kDecodeGroupRows / 16) {
+    if (a.M > kDecodeGroupRows) return launch_decode_gemm_rg<MB, F8, true>(a, tiles, kb, ev, stream);
+  }
+  return launch_decode_gemm_rg<MB, F8, false>(a, tiles, kb, ev, stream);
 }
 
 template <int KB, bool F8>
@@ -578,7 +596,9 @@ template <bool F8>
 hipError_t launch_decode_kernels(const DecodeGemmArgs &gemm, const DecodePlan &plan,
                                  const GemmEvents &ev, hipStream_t stream) {
   hipError_t e;
-  switch ((int)((gemm.M + 15) / 16)) {
+  // MB 16-row blocks cover one row group
+  const int64_t rows = gemm.M < kDecodeGroupRows ? gemm.M : kDecodeGroupRows;
+  switch ((int)((rows + 15) / 16)) {
     case 1: e = launch_decode_gemm<1, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
     case 2: e = launch_decode_gemm<2, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
     case 3: e = launch_decode_gemm<3, F8>(gemm, plan.tiles, plan.kb, ev, stream); break;
@@ -599,12 +619,14 @@ hipError_t launch_decode_kernels(const DecodeGemmArgs &gemm, const DecodePlan &p
 DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
   DecodePlan p;
   p.tiles = (int)((N + kTileN - 1) / kTileN);
+  // blocks per K split: tiles x row groups
+  const int64_t per = (int64_t)p.tiles * ((M + kDecodeGroupRows - 1) / kDecodeGroupRows);
   p.det_blocks = (int)((K + kDetCols - 1) / kDetCols);
   // K splits: a power of two, about kTargetBlocks blocks in all, and at least
   // one full stage of K per split
   auto splits_for = [&](int64_t target) {
     int b = 1;
-    while (b < kMaxSplits && (int64_t)p.tiles * (b * 2) <= target && K / (b * 2) >= kSubK)
+    while (b < kMaxSplits && per * (b * 2) <= target && K / (b * 2) >= kSubK)
       b *= 2;
     return b;
   };
@@ -622,7 +644,7 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
   if (M > 16 && (K + kb - 1) / kb > 2 * kSubK) {
     int b = kb;
     while (b < kMaxSplits && (K + b - 1) / b > 2 * kSubK) b *= 2;
-    kb = ((K + b - 1) / b <= 2 * kSubK && (int64_t)p.tiles * b <= kOnePassBlocks)
+    kb = ((K + b - 1) / b <= 2 * kSubK && per * b <= kOnePassBlocks)
              ? b
              : splits_for(kWideBlocks);
   }
@@ -633,15 +655,32 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
   return p;
 }
 
+// Up to 64 rows the small-M kernels always run. With 65 to 128 rows (two row
+// groups, whose blocks read the same Wq bytes) they run only when the plan
+// reaches K ranges of at most two stages within kOnePassBlocks blocks; the
+// large-M path is faster otherwise. Graph-replayed (same weights each call):
+// 65x4096x4096 33.1 -> 19.2 us, 128x4096x4096 33.6 -> 21.3 us on this path;
+// 128x4096x11008 35.3 against 66.2 us and 128x8192x8192 40.7 against 67.9 us
+// stay on the large-M path.
+bool use_decode_path(int64_t M, int64_t K, int64_t N) {
+  if (M <= kDecodeGroupRows) return true;
+  if (M > kDecodeMaxM) return false;
+  const DecodePlan p = decode_plan(M, K, N);
+  const int64_t groups = (M + kDecodeGroupRows - 1) / kDecodeGroupRows;
+  return p.kc <= 2 * kSubK && (int64_t)p.tiles * groups * p.kb <= kOnePassBlocks;
+}
+
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream) {
-  static_assert(kDetRowIters == 4, "detection row iterations");
+  static_assert(kDetRowIters == 8, "detection row iterations");
   if (det.M <= kDetRows)
     hipLaunchKernelGGL(k_decode_detect<1>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   else if (det.M <= 2 * kDetRows)
     hipLaunchKernelGGL(k_decode_detect<2>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
-  else
+  else if (det.M <= 4 * kDetRows)
     hipLaunchKernelGGL(k_decode_detect<4>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
+  else
+    hipLaunchKernelGGL(k_decode_detect<8>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return gemm.fp8 ? launch_decode_kernels<true>(gemm, plan, ev, stream)

@@ -210,6 +210,10 @@ struct DecodePlan {
   int64_t kc;      // k bytes per split (multiple of 64)
 };
 DecodePlan decode_plan(int64_t M, int64_t K, int64_t N);
+// Whether a layer call of this shape takes the small-M kernels (M <= 64
+// always; up to kDecodeMaxM rows when their plan streams every K range in one
+// pass).
+bool use_decode_path(int64_t M, int64_t K, int64_t N);
 
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream);

@@ -138,7 +138,9 @@ def test_small_shapes(dev, M, K, N, seed, threshold):
 # more than 32 detection blocks and a second 8192-column window of the outlier
 # list (K > 8192), 64 rows, and N not a multiple of 64.
 DECODE = [(3, 5632, 4096), (2, 9216, 4096), (9, 8192, 128), (4, 4096, 8192), (64, 2048, 2048),
-          (32, 1088, 72), (1, 12288, 1032)]
+          (32, 1088, 72), (1, 12288, 1032),
+          # two row groups of 64 (65 to 128 rows, K ranges of at most two stages)
+          (65, 4096, 4096), (100, 2048, 1032), (128, 4096, 520), (97, 1024, 136)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE)
@@ -785,8 +787,8 @@ SPLIT_CASES = [
     (1100, 4096, 1032, 3.0, 4),   # compacted k (about 30 % outliers): 45 tiles, 2 parts of ~12 stages
     (300, 4096, 264, 0.0, 0),     # every column an outlier: no int8 stage in any part
     (300, 4096, 264, math.inf, 0),  # no outlier: no fp16 product
-    (100, 16384, 264, 6.0, 2),    # 2 tiles in 8 parts
-    (65, 4096, 520, 6.0, 2),      # one row past the small-M path: 3 tiles of 128 rows
+    (130, 16384, 264, 6.0, 2),    # 2 x 2 tiles in 8 parts
+    (129, 4096, 520, 6.0, 2),     # one row past the small-M path: 2 x 3 tiles of 128 rows
     (768, 4096, 2056, 6.0, 3),    # 6 x 9 = 54 tiles of 128 rows in 2 parts (4 would leave 8 stages each)
     (768, 8192, 8192, 6.0, 3),    # 192 tiles of 128 rows do not split: 96 of 256 rows in 2 parts
 ]
