@@ -340,7 +340,8 @@ def test_workload_70b(dev, w70, threshold, call):
 
 # Every row of the 70b workload at all three thresholds: the full report run,
 # left out of routine runs for its time (about a minute of oracle work per
-# threshold on 16 threads). Enable with LLMINT8_FULL_70B=1.
+# threshold on 16 threads). Enable with LLMINT8_FULL_70B=1, and run pytest with -s so that
+# the oracle's progress lines (every 20 s) are not held back.
 @pytest.mark.skipif(os.environ.get("LLMINT8_FULL_70B") != "1",
                     reason="full 70b report run: set LLMINT8_FULL_70B=1")
 @pytest.mark.parametrize("threshold,call", [(6.0, 0), (math.inf, 1), (4.0, 2)])
