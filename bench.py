@@ -57,9 +57,10 @@ HBM_BOUND = ("tiny", "decode")
 DECODE_MAX_M = 128  # rows up to which the library may take its small-M path (65-128: shape-dependent)
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources of the GEMM kernels whose HBM counters are committed: the split-K
-# small-M kernels (up to 64 rows; the single-kernel path runs none of the
-# workloads with counters) and the large-M ones, digested separately so that a
-# change to one family leaves the other's counters valid.
+# small-M kernels (up to 64 rows, or 128 when they stream K in one pass; the
+# single-kernel path runs none of the workloads with counters) and the
+# large-M ones, digested separately so that a change to one family leaves the
+# other's counters valid.
 _CSRC = os.path.join(ROOT, "bit_quantized_matmul_col_amd", "csrc")
 KERNEL_SOURCES = {
     "small_m": [os.path.join(_CSRC, f) for f in ("common.hpp", "internal.hpp", "decode.hip")],

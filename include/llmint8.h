@@ -119,9 +119,11 @@ int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ld
  *              int32 accumulators of step 4.
  *   workspace  device scratch of at least llmint8_workspace_size(M, K, N) bytes.
  * When the outlier share is large, the int8 GEMM runs over the K - |O| kept
- * columns only (compacted operands); when M > 64 and the 256 x 256 output
- * tiles number fewer than the GPU's 256 CUs, each tile's k range is split
- * into parts whose int32 sums meet in the workspace. The result is identical
+ * columns only (compacted operands); when a large-M call's output tiles
+ * (128 x 256 or 256 x 256) number fewer than the GPU's 256 CUs, each tile's
+ * k range is split into parts whose int32 sums meet in the workspace. Up to
+ * 64 rows, and up to 128 when the shape lets the small-M kernels stream K in
+ * one pass, the call takes the small-M kernels. The result is identical
  * either way.
  */
 size_t llmint8_workspace_size(int64_t M, int64_t K, int64_t N);
