@@ -54,10 +54,10 @@ FP16_PEAK_TFLOPS = 2500.0
 # 256 CUs x 2.4 GHz x 8192
 INT8_OPS_PER_CU_CLOCK = 8192
 HBM_BOUND = ("tiny", "decode")
-DECODE_MAX_M = 128  # rows up to which the library may take its small-M path (65-128: shape-dependent)
+DECODE_MAX_M = 256  # rows up to which the library may take its small-M path (65-256: shape-dependent)
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources of the GEMM kernels whose HBM counters are committed: the split-K
-# small-M kernels (up to 64 rows, or 128 when they stream K in one pass; the
+# small-M kernels (up to 64 rows, or 256 when they stream K in one pass; the
 # single-kernel path runs none of the workloads with counters) and the
 # large-M ones, digested separately so that a change to one family leaves the
 # other's counters valid.
@@ -67,7 +67,7 @@ KERNEL_SOURCES = {
     "large_m": [os.path.join(_CSRC, f) for f in
                 ("common.hpp", "internal.hpp", "gemm_core.hpp", "gemm.hip", "gemm_narrow.hip")],
 }
-SMALL_M_MAX = 128  # rows up to which the layer runs the small-M kernels
+SMALL_M_MAX = 256  # rows up to which the layer runs the small-M kernels
 # the larger workloads measured by default next to the headline one
 SWEEP = (("prefill", (6.0,)), ("13b", (6.0,)), ("70b", (6.0, 4.0, math.inf)))
 

@@ -35,7 +35,7 @@ __host__ __device__ inline bool use_compaction(int count, int64_t K, int64_t M) 
 
 // Row count up to which the layer takes the small-M (decode) path, and the
 // rows of one of its row groups (a GEMM block covers one group).
-constexpr int kDecodeMaxM = 128;
+constexpr int kDecodeMaxM = 256;
 constexpr int kDecodeGroupRows = 64;
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }

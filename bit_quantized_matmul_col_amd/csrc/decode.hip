@@ -1,6 +1,6 @@
 // Small-M (decode-shaped) path of the LLM.int8() linear layer on gfx950.
 //
-// With M <= 128 rows the layer is bound by streaming the int8 weight Wq from
+// With M <= 256 rows the layer is bound by streaming the int8 weight Wq from
 // HBM (the decode regime of the INT8-vs-FP8 page, section one: every step
 // re-reads all weights). The path is three kernels. None communicates across
 // blocks inside a kernel (on gfx950 each XCD has its own L2, so an agent-scope
@@ -655,13 +655,15 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
   return p;
 }
 
-// Up to 64 rows the small-M kernels always run. With 65 to 128 rows (two row
-// groups, whose blocks read the same Wq bytes) they run only when the plan
-// reaches K ranges of at most two stages within kOnePassBlocks blocks; the
-// large-M path is faster otherwise. Graph-replayed (same weights each call):
-// 65x4096x4096 33.1 -> 19.2 us, 128x4096x4096 33.6 -> 21.3 us on this path;
+// Up to 64 rows the small-M kernels always run. With 65 to 256 rows (two to
+// four row groups, whose blocks read the same Wq bytes) they run only when the
+// plan reaches K ranges of at most two stages within kOnePassBlocks blocks;
+// the large-M path is faster otherwise. Graph-replayed (same weights each
+// call): 65x4096x4096 33.1 -> 19.2 us, 128x4096x4096 33.6 -> 21.3 us,
+// 192x4096x4096 33.9 -> 28.9 us, 192x2048x2048 31.5 -> 17.7 us on this path;
 // 128x4096x11008 35.3 against 66.2 us and 128x8192x8192 40.7 against 67.9 us
-// stay on the large-M path.
+// stay on the large-M path, and with a 1024-block budget 256x4096x4096 ran
+// level with it (34.5 us).
 bool use_decode_path(int64_t M, int64_t K, int64_t N) {
   if (M <= kDecodeGroupRows) return true;
   if (M > kDecodeMaxM) return false;
@@ -672,15 +674,17 @@ bool use_decode_path(int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,
                          const DecodePlan &plan, const GemmEvents &ev, hipStream_t stream) {
-  static_assert(kDetRowIters == 8, "detection row iterations");
+  static_assert(kDetRowIters == 16, "detection row iterations");
   if (det.M <= kDetRows)
     hipLaunchKernelGGL(k_decode_detect<1>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   else if (det.M <= 2 * kDetRows)
     hipLaunchKernelGGL(k_decode_detect<2>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   else if (det.M <= 4 * kDetRows)
     hipLaunchKernelGGL(k_decode_detect<4>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
-  else
+  else if (det.M <= 8 * kDetRows)
     hipLaunchKernelGGL(k_decode_detect<8>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
+  else
+    hipLaunchKernelGGL(k_decode_detect<16>, dim3(plan.det_blocks), dim3(256), 0, stream, det);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return gemm.fp8 ? launch_decode_kernels<true>(gemm, plan, ev, stream)

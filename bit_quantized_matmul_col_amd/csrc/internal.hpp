@@ -211,8 +211,8 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int64_t M, int64_t K, int64_t N);
 // Whether a layer call of this shape takes the small-M kernels (M <= 64
-// always; up to kDecodeMaxM rows when their plan streams every K range in one
-// pass).
+// always; up to kDecodeMaxM = 256 rows when their plan streams every K range
+// in one pass).
 bool use_decode_path(int64_t M, int64_t K, int64_t N);
 
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,

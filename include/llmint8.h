@@ -122,7 +122,7 @@ int llmint8_quantize_rowwise(const uint16_t *X, int64_t M, int64_t K, int64_t ld
  * columns only (compacted operands); when a large-M call's output tiles
  * (128 x 256 or 256 x 256) number fewer than the GPU's 256 CUs, each tile's
  * k range is split into parts whose int32 sums meet in the workspace. Up to
- * 64 rows, and up to 128 when the shape lets the small-M kernels stream K in
+ * 64 rows, and up to 256 when the shape lets the small-M kernels stream K in
  * one pass, the call takes the small-M kernels. The result is identical
  * either way.
  */

@@ -139,8 +139,9 @@ def test_small_shapes(dev, M, K, N, seed, threshold):
 # list (K > 8192), 64 rows, and N not a multiple of 64.
 DECODE = [(3, 5632, 4096), (2, 9216, 4096), (9, 8192, 128), (4, 4096, 8192), (64, 2048, 2048),
           (32, 1088, 72), (1, 12288, 1032),
-          # two row groups of 64 (65 to 128 rows, K ranges of at most two stages)
-          (65, 4096, 4096), (100, 2048, 1032), (128, 4096, 520), (97, 1024, 136)]
+          # two to four row groups of 64 (65 to 256 rows, K ranges of at most two stages)
+          (65, 4096, 4096), (100, 2048, 1032), (128, 4096, 520), (97, 1024, 136),
+          (129, 4096, 520), (192, 2048, 2048), (256, 2048, 1032), (250, 1024, 136)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE)
@@ -276,7 +277,7 @@ def test_deterministic(dev):
 
 # one shape per path: split-K small M, the single kernel (M <= 16, K = 1024),
 # large M
-@pytest.mark.parametrize("M,K,N", [(50, 128, 40), (8, 1024, 40), (130, 256, 72)])
+@pytest.mark.parametrize("M,K,N", [(50, 128, 40), (8, 1024, 40), (300, 256, 72)])
 def test_strided_inputs(dev, M, K, N):
     torch, lm = dev
     say(f"case strided leading dimensions M={M} K={K} N={N}")
@@ -422,11 +423,13 @@ def test_supplied_input_column_absmax(dev, M, K, N, threshold):
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
 
 
-def test_column_absmax_chains_two_layers(dev):
+# 200 rows take the small-M kernels in four row groups, 300 the large-M ones
+@pytest.mark.parametrize("M", [200, 300])
+def test_column_absmax_chains_two_layers(dev, M):
     # layer 1 emits its Y's column absmax; layer 2 takes it instead of scanning
     torch, lm = dev
-    say("case two chained layers through the column absmax")
-    X, W1, _ = workloads.random_case(200, 512, 1024, seed=31, n_out=3, w_sigma=0.2)
+    say(f"case two chained layers through the column absmax M={M}")
+    X, W1, _ = workloads.random_case(M, 512, 1024, seed=31, n_out=3, w_sigma=0.2)
     _, W2, _ = workloads.random_case(1, 1024, 256, seed=32)
     Xd = to_gpu(torch, X)
     W1d, W2d = to_gpu(torch, W1), to_gpu(torch, W2)
@@ -788,8 +791,8 @@ SPLIT_CASES = [
     (1100, 4096, 1032, 3.0, 4),   # compacted k (about 30 % outliers): 45 tiles, 2 parts of ~12 stages
     (300, 4096, 264, 0.0, 0),     # every column an outlier: no int8 stage in any part
     (300, 4096, 264, math.inf, 0),  # no outlier: no fp16 product
-    (130, 16384, 264, 6.0, 2),    # 2 x 2 tiles in 8 parts
-    (129, 4096, 520, 6.0, 2),     # one row past the small-M path: 2 x 3 tiles of 128 rows
+    (258, 16384, 264, 6.0, 2),    # 3 x 2 tiles in 8 parts
+    (257, 4096, 520, 6.0, 2),     # one row past the small-M path: 3 x 3 tiles of 128 rows
     (768, 4096, 2056, 6.0, 3),    # 6 x 9 = 54 tiles of 128 rows in 2 parts (4 would leave 8 stages each)
     (768, 8192, 8192, 6.0, 3),    # 192 tiles of 128 rows do not split: 96 of 256 rows in 2 parts
 ]
