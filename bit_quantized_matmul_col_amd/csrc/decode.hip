@@ -35,6 +35,7 @@ constexpr int kPmaxUnroll = 8;     // detection partials per thread loaded up fr
 constexpr int kTargetBlocks = 256; // GEMM blocks aimed for (one per CU)
 constexpr int kOnePassBlocks = 768;  // most blocks for K ranges of at most two stages
 constexpr int kWideBlocks = 512;     // blocks aimed for when that does not fit
+constexpr int kGroupedOneRangeBlocks = 384;  // most blocks for 3-4 row groups over all of K
 constexpr int kMaxSplits = 16;
 constexpr int kListWords = 256;    // mask words scanned per epilogue window
 constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
@@ -663,13 +664,20 @@ DecodePlan decode_plan(int64_t M, int64_t K, int64_t N) {
 // 192x4096x4096 33.9 -> 28.9 us, 192x2048x2048 31.5 -> 17.7 us on this path;
 // 128x4096x11008 35.3 against 66.2 us and 128x8192x8192 40.7 against 67.9 us
 // stay on the large-M path, and with a 1024-block budget 256x4096x4096 ran
-// level with it (34.5 us).
+// level with it (34.5 us). With three or four row groups and one K range per
+// block (K <= 1024, where the large-M path costs least, about 25 us) the
+// small-M kernels lose beyond kGroupedOneRangeBlocks blocks: 160x1024x11008
+// 29.9 against 25.1 us, 256x1024x8192 26.7 against 25.4 us, 160x1024x14336
+// 31.3 against 25.6 us, while 192x1024x8192 (384 blocks) ran 24.5 against
+// 25.1 us and 160x1024x8192 23.2 against 25.2 us.
 bool use_decode_path(int64_t M, int64_t K, int64_t N) {
   if (M <= kDecodeGroupRows) return true;
   if (M > kDecodeMaxM) return false;
   const DecodePlan p = decode_plan(M, K, N);
   const int64_t groups = (M + kDecodeGroupRows - 1) / kDecodeGroupRows;
-  return p.kc <= 2 * kSubK && (int64_t)p.tiles * groups * p.kb <= kOnePassBlocks;
+  const int64_t blocks = (int64_t)p.tiles * groups * p.kb;
+  if (p.kc > 2 * kSubK || blocks > kOnePassBlocks) return false;
+  return groups <= 2 || p.kb > 1 || blocks <= kGroupedOneRangeBlocks;
 }
 
 hipError_t launch_decode(const DecodeDetectArgs &det, const DecodeGemmArgs &gemm,

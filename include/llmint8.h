@@ -144,7 +144,7 @@ int llmint8_linear(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
  * besides the launches). It never splits the k range of its GEMM tiles, so
  * it needs llmint8_workspace_size(M, K, N) less the split-K area; a call
  * whose need exceeds the scratch returns LLMINT8_ERR_WORKSPACE before any HIP
- * call: in practice this covers the small-M (decode) shapes, M <= 128, and
+ * call: in practice this covers the small-M (decode) shapes, M <= 256, and
  * small large-M ones. Every call on one GPU
  * shares its scratch, so calls that may overlap on one GPU (different
  * streams, or host threads without ordering) race; order them on one stream.

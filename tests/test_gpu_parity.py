@@ -141,7 +141,9 @@ DECODE = [(3, 5632, 4096), (2, 9216, 4096), (9, 8192, 128), (4, 4096, 8192), (64
           (32, 1088, 72), (1, 12288, 1032),
           # two to four row groups of 64 (65 to 256 rows, K ranges of at most two stages)
           (65, 4096, 4096), (100, 2048, 1032), (128, 4096, 520), (97, 1024, 136),
-          (129, 4096, 520), (192, 2048, 2048), (256, 2048, 1032), (250, 1024, 136)]
+          (129, 4096, 520), (192, 2048, 2048), (256, 2048, 1032), (250, 1024, 136),
+          # three row groups over all of K: 384 blocks, and 516 blocks (the large-M path)
+          (192, 1024, 8192), (160, 1024, 11008)]
 
 
 @pytest.mark.parametrize("M,K,N", DECODE)

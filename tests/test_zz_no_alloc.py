@@ -54,7 +54,8 @@ PAIRS = [((64, 4096, 4096), (20, 1024, 520)),
          ((16, 4096, 11008), (3, 1024, 136)),
          ((300, 1024, 520), (70, 256, 64)),
          ((300, 4096, 520), (70, 256, 64)),
-         ((48, 8192, 4096), (1, 16, 8))]
+         ((48, 8192, 4096), (1, 16, 8)),
+         ((192, 2048, 2048), (129, 4096, 520))]  # small-M kernels in three and four row groups
 
 
 @pytest.mark.parametrize("first,second", PAIRS)
