@@ -39,6 +39,7 @@ constexpr int kGroupedOneRangeBlocks = 384;  // most blocks for 3-4 row groups o
 constexpr int kMaxSplits = 16;
 constexpr int kListWords = 256;    // mask words scanned per epilogue window
 constexpr int kOutBatch = 32;      // outlier columns staged per epilogue round
+constexpr int kEpilogueFillBlocks = 256;  // epilogue blocks that fill the CUs
 
 __device__ inline u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
 
@@ -384,21 +385,25 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeGemmArgs a) {
   }
 }
 
-// Block (tile, row group of 16): 64 columns x 16 rows, 4 outputs per thread
-// (rows wv + 4 i, column lane). KB is the number of K splits; F8: the partial
-// sums are fp32 (added in split order) and the dequantization is / 448^2.
-template <int KB, bool F8>
+// Block (tile, row block of ER = 16 or 8): 64 columns x ER rows, ER / 4
+// outputs per thread (rows wv + 4 i, column lane). KB is the number of K
+// splits; F8: the partial sums are fp32 (added in split order) and the
+// dequantization is / 448^2.
+template <int KB, bool F8, int ER>
 __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
+  constexpr int kEpiI = ER / 4;                 // outputs per thread
+  constexpr int kEpiXH = ER * kOutBatch / 256;  // X entries per thread and batch
+  static_assert(kEpiXH >= 1, "one X entry per thread at least");
   __shared__ int slist[kListWords * 32];             // outlier columns of one window
   __shared__ int swsum[4];
-  __shared__ float sxo[16][kOutBatch];               // [row][p]
+  __shared__ float sxo[ER][kOutBatch];               // [row][p]
   __shared__ __attribute__((aligned(16))) uint16_t swo[kOutBatch * kTileN];  // [p][col]
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * kTileN;
   const int64_t col = n0 + lane;
   const bool colok = col < a.N;
   const int64_t colc = colok ? col : 0;
-  const int rbase = blockIdx.y * 16;
+  const int rbase = blockIdx.y * ER;
 
   // every independent load first, the first mask window ahead of the rest:
   // the outlier chain (mask, list, W rows and X entries) is the longest
@@ -407,10 +412,10 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void *)a.omask, (short)0, (int)(a.kw * 4), 0x00020000);
   uint32_t mw = __builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * t, 0, 0);
 
-  int pp[4][KB];
-  float mrow[4];
+  int pp[kEpiI][KB];
+  float mrow[kEpiI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kEpiI; ++i) {
     const int row = rbase + wv + 4 * i;
     const int rowc = row < a.M ? row : 0;
 #pragma unroll
@@ -427,7 +432,9 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   // the outlier product runs with fp16 weight rows or with the int8 codes
   const bool i8w = a.ep.int8w != 0;
   const bool outl = a.w || i8w;
-  float yo[4] = {0.f, 0.f, 0.f, 0.f};
+  float yo[kEpiI];
+#pragma unroll
+  for (int i = 0; i < kEpiI; ++i) yo[i] = 0.f;
   // fp16 outlier terms, outlier columns in ascending order (yo: with int8
   // weight codes they are scaled by s / 127 at the end); the partial sums are
   // added after them, so the chain does not wait for the partial sums
@@ -470,10 +477,10 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
         // never stored or terms never summed.
         {  // X entries first (16 rows x 32 outliers, two per thread), then the
            // W rows (32 rows x 8 chunks of 8 columns, one per thread)
-          uint32_t xe[2];
-          int xr[2], xp[2];
+          uint32_t xe[kEpiXH];
+          int xr[kEpiXH], xp[kEpiXH];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int h = 0; h < kEpiXH; ++h) {
             const int q = t + 256 * h;
             xr[h] = q >> 5;
             xp[h] = q & 31;
@@ -498,13 +505,13 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
           }
           *(u32x4 *)(swo + p * kTileN + 8 * ch) = v;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) sxo[xr[h]][xp[h]] = h2f((uint16_t)xe[h]);
+          for (int h = 0; h < kEpiXH; ++h) sxo[xr[h]][xp[h]] = h2f((uint16_t)xe[h]);
         }
         __syncthreads();
         for (int p = 0; p < np; ++p) {
           const float wval = h2f(swo[p * kTileN + lane]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yo[i] += sxo[wv + 4 * i][p] * wval;
+          for (int i = 0; i < kEpiI; ++i) yo[i] += sxo[wv + 4 * i][p] * wval;
         }
         __syncthreads();
       }
@@ -521,10 +528,10 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
     if (t == 0) *a.count_out = scount[0] + scount[1] + scount[2] + scount[3];
   }
 
-  float y[4];
+  float y[kEpiI];
   const float sd = scol * (F8 ? 1.0f / 200704.0f : 1.0f / 16129.0f);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kEpiI; ++i) {
     int cacc = 0;
     float cf = 0.f;
 #pragma unroll
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(256) void k_decode_epilogue(DecodeGemmArgs a) {
   const float bcol = a.ep.bias ? h2f(braw) : 0.f;
   float cmax = 0.f;  // |Y| of this column over the block's rows
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kEpiI; ++i) {
     const int row = rbase + wv + 4 * i;
     const float v = y[i] + yo[i] * oscale + bcol;
     if (colok && row < a.M) a.y[(int64_t)row * a.ldy + col] = f2h(v);
@@ -586,10 +593,19 @@ hipError_t launch_decode_gemm(const DecodeGemmArgs &a, int tiles, int kb, const 
   return launch_decode_gemm_rg<MB, F8, false>(a, tiles, kb, ev, stream);
 }
 
+// 8-row blocks when 16-row blocks would leave CUs idle: graph-replayed,
+// 32x4096x4096 11.4-11.5 -> 11.3 us and 24x4096x4096 11.3 -> 11.0 us, while
+// with enough 16-row blocks the 8-row ones cost more (64x4096x11008 25.3 ->
+// 26.6 us, 128x4096x4096 20.6 -> 20.9 us).
 template <int KB, bool F8>
 hipError_t launch_decode_epilogue(const DecodeGemmArgs &a, int tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((k_decode_epilogue<KB, F8>), dim3(tiles, (unsigned)((a.M + 15) / 16)),
-                     dim3(256), 0, stream, a);
+  const int64_t blocks16 = (int64_t)tiles * ((a.M + 15) / 16);
+  if (blocks16 < kEpilogueFillBlocks)
+    hipLaunchKernelGGL((k_decode_epilogue<KB, F8, 8>), dim3(tiles, (unsigned)((a.M + 7) / 8)),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_decode_epilogue<KB, F8, 16>), dim3(tiles, (unsigned)((a.M + 15) / 16)),
+                       dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
