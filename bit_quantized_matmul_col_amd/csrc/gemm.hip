@@ -59,13 +59,24 @@ int64_t wide_columns(int64_t M, int64_t N, int cus) {
 // what the split saves.
 constexpr int64_t kSplitMinStages = 16;
 constexpr int kSplitMax = 8;
+// With a short k range (at most 16 stages, K <= 2048) a whole tile is short
+// too, and shorter parts pay: 128 x 256 tiles split into parts of at least 4
+// stages when there are at most kShortSplitFewTiles tiles, else of at least 8.
+// Graph-replayed calls: 300 x 1024 x 4096 25.4 -> 23.5 us, 512 x 1024 x 1024
+// 25.5 -> 23.2, 600 x 1024 x 2048 26.2 -> 24.2, 300 x 2048 x 2048 32.9 ->
+// 27.6 (4 parts), 768 x 2048 x 4096 35.7 -> 32.2, 400 x 2048 x 8192 35.5 ->
+// 32.8. Parts of 4 stages in 128 tiles (1024 x 1024 x 4096, 28.1 -> 30.3 us)
+// and 256 x 256 tiles in parts of 4 stages (257 x 1024 x 11008, 26.2 -> 38.2
+// us) were slower, so those stay whole.
+constexpr int64_t kShortSplitStages = 16;
+constexpr int64_t kShortSplitFewTiles = 96;
 
 }  // namespace
 
 // The tiles a split-K launch cuts. When a launch has fewer tiles than CUs (M
 // up to several hundred rows at these widths), most of the chip would idle:
 // every tile then cuts its k range into as many parts as the CUs take (at most
-// kSplitMax, each at least kSplitMinStages stages). The tiles are 128 x 256
+// kSplitMax, each at least kSplitMinStages stages, fewer for short k ranges). The tiles are 128 x 256
 // when that gives a split (a three-stage ring, and no zero rows below M = 128),
 // else 256 x 256. Measured on whole calls (best of six interleaved rounds),
 // 256 x 256 split tiles against whole ones: 128 x 8192 x 8192 78.4 -> 56.8 us,
@@ -80,12 +91,16 @@ constexpr int kSplitMax = 8;
 // launch agree.
 GemmSplitPlan gemm_split_plan(int64_t M, int64_t K, int64_t N) {
   constexpr int64_t cus = 256;
+  const int64_t nst = (K + 127) / 128;
+  const bool short_k = nst <= kShortSplitStages;
   for (const int bm : {128, 256}) {
+    if (short_k && bm == 256) break;
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
     if (tiles >= cus) continue;
+    const int64_t min_st = !short_k ? kSplitMinStages : tiles <= kShortSplitFewTiles ? 4 : 8;
     int64_t S = cus / tiles;
     if (S > kSplitMax) S = kSplitMax;
-    while (S > 1 && (K + 127) / 128 < S * kSplitMinStages) --S;
+    while (S > 1 && nst < S * min_st) --S;
     if (S >= 2) return GemmSplitPlan{tiles, (int)S, bm};
   }
   return GemmSplitPlan{0, 1, 256};

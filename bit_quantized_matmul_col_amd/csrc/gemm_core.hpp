@@ -503,6 +503,12 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int64_t bid, uin
   }
   if constexpr (SPLIT) {
     if (!split_merge<TH, MI * NI>(a, tile, split, acc)) return;
+  } else {
+    // With no k stage (every column an outlier, compacted) the k-loop has run
+    // no barrier, and the scales written to LDS above are not yet visible to
+    // every wave. Without this, a wave could read what an earlier block left
+    // in LDS (a NaN row scale of rows past M, say) into its dequantization.
+    if ((Kl + SK - 1) / SK == 0) __syncthreads();
   }
 
   // dequantize in place: C * m[i] * s[n] / 127^2 (or / 448^2)

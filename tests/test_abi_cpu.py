@@ -193,6 +193,12 @@ res["ws_size_6tiles"] = L.llmint8_workspace_size(300, 8192, 520)
 res["ws_fp8_6tiles"] = L.llmint8_linear_fp8_workspace_size(300, 8192, 520)
 res["ws_size_768"] = L.llmint8_workspace_size(768, 8192, 8192)
 res["ws_fp8_768"] = L.llmint8_linear_fp8_workspace_size(768, 8192, 8192)
+res["ws_size_short_k"] = L.llmint8_workspace_size(300, 2048, 2048)
+res["ws_fp8_short_k"] = L.llmint8_linear_fp8_workspace_size(300, 2048, 2048)
+res["ws_size_short_k_many"] = L.llmint8_workspace_size(1024, 1024, 4096)
+res["ws_fp8_short_k_many"] = L.llmint8_linear_fp8_workspace_size(1024, 1024, 4096)
+res["ws_size_short_k_wide"] = L.llmint8_workspace_size(400, 2048, 8192)
+res["ws_fp8_short_k_wide"] = L.llmint8_linear_fp8_workspace_size(400, 2048, 8192)
 res["ws_size_bad"] = L.llmint8_workspace_size(0, 4096, 4096)
 res["find_ws_ok"] = L.llmint8_find_outliers_workspace_size(8192, 8192)
 res["find_ws_bad"] = L.llmint8_find_outliers_workspace_size(8, 133160)
@@ -264,6 +270,11 @@ def test_invalid_arguments_are_rejected_before_any_hip_call():
     assert res["ws_size_6tiles"] - res["ws_fp8_6tiles"] == split_room(9, 4)
     # 768 x 8192 x 8192: 192 tiles of 128 x 256 do not split, 96 of 256 x 256 do (2 parts)
     assert res["ws_size_768"] - res["ws_fp8_768"] == split_room(96, 2, 256)
+    # short k ranges (K <= 2048, at most 16 stages): 128 x 256 tiles only, parts of
+    # at least 4 stages up to 96 tiles, else of at least 8
+    assert res["ws_size_short_k"] - res["ws_fp8_short_k"] == split_room(24, 4)
+    assert res["ws_size_short_k_many"] == res["ws_fp8_short_k_many"]  # 128 tiles of 8 stages
+    assert res["ws_size_short_k_wide"] - res["ws_fp8_short_k_wide"] == split_room(128, 2)
 
 
 def test_status_strings():

@@ -797,6 +797,10 @@ SPLIT_CASES = [
     (257, 4096, 520, 6.0, 2),     # one row past the small-M path: 3 x 3 tiles of 128 rows
     (768, 4096, 2056, 6.0, 3),    # 6 x 9 = 54 tiles of 128 rows in 2 parts (4 would leave 8 stages each)
     (768, 8192, 8192, 6.0, 3),    # 192 tiles of 128 rows do not split: 96 of 256 rows in 2 parts
+    # short k ranges (K <= 2048)
+    (300, 2048, 2048, 6.0, 3),    # 24 tiles in 4 parts of 4 stages
+    (600, 1040, 2056, 6.0, 2),    # 45 tiles in 2 parts of 4 and 5 stages; ragged K and N
+    (400, 2048, 8184, 6.0, 2),    # 128 tiles in 2 parts of 8 stages; ragged N
 ]
 
 
