@@ -112,6 +112,34 @@ SMALL = [
 ]
 
 
+def test_all_outlier_tiles_after_ragged_calls(dev):
+    # Every column an outlier, compacted: the GEMM tiles run no int8 k stage, so
+    # nothing but an explicit barrier orders their LDS scales before the
+    # dequantization. A ragged-M call just before each one leaves NaN row scales
+    # (rows past M) in the LDS of the CUs it ran on.
+    torch, lm = dev
+    say("case all-outlier compacted tiles after ragged-M calls")
+    Xr, Wr, _ = workloads.random_case(300, 1024, 520, seed=41, n_out=2)
+    X, W, _ = workloads.random_case(2000, 96, 40, seed=2096, n_out=2)
+    idx_r = oracle.find_outliers(X, 2.0)
+    assert idx_r.size == 96, "case must make every column an outlier"
+    Wq_r, s_r = oracle.quantize_colwise(W)
+    Xq_r, m_r = oracle.quantize_rowwise(X, idx_r)
+    Y_r = oracle.merge(oracle.gemm_i8(Xq_r, Wq_r), m_r, s_r, X, W, idx_r)
+    Xrd, Wrd, Xd, Wd = to_gpu(torch, Xr), to_gpu(torch, Wr), to_gpu(torch, X), to_gpu(torch, W)
+    Wqr, sr = lm.llmint8_quantize_colwise(Wrd)
+    Wq, s = lm.llmint8_quantize_colwise(Wd)
+    first = None
+    for rep in range(4):
+        lm.llmint8_linear(Xrd, Wqr, sr, Wrd, 6.0)
+        Y = lm.llmint8_linear(Xd, Wq, s, Wd, 2.0)
+        torch.cuda.synchronize()
+        assert_y_close(Y.cpu().numpy(), Y_r, f"all-outlier Y, call {rep}")
+        if first is None:
+            first = Y.clone()
+        assert torch.equal(Y.view(torch.int16), first.view(torch.int16)), f"call {rep} differs"
+
+
 @pytest.mark.parametrize("M,K,N,threshold", [
     (600, 256, 136, 3.0), (1100, 512, 264, 3.2), (700, 1008, 200, 3.0), (2000, 96, 40, 2.0)])
 def test_compacted_inner_dimension(dev, M, K, N, threshold):
